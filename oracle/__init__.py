@@ -1,0 +1,180 @@
+"""CPU oracle for the W4A16 decode GEMV -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check and the bench's CPU-baseline leg may import this package.
+The product (the HIP library and its Python binding) never imports, links or runs it,
+and the two share no code: this side is plain single-threaded C in float64
+(w4a16_oracle.c), loaded through ctypes, with numpy wrappers below.
+
+It computes y[n] = sum_k q[n,k] * s[n, k/128] * x[k] exactly as that sum reads (float64),
+plus mag[n] = sum_k |q s x|, the basis of the per-element tolerance
+|err| <= 1e-3 * mag + 1e-5. See w4a16_oracle.c for the storage format and the passage of
+the local-kimi README it follows.
+
+Pins (tests/test_oracle_pins.py) tie it to facts other than itself: hand-computed worked
+examples, IEEE decodes checked against numpy's own conversions over every bit pattern,
+unit-vector probes with chosen nibbles and scales, zero-scale groups, linearity in x and
+negation, and exact closed forms for constant rows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "w4a16_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+TOL_REL = 1e-3
+TOL_ABS = 1e-5
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile an oracle C source with gcc (-O2, no fast-math) into a shared object."""
+    tmp = out + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
+                           "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build() -> str:
+    return compile_source(SOURCE, _LIB)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows(rows, N):
+    if rows is None:
+        return None, N
+    r = _c(rows, np.int64)
+    return r, r.size
+
+
+class Oracle:
+    """numpy front end over one compiled copy of the oracle."""
+
+    def __init__(self, lib_path: str):
+        lib = ctypes.CDLL(lib_path)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_double.restype = ctypes.c_double
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_unpack.argtypes = [P, P, i64, i64]
+        lib.oracle_gemv.argtypes = [P, P, P, i64, i64, i32, P, i64, P, P]
+        lib.oracle_gemv_batched.argtypes = [P, P, P, i64, i32, i64, i64, i32, P, i64, P, P]
+        lib.oracle_moe_gemv.argtypes = [P, P, P, i32, i32, P, i64, i64, i32, P, i64, P, P]
+        for f in (lib.oracle_unpack, lib.oracle_gemv, lib.oracle_gemv_batched,
+                  lib.oracle_moe_gemv):
+            f.restype = ctypes.c_int
+        self.lib = lib
+
+    def f16_to_double(self, bits: int) -> float:
+        return self.lib.oracle_f16_to_double(int(bits))
+
+    def bf16_to_double(self, bits: int) -> float:
+        return self.lib.oracle_bf16_to_double(int(bits))
+
+    def unpack(self, qweight: np.ndarray, K: int) -> np.ndarray:
+        """int8 [N][K] signed values of packed uint32 [N][K/8] words."""
+        qw = _c(qweight, np.uint32)
+        N = qw.shape[0] if qw.ndim == 2 else 1
+        out = np.empty((N, K), np.int8)
+        if self.lib.oracle_unpack(_ptr(qw), _ptr(out), N, K):
+            raise ValueError("oracle_unpack: bad arguments")
+        return out
+
+    def gemv(self, qweight, scales, x, K: int, group: int = 128,
+             rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """(y, mag) as float64 for the listed rows (all rows by default)."""
+        qw, sc, xx = _c(qweight, np.uint32), _c(scales, np.uint16), _c(x, np.uint16).reshape(-1)
+        N = qw.shape[0]
+        if xx.size < K:
+            raise ValueError("x shorter than K")
+        r, nr = _rows(rows, N)
+        y, mag = np.empty(nr), np.empty(nr)
+        if self.lib.oracle_gemv(_ptr(qw), _ptr(sc), _ptr(xx), N, K, group, _ptr(r), nr,
+                                _ptr(y), _ptr(mag)):
+            raise ValueError("oracle_gemv: bad arguments")
+        return y, mag
+
+    def gemv_batched(self, qweight, scales, X, K: int, group: int = 128,
+                     rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """(Y, mag) as float64 [M][rows] for activation rows X [M][ldx]."""
+        qw, sc, XX = _c(qweight, np.uint32), _c(scales, np.uint16), _c(X, np.uint16)
+        if XX.ndim == 1:
+            XX = XX.reshape(1, -1)
+        M, ldx = XX.shape
+        N = qw.shape[0]
+        r, nr = _rows(rows, N)
+        Y, mag = np.empty((M, nr)), np.empty((M, nr))
+        if self.lib.oracle_gemv_batched(_ptr(qw), _ptr(sc), _ptr(XX), ldx, M, N, K, group,
+                                        _ptr(r), nr, _ptr(Y), _ptr(mag)):
+            raise ValueError("oracle_gemv_batched: bad arguments")
+        return Y, mag
+
+    def moe_gemv(self, qweight, scales, ids, x, K: int, group: int = 128,
+                 rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """(y, mag) as float64 [topk][rows] for experts ids over qweight [E][N][K/8]."""
+        qw, sc = _c(qweight, np.uint32), _c(scales, np.uint16)
+        ii, xx = _c(ids, np.int32).reshape(-1), _c(x, np.uint16).reshape(-1)
+        E, N = qw.shape[0], qw.shape[1]
+        r, nr = _rows(rows, N)
+        y, mag = np.empty((ii.size, nr)), np.empty((ii.size, nr))
+        if self.lib.oracle_moe_gemv(_ptr(qw), _ptr(sc), _ptr(ii), ii.size, E, _ptr(xx), N, K,
+                                    group, _ptr(r), nr, _ptr(y), _ptr(mag)):
+            raise ValueError("oracle_moe_gemv: bad arguments")
+        return y, mag
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    """The oracle compiled from w4a16_oracle.c (rebuilt when the source is newer)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(_LIB)
+    return _default
+
+
+def f16_to_double(bits):
+    return default().f16_to_double(bits)
+
+
+def bf16_to_double(bits):
+    return default().bf16_to_double(bits)
+
+
+def unpack(qweight, K):
+    return default().unpack(qweight, K)
+
+
+def gemv(*a, **kw):
+    return default().gemv(*a, **kw)
+
+
+def gemv_batched(*a, **kw):
+    return default().gemv_batched(*a, **kw)
+
+
+def moe_gemv(*a, **kw):
+    return default().moe_gemv(*a, **kw)
+
+
+def bound(mag: np.ndarray) -> np.ndarray:
+    """Per-element allowance: 1e-3 * sum|q s x| + 1e-5."""
+    return TOL_REL * np.asarray(mag) + TOL_ABS

@@ -1,0 +1,193 @@
+/*
+ * CPU oracle for the W4A16 decode GEMV -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the bench's CPU-baseline leg may load this.
+ * The product library never links, loads or calls it, and this file shares no code,
+ * header, table or constant with the HIP path.
+ *
+ * What it computes (one thread, float64, no SIMD intrinsics, no reordering):
+ *
+ *     y[n] = sum_{k=0}^{K-1} q[n,k] * s[n, k / G] * x[k]
+ *
+ * The local-kimi README (github.1485827954.workers.dev/RightNow-AI/local-kimi), technical-detail section,
+ * paragraph on the GEMV rewrite, describes the operation as a true matrix-vector product
+ * over packed INT4 weights with 16-bit activations that reduces along K, the axis the
+ * packed weights keep contiguous; the grouped-expert form applies the same product to
+ * the weights of router-selected experts. The pages print no formula, so the plain
+ * definition above is written out here: dequantise each group (q times its scale, exact
+ * in float64) and take the float64 dot product with x.
+ *
+ * Storage (the plainest reading of "packed INT4 weights, reduction axis contiguous";
+ * the pages give no further layout):
+ *   qweight  uint32[N][K/8]: value k = 8w + i sits in bits [4i, 4i+3] of word w of its
+ *            row; the nibble is a two's-complement integer in [-8, 7] (no zero point).
+ *   scales   IEEE binary16 bit patterns [N][K/G], one per G-wide K group.
+ *   x        bfloat16 bit patterns [K] (the upper half of an IEEE binary32).
+ *
+ * Alongside y it returns mag[n] = sum_k |q s x|, the per-element tolerance basis
+ * |err| <= 1e-3 * mag + 1e-5 that the parity tests apply.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+
+/* IEEE-754 binary16 -> double, decoded from the bit fields by hand (exact). */
+double oracle_f16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1F;
+    int frac = h & 0x3FF;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -24);              /* zero or subnormal: frac * 2^-24 */
+    } else if (expo == 31) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + frac), expo - 25); /* (1 + frac/1024) * 2^(expo-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double: sign, 8-bit exponent (bias 127), 7-bit fraction (exact). */
+double oracle_bf16_to_double(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int expo = (b >> 7) & 0xFF;
+    int frac = b & 0x7F;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -133);             /* subnormal: frac/128 * 2^-126 */
+    } else if (expo == 255) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(128 + frac), expo - 134);
+    }
+    return sign ? -v : v;
+}
+
+/* Signed 4-bit value number k of a packed row. */
+int oracle_nibble(const uint32_t *row, int64_t k)
+{
+    uint32_t word = row[k / 8];
+    int u = (int)((word >> (4 * (k % 8))) & 0xFu);
+    return u >= 8 ? u - 16 : u;
+}
+
+/* q_out[N][K] = the signed nibble values of qweight[N][K/8]. */
+int oracle_unpack(const uint32_t *qweight, int8_t *q_out, int64_t N, int64_t K)
+{
+    if (!qweight || !q_out || N < 0 || K < 0 || K % 8)
+        return ORACLE_BAD_ARG;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            q_out[n * K + k] = (int8_t)oracle_nibble(qweight + n * (K / 8), k);
+    return ORACLE_OK;
+}
+
+/* One output element: the dequantise-then-dot of row `row` against activation row `x`. */
+static void dot_row(const uint32_t *row, const uint16_t *srow, const uint16_t *x,
+                    int64_t K, int64_t G, double *y, double *mag)
+{
+    double acc = 0.0, m = 0.0;
+    for (int64_t g = 0; g < K / G; ++g) {
+        double s = oracle_f16_to_double(srow[g]);
+        for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+            double w = (double)oracle_nibble(row, k) * s;   /* exact: 4 x 11 bits */
+            double p = w * oracle_bf16_to_double(x[k]);     /* exact: 15 x 8 bits */
+            acc += p;
+            m += fabs(p);
+        }
+    }
+    *y = acc;
+    *mag = m;
+}
+
+static int check_dense(const uint32_t *qweight, const uint16_t *scales, const void *x,
+                       int64_t N, int64_t K, int32_t G, const int64_t *rows, int64_t n_rows,
+                       const double *y, const double *mag)
+{
+    if (!qweight || !scales || !x || !y || !mag)
+        return ORACLE_BAD_ARG;
+    if (N < 1 || K < 1 || G < 8 || G % 8 || K % G || n_rows < 0)
+        return ORACLE_BAD_ARG;
+    if (rows)
+        for (int64_t r = 0; r < n_rows; ++r)
+            if (rows[r] < 0 || rows[r] >= N)
+                return ORACLE_BAD_ARG;
+    return ORACLE_OK;
+}
+
+/*
+ * y[r], mag[r] for the rows listed in rows[0..n_rows) (rows == NULL: all N rows, and
+ * n_rows must be N). Lets the tests check sampled rows of full-size matrices.
+ */
+int oracle_gemv(const uint32_t *qweight, const uint16_t *scales, const uint16_t *x,
+                int64_t N, int64_t K, int32_t G, const int64_t *rows, int64_t n_rows,
+                double *y, double *mag)
+{
+    if (check_dense(qweight, scales, x, N, K, G, rows, n_rows, y, mag))
+        return ORACLE_BAD_ARG;
+    if (!rows && n_rows != N)
+        return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t n = rows ? rows[r] : r;
+        dot_row(qweight + n * (K / 8), scales + n * (K / G), x, K, G, &y[r], &mag[r]);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Batched form: Y[m][r] for activation rows X[m] (row stride ldx elements), m < M.
+ * Output layout [M][n_rows], row-major.
+ */
+int oracle_gemv_batched(const uint32_t *qweight, const uint16_t *scales,
+                        const uint16_t *X, int64_t ldx, int32_t M, int64_t N, int64_t K,
+                        int32_t G, const int64_t *rows, int64_t n_rows, double *Y, double *mag)
+{
+    if (check_dense(qweight, scales, X, N, K, G, rows, n_rows, Y, mag))
+        return ORACLE_BAD_ARG;
+    if (M < 1 || ldx < K || (!rows && n_rows != N))
+        return ORACLE_BAD_ARG;
+    for (int32_t m = 0; m < M; ++m)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t n = rows ? rows[r] : r;
+            dot_row(qweight + n * (K / 8), scales + n * (K / G), X + m * ldx, K, G,
+                    &Y[m * n_rows + r], &mag[m * n_rows + r]);
+        }
+    return ORACLE_OK;
+}
+
+/*
+ * Grouped-expert form: y[t][r] is the product of expert ids[t]'s weights with x.
+ * qweight uint32[E][N][K/8], scales fp16 bits [E][N][K/G]. An id outside [0, E) names
+ * no expert; its output row is defined as zero (with mag zero).
+ */
+int oracle_moe_gemv(const uint32_t *qweight, const uint16_t *scales, const int32_t *ids,
+                    int32_t topk, int32_t E, const uint16_t *x, int64_t N, int64_t K,
+                    int32_t G, const int64_t *rows, int64_t n_rows, double *y, double *mag)
+{
+    if (check_dense(qweight, scales, x, N, K, G, rows, n_rows, y, mag))
+        return ORACLE_BAD_ARG;
+    if (!ids || topk < 1 || E < 1 || (!rows && n_rows != N))
+        return ORACLE_BAD_ARG;
+    for (int32_t t = 0; t < topk; ++t) {
+        int32_t e = ids[t];
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t n = rows ? rows[r] : r;
+            double *yo = &y[(int64_t)t * n_rows + r], *mo = &mag[(int64_t)t * n_rows + r];
+            if (e < 0 || e >= E) {
+                *yo = 0.0;
+                *mo = 0.0;
+                continue;
+            }
+            const uint32_t *wq = qweight + ((int64_t)e * N + n) * (K / 8);
+            const uint16_t *ws = scales + ((int64_t)e * N + n) * (K / G);
+            dot_row(wq, ws, x, K, G, yo, mo);
+        }
+    }
+    return ORACLE_OK;
+}

@@ -1,0 +1,292 @@
+"""Pins that tie the CPU oracle to facts other than itself.
+
+Each pin takes an `oracle.Oracle` and raises AssertionError when the oracle disagrees with
+what the storage format and the mathematics fix. They are run against the shipped oracle
+(test_oracle_pins.py) and against copies of it with a mistake planted in the C source
+(test_oracle_mutants.py), where at least one pin must fail.
+
+The operation pinned is the W4A16 GEMV of the local-kimi README
+(github.1485827954.workers.dev/RightNow-AI/local-kimi), technical-detail section, GEMV-rewrite paragraph:
+y = W x reduced along K, W stored as packed signed 4-bit values with one fp16 scale per
+128-wide K group. The pages print no worked example, no test vector and no error bound,
+so the expected values here are hand derivations (tests/golden), IEEE decodes from numpy,
+closed forms and exact invariants.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- test-side helpers
+def pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """Pack signed values q[N][K] in [-8, 7] into uint32 words, one nibble at a time.
+
+    Written as the explicit loop over the 8 positions of a word so it reads against the
+    format statement: value k = 8w + i goes to bits [4i, 4i+3] of word w, as the low 4 bits
+    of its two's-complement byte.
+    """
+    q = np.asarray(q, dtype=np.int64)
+    N, K = q.shape
+    codes = (q & 0xF).astype(np.uint64)            # two's complement, low 4 bits
+    words = np.zeros((N, K // 8), np.uint64)
+    for i in range(8):
+        words |= codes[:, i::8] << np.uint64(4 * i)
+    return words.astype(np.uint32)
+
+
+def f16_bits_pow2(e: int) -> int:
+    """fp16 bit pattern of 2**e for a normal exponent (e in [-14, 15])."""
+    assert -14 <= e <= 15
+    return (e + 15) << 10
+
+
+def bf16_scale_pow2(bits: np.ndarray, a: int) -> np.ndarray:
+    """Multiply bf16 values by 2**a by moving the exponent field (normal values only)."""
+    b = bits.astype(np.int64)
+    expo = (b >> 7) & 0xFF
+    normal = (expo > 0) & (expo < 255)
+    assert np.all((expo[normal] + a > 0) & (expo[normal] + a < 255))
+    out = np.where(normal, b + (a << 7), b)
+    return out.astype(np.uint16)
+
+
+def numpy_dense_weights(words: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
+    """Independent float64 dequantisation with vectorised numpy (for the brute-force check)."""
+    w = words.astype(np.uint64)[:, :, None] >> (np.arange(8, dtype=np.uint64) * 4)
+    u = (w & 0xF).astype(np.int64).reshape(words.shape[0], K)
+    q = np.where(u >= 8, u - 16, u)
+    s = scales.view(np.float16).astype(np.float64)
+    return q * np.repeat(s, 128, axis=1)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    with np.errstate(invalid="ignore"):     # signalling-NaN patterns convert to quiet NaN
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def random_case(N, K, seed, M=None):
+    rng = np.random.default_rng(1000 + seed)
+    q = rng.integers(-8, 8, size=(N, K))
+    s = rng.uniform(0.001, 0.01, size=(N, K // 128)).astype(np.float16).view(np.uint16)
+    shape = (K,) if M is None else (M, K)
+    xf = rng.standard_normal(shape).astype(np.float32)
+    x = (xf.view(np.uint32) >> 16).astype(np.uint16)       # truncation is fine for inputs
+    return q, pack_nibbles(q), s, x
+
+
+# ---------------------------------------------------------------- pins
+def pin_f16_decode(orc):
+    """The hand-written binary16 decoder equals numpy's conversion for all 65536 patterns."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([orc.f16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_bf16_decode(orc):
+    """The bf16 decoder equals the binary32 reading of the same bits, all 65536 patterns."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bf16_bits_to_f64(bits)
+    got = np.array([orc.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_w1(orc):
+    g = _golden("w1_sign_and_nibble_order.json")
+    N, K = g["N"], g["K"]
+    words = np.array([[int(w, 16)] * (K // 8) for w in g["row_word"]], np.uint32)
+    scales = np.array([[int(s, 16)] for s in g["scale_bits"]], np.uint16)
+    one = int(g["cases"][0]["x_bits"], 16)
+    for case in g["cases"]:
+        x = np.zeros(K, np.uint16)
+        if case["x"] == "ones":
+            x[:] = one
+        else:
+            x[int(case["x"].split("_")[1])] = one
+        y, mag = orc.gemv(words, scales, x, K)
+        assert np.array_equal(y, np.array(case["y"])), (case["x"], y)
+        assert np.array_equal(mag, np.array(case["mag"])), (case["x"], mag)
+
+
+def pin_w2(orc):
+    g = _golden("w2_group_scale_index.json")
+    K = g["K"]
+    words = np.array([[int(g["group_word"][k // 16], 16) for k in range(K // 8)]], np.uint32)
+    scales = np.array([[int(s, 16) for s in g["scale_bits"]]], np.uint16)
+    x = np.full(K, int(g["x_bits"], 16), np.uint16)
+    y, _ = orc.gemv(words, scales, x, K)
+    assert y[0] == g["y"], y
+    y2, _ = orc.gemv(words, scales[:, ::-1], x, K)
+    assert y2[0] == g["y_if_scales_swapped"], y2
+
+
+def pin_unpack(orc):
+    """Unpack returns exactly the values the test packed, one nibble at a time."""
+    rng = np.random.default_rng(7)
+    q = rng.integers(-8, 8, size=(6, 256))
+    got = orc.unpack(pack_nibbles(q), 256)
+    assert np.array_equal(got.astype(np.int64), q)
+
+
+def pin_unit_probes(orc):
+    """x = e_j returns column j times its group scale, exactly, for every j.
+
+    Scales are distinct powers of two per (row, group), so a scale taken from the wrong row
+    or group, or a wrong nibble, shows as a different exact value.
+    """
+    N, K = 5, 384
+    rng = np.random.default_rng(11)
+    q = rng.integers(-8, 8, size=(N, K))
+    exps = np.array([[-(2 + (3 * n + 5 * g) % 11) for g in range(K // 128)] for n in range(N)])
+    scales = np.vectorize(f16_bits_pow2)(exps).astype(np.uint16)
+    eye = np.zeros((K, K), np.uint16)
+    eye[np.arange(K), np.arange(K)] = 0x3F80
+    Y, mag = orc.gemv_batched(pack_nibbles(q), scales, eye, K)
+    expect = (q * np.exp2(np.repeat(exps, 128, axis=1))).T     # [K][N]
+    assert np.array_equal(Y, expect)
+    assert np.array_equal(mag, np.abs(expect))
+
+
+def pin_zero_scale_groups(orc):
+    """A zero scale removes its group exactly: same y as zeroing x over that group."""
+    N, K = 7, 512
+    _, words, scales, x = random_case(N, K, 1)
+    s0 = scales.copy()
+    s0[:, 1] = 0x0000
+    s0[:, 3] = 0x8000                                   # -0 as well
+    x0 = x.copy()
+    x0[128:256] = 0
+    x0[384:512] = 0
+    ya, _ = orc.gemv(words, s0, x, K)
+    yb, _ = orc.gemv(words, scales, x0, K)
+    assert np.array_equal(ya, yb)
+    yz, mz = orc.gemv(words, np.zeros_like(scales), x, K)
+    assert np.all(yz == 0) and np.all(mz == 0)
+
+
+def pin_linearity(orc):
+    """y(2^a x) = 2^a y(x) exactly; additivity over disjoint supports."""
+    N, K = 9, 1024
+    _, words, scales, x = random_case(N, K, 2)
+    y, mag = orc.gemv(words, scales, x, K)
+    for a in (3, -5):
+        ya, _ = orc.gemv(words, scales, bf16_scale_pow2(x, a), K)
+        assert np.array_equal(ya, y * 2.0 ** a)
+    x1, x2 = x.copy(), x.copy()
+    x1[1::2] = 0
+    x2[0::2] = 0
+    y1, _ = orc.gemv(words, scales, x1, K)
+    y2, _ = orc.gemv(words, scales, x2, K)
+    assert np.all(np.abs(y1 + y2 - y) <= 1e-12 * mag)
+    assert not np.allclose(y1, y) and not np.allclose(y2, y)
+
+
+def pin_negation(orc):
+    N, K = 9, 640
+    _, words, scales, x = random_case(N, K, 3)
+    y, _ = orc.gemv(words, scales, x, K)
+    yn, _ = orc.gemv(words, scales, x ^ np.uint16(0x8000), K)
+    assert np.array_equal(yn, -y)
+
+
+def pin_constant_rows(orc):
+    """A row whose nibbles all equal q* gives q* * sum_g s_g * sum_{k in g} x_k."""
+    K = 768
+    rng = np.random.default_rng(5)
+    qs = np.array([-8, -3, -1, 0, 1, 5, 7])
+    words = np.array([[(int(v) & 0xF) * 0x11111111] * (K // 8) for v in qs], np.uint32)
+    scales = rng.uniform(0.001, 0.01, size=(len(qs), K // 128)).astype(np.float16)
+    xf = rng.standard_normal(K).astype(np.float32)
+    x = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    xv = bf16_bits_to_f64(x)
+    gsum = xv.reshape(-1, 128).sum(axis=1)
+    expect = qs * (scales.astype(np.float64) * gsum).sum(axis=1)
+    y, mag = orc.gemv(words, scales.view(np.uint16), x, K)
+    assert np.all(np.abs(y - expect) <= 1e-13 * np.maximum(mag, 1e-300))
+    expect_mag = np.abs(qs) * (scales.astype(np.float64) * np.abs(xv).reshape(-1, 128).sum(1)).sum(1)
+    assert np.all(np.abs(mag - expect_mag) <= 1e-13 * np.maximum(expect_mag, 1e-300))
+
+
+def pin_brute_force(orc):
+    """Agrees with an independent vectorised numpy dequantise + BLAS matrix-vector product."""
+    N, K = 64, 2048
+    _, words, scales, x = random_case(N, K, 4)
+    W = numpy_dense_weights(words, scales, K)
+    ref = W @ bf16_bits_to_f64(x)
+    y, mag = orc.gemv(words, scales, x, K)
+    assert np.all(np.abs(y - ref) <= 1e-12 * mag)
+    assert np.all(np.abs(mag - np.abs(W * bf16_bits_to_f64(x)).sum(1)) <= 1e-12 * mag)
+
+
+def pin_mag_nonnegative(orc):
+    """With every term non-negative, mag equals y exactly."""
+    N, K = 4, 256
+    rng = np.random.default_rng(6)
+    q = rng.integers(0, 8, size=(N, K))
+    s = rng.uniform(0.001, 0.01, size=(N, K // 128)).astype(np.float16).view(np.uint16)
+    x = (np.abs(rng.standard_normal(K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y, mag = orc.gemv(pack_nibbles(q), s, x, K)
+    assert np.array_equal(y, mag)
+
+
+def pin_batched(orc):
+    """Batched row m equals the single-token product of X[m]; the row stride is honoured."""
+    N, K, M, ld = 6, 512, 3, 640
+    _, words, scales, X = random_case(N, K, 8, M=M)
+    Xp = np.full((M, ld), 0x7FC0, np.uint16)            # NaN padding past K must be ignored
+    Xp[:, :K] = X
+    Y, mag = orc.gemv_batched(words, scales, Xp, K)
+    for m in range(M):
+        y, mg = orc.gemv(words, scales, X[m], K)
+        assert np.array_equal(Y[m], y) and np.array_equal(mag[m], mg)
+
+
+def pin_moe(orc):
+    """Slot t equals the dense product with expert ids[t]; ids outside [0, E) give zeros."""
+    E, N, K = 5, 4, 256
+    rng = np.random.default_rng(9)
+    q = rng.integers(-8, 8, size=(E, N, K))
+    words = np.stack([pack_nibbles(q[e]) for e in range(E)])
+    scales = rng.uniform(0.001, 0.01, size=(E, N, K // 128)).astype(np.float16).view(np.uint16)
+    x = (rng.standard_normal(K).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ids = np.array([3, 0, -1, 4, 3, 1], np.int32)
+    y, mag = orc.moe_gemv(words, scales, ids, x, K)
+    for t, e in enumerate(ids):
+        if 0 <= e < E:
+            ref, rm = orc.gemv(words[e], scales[e], x, K)
+            assert np.array_equal(y[t], ref) and np.array_equal(mag[t], rm)
+        else:
+            assert np.all(y[t] == 0) and np.all(mag[t] == 0)
+    assert not np.array_equal(y[0], y[1])
+
+
+def pin_row_subset(orc):
+    N, K = 11, 384
+    _, words, scales, x = random_case(N, K, 10)
+    y, mag = orc.gemv(words, scales, x, K)
+    rows = [10, 0, 5, 5]
+    ys, ms = orc.gemv(words, scales, x, K, rows=rows)
+    assert np.array_equal(ys, y[rows]) and np.array_equal(ms, mag[rows])
+
+
+ALL_PINS = [
+    pin_f16_decode, pin_bf16_decode, pin_w1, pin_w2, pin_unpack, pin_unit_probes,
+    pin_zero_scale_groups, pin_linearity, pin_negation, pin_constant_rows, pin_brute_force,
+    pin_mag_nonnegative, pin_batched, pin_moe, pin_row_subset,
+]

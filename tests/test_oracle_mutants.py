@@ -1,0 +1,50 @@
+"""Planted mistakes in the oracle's C source must each fail at least one pin (CPU only).
+
+Every mutant is a copy of w4a16_oracle.c with one plausible slip (a wrong nibble order,
+sign encoding, scale index, exponent bias, a dropped term, a transposed operand ...),
+compiled to a temporary library. None of them may pass every pin.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTANTS = {
+    "nibble_order_high_first": ("(4 * (k % 8))", "(4 * (7 - k % 8))"),
+    "offset_binary_sign": ("u >= 8 ? u - 16 : u", "u - 8"),
+    "sign_ignored": ("u >= 8 ? u - 16 : u", "u"),
+    "scale_row_stride": ("scales + n * (K / G), x, K, G, &y[r]", "scales + n, x, K, G, &y[r]"),
+    "scale_group_index": ("double s = oracle_f16_to_double(srow[g]);",
+                          "double s = oracle_f16_to_double(srow[(g + 1) % (K / G)]);"),
+    "f16_bias": ("expo - 25", "expo - 24"),
+    "f16_subnormal": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "f16_hidden_bit": ("(double)(1024 + frac)", "(double)(frac)"),
+    "bf16_bias": ("expo - 134", "expo - 133"),
+    "bf16_sign": ("    return sign ? -v : v;\n}\n\n/* Signed", "    return v;\n}\n\n/* Signed"),
+    "dropped_last_term": ("k < (g + 1) * G; ++k", "k < (g + 1) * G - 1; ++k"),
+    "x_pair_swap": ("oracle_bf16_to_double(x[k])", "oracle_bf16_to_double(x[k ^ 1])"),
+    "mag_signed": ("m += fabs(p);", "m += p;"),
+    "moe_slot_not_id": ("((int64_t)e * N + n) * (K / 8)", "((int64_t)t * N + n) * (K / 8)"),
+    "batched_ignores_ldx": ("X + m * ldx", "X + m * K"),
+    "word_index": ("row[k / 8]", "row[k / 8 + (k >= 8 ? -1 : 0)]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new, 1))
+    lib = oracle.compile_source(str(path), str(tmp_path / "mutant.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
