@@ -1,0 +1,126 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 decode GEMV library, libw4a16.so.
+ *
+ * The operation is the matrix-vector product that the local-kimi README
+ * (github.1485827954.workers.dev/RightNow-AI/local-kimi), technical-detail section, puts at the centre of
+ * single-stream decode: INT4 weights with 16-bit activations, computed as a true GEMV that
+ * walks the contiguous reduction axis K with one accumulator per output row (its GEMV-rewrite
+ * paragraph), in a dense form and a grouped-expert form over the experts a router selected.
+ * The same section states that the fast path allocates no per-call partial buffers; this
+ * library allocates no device or host memory in any call.
+ *
+ *   y[n] = sum_{k=0}^{K-1} q[n,k] * s[n, k/128] * x[k]
+ *
+ * Storage (all row-major, little-endian):
+ *   qweight  uint32[N][K/8]    value k = 8w + i is bits [4i, 4i+3] of word w of its row, a
+ *                              two's-complement integer in [-8, 7] (no zero point)
+ *   scales   uint16[N][K/128]  IEEE binary16 bit patterns, one per 128-wide group of a row
+ *   x        uint16[K]         bfloat16 bit patterns
+ *   y        float[N]          IEEE binary32, fully overwritten (no accumulate-into)
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is a DEVICE pointer on the current HIP device, owned by the caller,
+ *     who keeps it alive until the work on `stream` has completed.
+ *   - Arguments are validated on the host before anything is enqueued. On any error the
+ *     call returns a non-zero status and enqueues nothing.
+ *   - On W4A16_OK the work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without synchronising. Faults inside a kernel surface at the caller's next
+ *     synchronisation, as for any HIP launch.
+ *   - Results are computed in fp32 from exact products (|q| <= 8 and a binary16 scale and a
+ *     bfloat16 activation multiply exactly in fp32); only the order of the fp32 sums differs
+ *     from the plain definition, and that order is fixed, so repeated calls give identical
+ *     bits. Activations must be finite and |x| <= 2^100: the kernels carry a constant offset
+ *     of 136 per weight through the sum and remove it with the group sums of x, so an
+ *     infinite or NaN activation turns every output that reads it into NaN.
+ *   - Calls are thread-safe. The library keeps one cached record of device properties per
+ *     device and no other global state.
+ *   - No C++ exception crosses this boundary and nothing is printed.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same definition as hip_runtime_api.h, so this header stands alone. */
+typedef struct ihipStream_t *hipStream_t;
+
+#define W4A16_ABI_VERSION 1
+#define W4A16_GROUP_SIZE 128
+#define W4A16_MAX_BATCH 16
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL_POINTER = 1,       /* a required pointer is NULL                          */
+    W4A16_ERR_BAD_SHAPE = 2,          /* N, K, M, topk, E, ldx or ldy out of range (below)    */
+    W4A16_ERR_BAD_GROUP = 3,          /* group_size != 128                                    */
+    W4A16_ERR_MISALIGNED = 4,         /* qweight/x/X not 16-byte aligned, ldx % 8 != 0,
+                                         scales not 2-byte aligned, y/Y not 4-byte aligned    */
+    W4A16_ERR_UNSUPPORTED_DEVICE = 5, /* no current HIP device, or it is not gfx950           */
+    W4A16_ERR_LAUNCH = 6              /* the HIP runtime refused the kernel launch            */
+} w4a16_status_t;
+
+/*
+ * Dense single-token GEMV: y = W x.
+ *   qweight uint32[N][K/8], scales fp16 bits [N][K/128], x bf16 bits [K], y float[N].
+ *   1 <= N <= 2^31 - 1;  128 <= K <= 65536, K % 128 == 0;  group_size == 128.
+ */
+w4a16_status_t w4a16_gemv(const uint32_t *qweight, const uint16_t *scales, const uint16_t *x,
+                          float *y, int64_t N, int64_t K, int32_t group_size,
+                          hipStream_t stream);
+
+/*
+ * Small-batch GEMV for decode of M tokens at once: Y = X W^T.
+ *   X bf16 bits, M rows with row stride ldx elements (ldx >= K, ldx % 8 == 0);
+ *   Y float, M rows with row stride ldy elements (ldy >= N).
+ *   1 <= M <= 16; N and K as for w4a16_gemv (K up to 2^20 when M >= 2).
+ *   Row m of Y equals w4a16_gemv of row m of X to within the fp32 summation order.
+ */
+w4a16_status_t w4a16_gemv_batched(const uint32_t *qweight, const uint16_t *scales,
+                                  const uint16_t *X, int64_t ldx, float *Y, int64_t ldy,
+                                  int32_t M, int64_t N, int64_t K, int32_t group_size,
+                                  hipStream_t stream);
+
+/*
+ * Grouped-expert GEMV for one token: y[t] = W_{expert_ids[t]} x for t < topk.
+ *   qweight uint32[E][N][K/8], scales fp16 bits [E][N][K/128] (experts contiguous);
+ *   expert_ids int32[topk] in DEVICE memory (read by the kernel, no host synchronisation);
+ *   x bf16 bits [K]; y float[topk][N].
+ *   Only the weights and scales of the listed experts are read. An id outside [0, E) names
+ *   no expert and its output row is written as +0.0f. Repeated ids are computed independently.
+ *   1 <= topk <= 1024; 1 <= E; N, K as for w4a16_gemv.
+ */
+w4a16_status_t w4a16_moe_gemv(const uint32_t *qweight, const uint16_t *scales,
+                              const int32_t *expert_ids, int32_t topk, int32_t num_experts,
+                              const uint16_t *x, float *y, int64_t N, int64_t K,
+                              int32_t group_size, hipStream_t stream);
+
+/*
+ * Test support: q_out int8[N][K] receives the signed value of every packed nibble, so the
+ * unpacking can be checked bit for bit. 1 <= N, 8 <= K, K % 8 == 0; qweight 16-byte aligned.
+ */
+w4a16_status_t w4a16_unpack_debug(const uint32_t *qweight, int8_t *q_out, int64_t N, int64_t K,
+                                  hipStream_t stream);
+
+/*
+ * Host-only introspection: writes into buf (at most len bytes, NUL-terminated) the kernel and
+ * launch shape the entry points would choose for (M, N, K, topk) on a device with `cus` compute
+ * units; topk = 0 means a dense call. Returns W4A16_OK or W4A16_ERR_BAD_SHAPE. Touches no device.
+ */
+w4a16_status_t w4a16_describe_plan(int32_t M, int64_t N, int64_t K, int32_t topk, int32_t cus,
+                                   char *buf, int64_t len);
+
+/* Static, never-NULL description of a status code. */
+const char *w4a16_status_string(w4a16_status_t status);
+
+/* W4A16_ABI_VERSION of the loaded library. */
+int32_t w4a16_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,139 @@
+"""The C-ABI library without a GPU: exported symbols, host-side validation, dispatch plan."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import weight_only_int4_w4a16_amd as w
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+OK, NULLP, SHAPE, GROUP, ALIGN, DEVICE, LAUNCH = range(7)
+A = 0x10000          # a fake, 16-byte aligned address: validation never dereferences it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:w4a16_status_t|const char \*|int32_t)\s*\*?\s*"
+                                 r"(w4a16_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("w4a16_gemv", "w4a16_gemv_batched", "w4a16_moe_gemv", "w4a16_unpack_debug",
+              "w4a16_describe_plan", "w4a16_status_string", "w4a16_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = w.library()
+    out = subprocess.run(["nm", "-D", "--defined-only", w.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        getattr(lib, n)
+    assert lib.w4a16_abi_version() == 1
+
+
+def test_library_has_no_oracle_dependency():
+    out = subprocess.run(["nm", "-D", w.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in out
+    deps = subprocess.run(["ldd", w.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in deps
+
+
+def test_status_strings():
+    lib = w.library()
+    for s in range(7):
+        assert lib.w4a16_status_string(s)
+    assert b"unknown" in lib.w4a16_status_string(99)
+
+
+def gemv(qw=A, sc=A, x=A, y=A, N=64, K=256, G=128):
+    return w.library().w4a16_gemv(qw, sc, x, y, N, K, G, None)
+
+
+def batched(qw=A, sc=A, X=A, ldx=256, Y=A, ldy=64, M=4, N=64, K=256, G=128):
+    return w.library().w4a16_gemv_batched(qw, sc, X, ldx, Y, ldy, M, N, K, G, None)
+
+
+def moe(qw=A, sc=A, ids=A, topk=8, E=16, x=A, y=A, N=64, K=256, G=128):
+    return w.library().w4a16_moe_gemv(qw, sc, ids, topk, E, x, y, N, K, G, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qw=None), NULLP), (dict(sc=None), NULLP), (dict(x=None), NULLP), (dict(y=None), NULLP),
+    (dict(G=64), GROUP), (dict(G=0), GROUP),
+    (dict(N=0), SHAPE), (dict(N=-5), SHAPE), (dict(N=1 << 31), SHAPE),
+    (dict(K=0), SHAPE), (dict(K=64), SHAPE), (dict(K=200), SHAPE), (dict(K=65536 + 128), SHAPE),
+    (dict(qw=A + 8), ALIGN), (dict(x=A + 4), ALIGN), (dict(sc=A + 1), ALIGN), (dict(y=A + 2), ALIGN),
+])
+def test_gemv_validation(kw, status):
+    assert gemv(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), NULLP), (dict(M=0), SHAPE), (dict(M=17), SHAPE), (dict(ldx=255), SHAPE),
+    (dict(ldy=63), SHAPE), (dict(ldx=260), ALIGN), (dict(X=A + 8), ALIGN), (dict(G=256), GROUP),
+])
+def test_batched_validation(kw, status):
+    assert batched(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ids=None), NULLP), (dict(topk=0), SHAPE), (dict(topk=1025), SHAPE), (dict(E=0), SHAPE),
+    (dict(ids=A + 2), ALIGN), (dict(K=384 + 64), SHAPE), (dict(N=1 << 30, topk=4), SHAPE),
+])
+def test_moe_validation(kw, status):
+    assert moe(**kw) == status
+
+
+def test_unpack_validation():
+    lib = w.library()
+    assert lib.w4a16_unpack_debug(None, A, 4, 64, None) == NULLP
+    assert lib.w4a16_unpack_debug(A, A, 4, 12, None) == SHAPE
+    assert lib.w4a16_unpack_debug(A, A, 0, 64, None) == SHAPE
+    assert lib.w4a16_unpack_debug(A + 2, A, 4, 64, None) == ALIGN
+
+
+def test_valid_arguments_reach_the_device_check_only():
+    # With well-formed arguments the call gets past validation; on a host without a gfx950 GPU
+    # it must stop at the device check and enqueue nothing.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert gemv() == DEVICE
+    assert batched() == DEVICE
+    assert moe() == DEVICE
+
+
+@pytest.mark.parametrize("M,N,K,topk,kind", [
+    (1, 1024, 2048, 0, "valu "), (1, 4096, 4096, 0, "valu "), (1, 28672, 4096, 0, "valu "),
+    (1, 4096, 14336, 0, "valu "), (1, 8192, 8192, 0, "valu "), (1, 163840, 2304, 0, "valu "),
+    (1, 2048, 2304, 8, "valu_moe"), (1, 5, 128, 0, "valu "),
+    (16, 8192, 8192, 0, "mfma"), (16, 163840, 2304, 0, "mfma"), (8, 8192, 8192, 0, "mfma"),
+])
+def test_default_dispatch(M, N, K, topk, kind):
+    """The shipped entry points pick the tuned kernels with no configuration (no env switch)."""
+    plan = w.describe_plan(M, N, K, topk, cus=256)
+    assert plan.startswith(kind), plan
+    if kind.startswith("valu"):
+        assert f"tokens={M}" in plan
+
+
+def test_every_valid_shape_has_a_plan():
+    for M in range(1, 17):
+        for K in (128, 256, 384, 1152, 2304, 4096, 14336, 65536 if M == 1 else 131072):
+            assert w.describe_plan(M, 777, K, 0, 256)
+    for K in (128, 2304, 65536):
+        assert w.describe_plan(1, 33, K, 8, 256).startswith("valu_moe")
+
+
+def test_describe_rejects_bad_shapes():
+    for args in ((0, 10, 128), (17, 10, 128), (1, 0, 128), (1, 10, 100), (2, 10, 128, 4)):
+        with pytest.raises(w.W4A16Error):
+            w.describe_plan(*args)

@@ -1,0 +1,178 @@
+"""MI355X (gfx950) W4A16 decode GEMV.
+
+Thin ctypes binding over libw4a16.so (C ABI in include/w4a16.h). This module only checks and
+marshals arguments; every step of the computation runs in the HIP kernels of the library.
+PyTorch supplies device memory and the current stream.
+
+Tensor conventions:
+  qweight  torch.int32  [N, K/8]       packed signed 4-bit values (uint32 bit patterns)
+  scales   torch.float16 [N, K/128]    one scale per 128-wide K group
+  x        torch.bfloat16 [K]          activations (batched: [M, ldx], unit stride along K)
+  out      torch.float32 [N]           (batched: [M, N] with any row stride >= N)
+  MoE      qweight [E, N, K/8], scales [E, N, K/128], expert_ids torch.int32 [topk] on the GPU,
+           out [topk, N]
+
+If libw4a16.so has not been built, every call raises ImportError; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["gemv", "gemv_batched", "moe_gemv", "unpack_debug", "describe_plan", "W4A16Error",
+           "library", "LIB_PATH", "GROUP_SIZE", "MAX_BATCH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")
+GROUP_SIZE = 128
+MAX_BATCH = 16
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libw4a16.so; raises ImportError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m weight_only_int4_w4a16_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.w4a16_gemv.argtypes = [P, P, P, P, i64, i64, i32, P]
+    lib.w4a16_gemv_batched.argtypes = [P, P, P, i64, P, i64, i32, i64, i64, i32, P]
+    lib.w4a16_moe_gemv.argtypes = [P, P, P, i32, i32, P, P, i64, i64, i32, P]
+    lib.w4a16_unpack_debug.argtypes = [P, P, i64, i64, P]
+    lib.w4a16_describe_plan.argtypes = [i32, i64, i64, i32, i32, ctypes.c_char_p, i64]
+    lib.w4a16_status_string.argtypes = [ctypes.c_int]
+    lib.w4a16_status_string.restype = ctypes.c_char_p
+    lib.w4a16_abi_version.argtypes = []
+    for f in (lib.w4a16_gemv, lib.w4a16_gemv_batched, lib.w4a16_moe_gemv,
+              lib.w4a16_unpack_debug, lib.w4a16_describe_plan, lib.w4a16_abi_version):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().w4a16_status_string(int(status)).decode()
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+
+
+def _ok(status: int, where: str):
+    if status != 0:
+        raise W4A16Error(status, where)
+
+
+def gemv(qweight: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
+         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = W x for one token. Returns out (allocated as float32 [N] when not given)."""
+    _need(qweight, torch.int32, "qweight", 2)
+    _need(scales, torch.float16, "scales", 2)
+    _need(x, torch.bfloat16, "x", 1)
+    N, K = qweight.shape[0], qweight.shape[1] * 8
+    if not (qweight.is_contiguous() and scales.is_contiguous() and x.is_contiguous()):
+        raise ValueError("qweight, scales and x must be contiguous")
+    if tuple(scales.shape) != (N, K // GROUP_SIZE) or x.numel() != K:
+        raise ValueError(f"shape mismatch: qweight {tuple(qweight.shape)}, scales "
+                         f"{tuple(scales.shape)}, x {tuple(x.shape)}")
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=qweight.device)
+    _need(out, torch.float32, "out", 1)
+    if out.numel() != N or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of N elements")
+    _ok(library().w4a16_gemv(qweight.data_ptr(), scales.data_ptr(), x.data_ptr(),
+                             out.data_ptr(), N, K, GROUP_SIZE, _stream(stream)), "w4a16_gemv")
+    return out
+
+
+def gemv_batched(qweight: torch.Tensor, scales: torch.Tensor, X: torch.Tensor,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y = X W^T for M <= 16 tokens. X [M, >=K] bf16 with unit stride along K."""
+    _need(qweight, torch.int32, "qweight", 2)
+    _need(scales, torch.float16, "scales", 2)
+    _need(X, torch.bfloat16, "X", 2)
+    N, K = qweight.shape[0], qweight.shape[1] * 8
+    M = X.shape[0]
+    if not (qweight.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("qweight and scales must be contiguous")
+    if tuple(scales.shape) != (N, K // GROUP_SIZE) or X.shape[1] < K or X.stride(1) != 1:
+        raise ValueError("shape mismatch between qweight, scales and X")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=qweight.device)
+    _need(out, torch.float32, "out", 2)
+    if out.shape[0] != M or out.shape[1] != N or out.stride(1) != 1:
+        raise ValueError("out must be float32 [M, N] with unit stride along N")
+    ldx = X.stride(0) if M > 1 else max(X.stride(0), K)
+    ldy = out.stride(0) if M > 1 else max(out.stride(0), N)
+    _ok(library().w4a16_gemv_batched(qweight.data_ptr(), scales.data_ptr(), X.data_ptr(), ldx,
+                                     out.data_ptr(), ldy, M, N, K, GROUP_SIZE, _stream(stream)),
+        "w4a16_gemv_batched")
+    return out
+
+
+def moe_gemv(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tensor,
+             x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[t] = W_{expert_ids[t]} x for every selected expert; reads only those experts."""
+    _need(qweight, torch.int32, "qweight", 3)
+    _need(scales, torch.float16, "scales", 3)
+    _need(expert_ids, torch.int32, "expert_ids", 1)
+    _need(x, torch.bfloat16, "x", 1)
+    E, N, K = qweight.shape[0], qweight.shape[1], qweight.shape[2] * 8
+    topk = expert_ids.numel()
+    if not all(t.is_contiguous() for t in (qweight, scales, expert_ids, x)):
+        raise ValueError("qweight, scales, expert_ids and x must be contiguous")
+    if tuple(scales.shape) != (E, N, K // GROUP_SIZE) or x.numel() != K:
+        raise ValueError("shape mismatch between qweight, scales and x")
+    if out is None:
+        out = torch.empty((topk, N), dtype=torch.float32, device=qweight.device)
+    _need(out, torch.float32, "out", 2)
+    if tuple(out.shape) != (topk, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [topk, N] tensor")
+    _ok(library().w4a16_moe_gemv(qweight.data_ptr(), scales.data_ptr(), expert_ids.data_ptr(),
+                                 topk, E, x.data_ptr(), out.data_ptr(), N, K, GROUP_SIZE,
+                                 _stream(stream)), "w4a16_moe_gemv")
+    return out
+
+
+def unpack_debug(qweight: torch.Tensor, stream=None) -> torch.Tensor:
+    """int8 [N, K]: the signed value of every packed nibble, decoded by the GEMV unpack."""
+    _need(qweight, torch.int32, "qweight", 2)
+    if not qweight.is_contiguous():
+        raise ValueError("qweight must be contiguous")
+    N, K = qweight.shape[0], qweight.shape[1] * 8
+    out = torch.empty((N, K), dtype=torch.int8, device=qweight.device)
+    _ok(library().w4a16_unpack_debug(qweight.data_ptr(), out.data_ptr(), N, K, _stream(stream)),
+        "w4a16_unpack_debug")
+    return out
+
+
+def describe_plan(M: int, N: int, K: int, topk: int = 0, cus: int = 256) -> str:
+    """The kernel and launch shape the library picks for a call (host-only, no device)."""
+    buf = ctypes.create_string_buffer(256)
+    _ok(library().w4a16_describe_plan(M, N, K, topk, cus, buf, len(buf)), "w4a16_describe_plan")
+    return buf.value.decode()

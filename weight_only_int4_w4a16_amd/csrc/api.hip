@@ -1,0 +1,184 @@
+// C ABI of libw4a16.so (declared in include/w4a16.h): host-side validation, device checks and
+// kernel dispatch. Nothing here allocates device or host memory.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "plan.h"
+#include "w4a16.h"
+
+namespace w4a16 {
+hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream);
+hipError_t launch_unpack(const uint32_t *qw, int8_t *out, int64_t words, int cus,
+                         hipStream_t stream);
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxN = (1LL << 31) - 1;
+constexpr int64_t kMaxKDense = 65536;
+constexpr int64_t kMaxKBatched = 1LL << 20;
+constexpr int32_t kMaxTopk = 1024;
+
+struct DeviceInfo {
+    bool ok;
+    int cus;
+    int64_t lds_limit;
+};
+
+std::once_flag g_once[kMaxDevices];
+DeviceInfo g_info[kMaxDevices];
+
+void probe_device(int dev)
+{
+    DeviceInfo info{false, 0, 0};
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+        strncmp(prop.gcnArchName, "gfx950", 6) == 0) {
+        info.ok = true;
+        info.cus = prop.multiProcessorCount;
+        info.lds_limit = (int64_t)prop.sharedMemPerBlock;
+    }
+    g_info[dev] = info;
+}
+
+// Current device's cached properties, or null when it is missing or not gfx950.
+const DeviceInfo *current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::call_once(g_once[dev], probe_device, dev);
+    return g_info[dev].ok ? &g_info[dev] : nullptr;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+w4a16_status_t check_common(const void *qweight, const void *scales, const void *x,
+                            const void *y, int64_t N, int64_t K, int32_t group_size,
+                            int64_t max_k)
+{
+    if (!qweight || !scales || !x || !y)
+        return W4A16_ERR_NULL_POINTER;
+    if (group_size != W4A16_GROUP_SIZE)
+        return W4A16_ERR_BAD_GROUP;
+    if (N < 1 || N > kMaxN || K < W4A16_GROUP_SIZE || K % W4A16_GROUP_SIZE != 0 || K > max_k)
+        return W4A16_ERR_BAD_SHAPE;
+    if (!aligned(qweight, 16) || !aligned(x, 16) || !aligned(scales, 2) || !aligned(y, 4))
+        return W4A16_ERR_MISALIGNED;
+    return W4A16_OK;
+}
+
+w4a16_status_t run(const GemvArgs &a, int M, int topk, hipStream_t stream)
+{
+    const DeviceInfo *dev = current_device();
+    if (!dev)
+        return W4A16_ERR_UNSUPPORTED_DEVICE;
+    Plan plan;
+    if (!make_plan(M, a.N, a.K, topk, dev->cus, dev->lds_limit, &plan))
+        return W4A16_ERR_BAD_SHAPE;
+    return launch(a, plan, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" {
+
+w4a16_status_t w4a16_gemv(const uint32_t *qweight, const uint16_t *scales, const uint16_t *x,
+                          float *y, int64_t N, int64_t K, int32_t group_size, hipStream_t stream)
+{
+    const w4a16_status_t st = check_common(qweight, scales, x, y, N, K, group_size, kMaxKDense);
+    if (st != W4A16_OK)
+        return st;
+    GemvArgs a{qweight, scales, x, K, y, N, nullptr, 0, 0, N, (int32_t)K, 1};
+    return run(a, 1, 0, stream);
+}
+
+w4a16_status_t w4a16_gemv_batched(const uint32_t *qweight, const uint16_t *scales,
+                                  const uint16_t *X, int64_t ldx, float *Y, int64_t ldy,
+                                  int32_t M, int64_t N, int64_t K, int32_t group_size,
+                                  hipStream_t stream)
+{
+    const int64_t max_k = M == 1 ? kMaxKDense : kMaxKBatched;
+    w4a16_status_t st = check_common(qweight, scales, X, Y, N, K, group_size, max_k);
+    if (st != W4A16_OK)
+        return st;
+    if (M < 1 || M > W4A16_MAX_BATCH || ldx < K || ldy < N)
+        return W4A16_ERR_BAD_SHAPE;
+    if (ldx % 8 != 0)
+        return W4A16_ERR_MISALIGNED;
+    GemvArgs a{qweight, scales, X, ldx, Y, ldy, nullptr, 0, 0, N, (int32_t)K, M};
+    return run(a, M, 0, stream);
+}
+
+w4a16_status_t w4a16_moe_gemv(const uint32_t *qweight, const uint16_t *scales,
+                              const int32_t *expert_ids, int32_t topk, int32_t num_experts,
+                              const uint16_t *x, float *y, int64_t N, int64_t K,
+                              int32_t group_size, hipStream_t stream)
+{
+    w4a16_status_t st = check_common(qweight, scales, x, y, N, K, group_size, kMaxKDense);
+    if (st != W4A16_OK)
+        return st;
+    if (!expert_ids)
+        return W4A16_ERR_NULL_POINTER;
+    if (topk < 1 || topk > kMaxTopk || num_experts < 1 || (int64_t)topk * N > kMaxN)
+        return W4A16_ERR_BAD_SHAPE;
+    if (!aligned(expert_ids, 4))
+        return W4A16_ERR_MISALIGNED;
+    GemvArgs a{qweight, scales, x, K, y, N, expert_ids, topk, num_experts, N, (int32_t)K, 1};
+    return run(a, 1, topk, stream);
+}
+
+w4a16_status_t w4a16_unpack_debug(const uint32_t *qweight, int8_t *q_out, int64_t N, int64_t K,
+                                  hipStream_t stream)
+{
+    if (!qweight || !q_out)
+        return W4A16_ERR_NULL_POINTER;
+    if (N < 1 || K < 8 || K % 8 != 0 || N > kMaxN || K > kMaxKBatched)
+        return W4A16_ERR_BAD_SHAPE;
+    if (!aligned(qweight, 4))
+        return W4A16_ERR_MISALIGNED;
+    const DeviceInfo *dev = current_device();
+    if (!dev)
+        return W4A16_ERR_UNSUPPORTED_DEVICE;
+    return launch_unpack(qweight, q_out, N * (K / 8), dev->cus, stream) == hipSuccess
+               ? W4A16_OK
+               : W4A16_ERR_LAUNCH;
+}
+
+w4a16_status_t w4a16_describe_plan(int32_t M, int64_t N, int64_t K, int32_t topk, int32_t cus,
+                                   char *buf, int64_t len)
+{
+    if (!buf || len < 1)
+        return W4A16_ERR_NULL_POINTER;
+    buf[0] = '\0';
+    Plan plan;
+    // 160 KiB of LDS per work-group, as on gfx950.
+    if (cus < 1 || !make_plan(M, N, K, topk, cus, 160 * 1024, &plan))
+        return W4A16_ERR_BAD_SHAPE;
+    describe_plan(plan, buf, (size_t)len);
+    return W4A16_OK;
+}
+
+const char *w4a16_status_string(w4a16_status_t status)
+{
+    switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_NULL_POINTER: return "null pointer argument";
+    case W4A16_ERR_BAD_SHAPE: return "shape out of range";
+    case W4A16_ERR_BAD_GROUP: return "group size must be 128";
+    case W4A16_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case W4A16_ERR_UNSUPPORTED_DEVICE: return "current device is missing or not gfx950";
+    case W4A16_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+}  // extern "C"

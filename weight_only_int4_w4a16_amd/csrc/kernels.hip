@@ -1,0 +1,511 @@
+// W4A16 GEMV kernels for gfx950 (CDNA4, wave64).
+//
+// The operation (local-kimi README, technical-detail section, GEMV-rewrite paragraph): a true
+// matrix-vector product over packed INT4 weights, walking the contiguous reduction axis K with a
+// single accumulator per output row, instead of a matrix-matrix kernel applied to one token.
+//
+// Decode path shared by every kernel here. A 32-bit word holds 8 two's-complement nibbles; one
+// v_bitop3 per pair turns nibbles (i, i+4) into two bf16 values 136 + q:
+//     ((w >> 4i) & 0x000F000F) ^ 0x43084308
+// The mask keeps nibble i in bits 0-3 of the low half and nibble i+4 in bits 0-3 of the high half;
+// the XOR sets the bf16 exponent of 128 (0x4300, one mantissa step = 1.0) and flips bit 3, which
+// maps the two's-complement code to q + 8. So each half reads 128 + (q + 8) = 136 + q exactly.
+// The products (136 + q) * x are formed by v_dot2c_f32_bf16 against activation pairs (x_i, x_{i+4})
+// staged in that order, and the constant part 136 * sum(x) of each 32-value chunk is removed by
+// starting the chunk's accumulator at -136 * sum(x). The chunk total is then scaled by its fp16
+// group scale in fp32. All products are exact in fp32; only the summation order differs from the
+// plain definition.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace w4a16 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+static constexpr uint32_t kMask = 0x000F000Fu;
+static constexpr uint32_t kMagic = 0x43084308u;   // bf16 pair (128, 128) with bit 3 flipped
+static constexpr float kOffset = 136.0f;
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Weights are read exactly once per call: stream them past the caches when asked to.
+#ifndef W4A16_STREAM_LOADS
+#define W4A16_STREAM_LOADS 1
+#endif
+__device__ __forceinline__ uint4 load_weights(const uint4 *p)
+{
+#if W4A16_STREAM_LOADS
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b16)
+{
+    return __builtin_bit_cast(float, b16 << 16);
+}
+
+// Nibble pairs (0,4) (1,5) (2,6) (3,7) of w as bf16 pairs holding 136 + q.
+__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t p[4])
+{
+    p[0] = (w & kMask) ^ kMagic;
+    p[1] = ((w >> 4) & kMask) ^ kMagic;
+    p[2] = ((w >> 8) & kMask) ^ kMagic;
+    p[3] = ((w >> 12) & kMask) ^ kMagic;
+}
+
+// Eight consecutive bf16 activations (x0..x7 in natural order) re-paired as
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7) to match unpack_word.
+__device__ __forceinline__ uint4 pair_activations(uint4 v)
+{
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+    o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+    o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+    o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+    return o;
+}
+
+__device__ __forceinline__ float chunk_dot(uint4 wv, const uint4 xq[4], float acc)
+{
+    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t p[4];
+        unpack_word(wd[j], p);
+        acc = dot2(p[0], xq[j].x, acc);
+        acc = dot2(p[1], xq[j].y, acc);
+        acc = dot2(p[2], xq[j].z, acc);
+        acc = dot2(p[3], xq[j].w, acc);
+    }
+    return acc;
+}
+
+// ------------------------------------------------------------------------------------------
+// VALU GEMV: MT tokens (1..4), one wave streams U*R rows at a time, R = 64/L rows side by side,
+// L lanes per row. Lane p of a row owns the 16-byte chunks p, p+L, p+2L, ... of that row, so each
+// load instruction of the wave covers R runs of L*16 contiguous bytes (whole cache lines).
+// Activations live in LDS, re-paired, laid out [token][word-in-chunk j][chunk c] so the L lanes of a
+// row read consecutive 16-byte slots; per-chunk offsets -136*sum(x) follow them.
+// A wave walks a flat sequence of (row block, chunk batch) items and prefetches the next item's
+// weights and scales before computing the current one. No global scratch, no atomics.
+// ------------------------------------------------------------------------------------------
+template <int L, int V, int U>
+struct ValuBuf {
+    uint4 w[V][U];
+    uint16_t s[V][U];
+};
+
+template <int MT, int L, int V, int U, bool MOE>
+__global__ void __launch_bounds__(256)
+gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
+                 const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
+                 const int32_t *__restrict__ ids, int32_t topk, int32_t E, int64_t N, int32_t K)
+{
+    constexpr int R = 64 / L;
+    constexpr int ROWS = U * R;
+    extern __shared__ uint4 smem[];
+    const int KW = K >> 3;    // words per row
+    const int CPR = K >> 5;   // 16-byte chunks per row
+    const int GPR = K >> 7;   // scale groups per row
+    uint4 *xs = smem;                                          // [MT][4][CPR]
+    float *bs = reinterpret_cast<float *>(smem + MT * KW);    // [MT][CPR]
+
+    // ---- stage activations: re-pair, transpose to [j][c], and form per-chunk offsets
+    for (int t = 0; t < MT; ++t) {
+        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
+        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
+            const uint4 v = xg[w];
+            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+            float sum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sum += bf16_bits_to_float(d[e] & 0xFFFFu);
+                sum += bf16_bits_to_float(d[e] >> 16);
+            }
+            // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            if ((w & 3) == 0)
+                bs[t * CPR + (w >> 2)] = -kOffset * sum;
+        }
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int pr = lane & (L - 1);
+    const int rr = lane / L;
+    const int wpb = blockDim.x >> 6;
+    const int64_t gw = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6);
+    const int64_t GW = (int64_t)gridDim.x * wpb;
+    const int64_t rows_total = MOE ? (int64_t)topk * N : N;
+    const int64_t n_super = (rows_total + ROWS - 1) / ROWS;
+    const int nb = CPR / (L * V);
+    if (gw >= n_super)
+        return;
+
+    // Row pointers of a row block for loading.
+    struct Rows {
+        const uint4 *w[U];
+        const uint16_t *s[U];
+        bool ok[U];
+    };
+    auto rows_of = [&](int64_t st, Rows &r) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t vrow = st * ROWS + u * R + rr;
+            int64_t row = 0;
+            bool ok = vrow < rows_total;
+            if (MOE) {
+                const int64_t slot = ok ? vrow / N : 0;
+                const int64_t n = vrow - slot * N;
+                const int32_t e = ok ? ids[slot] : -1;
+                ok = ok && e >= 0 && e < E;
+                row = ok ? (int64_t)e * N + n : 0;
+            } else {
+                row = ok ? vrow : 0;
+            }
+            r.w[u] = qw + row * CPR;
+            r.s[u] = sc + row * GPR;
+            r.ok[u] = ok;
+        }
+    };
+    auto load = [&](const Rows &r, int b, ValuBuf<L, V, U> &buf) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int c = pr + L * (v + V * b);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (r.ok[u]) {
+                    buf.w[v][u] = load_weights(r.w[u] + c);
+                    buf.s[v][u] = r.s[u][c >> 2];
+                } else {
+                    buf.w[v][u] = make_uint4(0, 0, 0, 0);
+                    buf.s[v][u] = 0;
+                }
+            }
+        }
+    };
+
+    float acc[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            acc[u][t] = 0.0f;
+
+    auto compute = [&](int b, const ValuBuf<L, V, U> &buf) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int c = pr + L * (v + V * b);
+            uint4 xq[MT][4];
+            float off[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xq[t][j] = xs[t * KW + j * CPR + c];
+                off[t] = bs[t * CPR + c];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float s = half_bits_to_float(buf.s[v][u]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[u][t] = fmaf(s, chunk_dot(buf.w[v][u], xq[t], off[t]), acc[u][t]);
+            }
+        }
+    };
+
+    auto finish = [&](int64_t st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                float v = acc[u][t];
+#pragma unroll
+                for (int off = L / 2; off >= 1; off >>= 1)
+                    v += __shfl_xor(v, off);
+                acc[u][t] = v;
+            }
+        }
+        if (pr == 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t vrow = st * ROWS + u * R + rr;
+                if (vrow < rows_total) {
+                    bool zero = false;
+                    if (MOE) {
+                        const int32_t e = ids[vrow / N];
+                        zero = e < 0 || e >= E;
+                    }
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+                        Y[t * ldy + vrow] = zero ? 0.0f : acc[u][t];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                acc[u][t] = 0.0f;
+    };
+
+    // Flat walk over (row block, batch) items with one item of prefetch.
+    int64_t st = gw;
+    int b = 0;
+    Rows cur;
+    rows_of(st, cur);
+    ValuBuf<L, V, U> bufA, bufB;
+    load(cur, 0, bufA);
+    auto step = [&](ValuBuf<L, V, U> &now, ValuBuf<L, V, U> &next) -> bool {
+        int64_t nst = st;
+        int nbb = b + 1;
+        if (nbb == nb) {
+            nbb = 0;
+            nst += GW;
+        }
+        const bool more = nst < n_super;
+        if (more) {
+            if (nst != st)
+                rows_of(nst, cur);
+            load(cur, nbb, next);
+        }
+        compute(b, now);
+        if (b == nb - 1)
+            finish(st);
+        st = nst;
+        b = nbb;
+        return more;
+    };
+    for (;;) {
+        if (!step(bufA, bufB))
+            break;
+        if (!step(bufB, bufA))
+            break;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// MFMA GEMV for 2..16 tokens (v_mfma_f32_16x16x32_bf16). A = 16 weight rows x 32 K values: lane
+// (i = l%16, g = l/16) unpacks word j of chunk 4s+g of row i into 8 bf16 (136+q, re-paired); B = the
+// same K positions of token i's activations (loaded from global memory and re-paired in registers);
+// D[4g+r][i] accumulates over the 4 words of the group. The 136 offset is removed by starting D at
+// -(136 * column sums), themselves one MFMA chain against a constant-136 A operand per group, shared
+// by every tile. The group total is scaled by the row's fp16 scale in fp32.
+// A wave owns T tiles of 16 rows; KS waves of a block split the groups of K and their partial sums
+// are added through LDS in a fixed order.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    u32x4_t v = {a, b, c, d};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int T, int KS>
+__global__ void __launch_bounds__(256)
+gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
+                 const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
+                 int32_t M, int64_t N, int32_t K)
+{
+    constexpr int RG = 4 / KS;   // row groups per block
+    __shared__ f32x4_t red[KS > 1 ? 4 : 1][T][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i = lane & 15;
+    const int g = lane >> 4;
+    const int ks = wave % KS;
+    const int rg = wave / KS;
+    const int CPR = K >> 5;
+    const int GPR = K >> 7;
+    const int gpk = GPR / KS;
+    const int s0 = ks * gpk;
+    const int s1 = s0 + gpk;
+    const int64_t row0 = ((int64_t)blockIdx.x * RG + rg) * (16 * T);
+
+    const uint4 *wp[T];
+    const uint16_t *sp[T][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        int64_t ra = row0 + t * 16 + i;
+        ra = ra < N ? ra : N - 1;
+        wp[t] = qw + ra * CPR + g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int64_t rd = row0 + t * 16 + 4 * g + r;
+            rd = rd < N ? rd : N - 1;
+            sp[t][r] = sc + rd * GPR;
+        }
+    }
+    const bool xon = i < M;
+    const uint4 *xp = reinterpret_cast<const uint4 *>(X + (int64_t)(xon ? i : 0) * ldx) + 4 * g;
+    const bf16x8_t c136 = as_bf16x8(0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u);
+
+    f32x4_t acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int s = s0; s < s1; ++s) {
+        uint4 wv[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            wv[t] = load_weights(wp[t] + 4 * s);
+        bf16x8_t xb[4];
+        f32x4_t off = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 raw = xon ? xp[16 * s + j] : make_uint4(0, 0, 0, 0);
+            const uint4 pq = pair_activations(raw);
+            xb[j] = as_bf16x8(pq.x, pq.y, pq.z, pq.w);
+            off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c136, xb[j], off, 0, 0, 0);
+        }
+        off = -off;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float sv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sv[r] = half_bits_to_float(sp[t][r][s]);
+            const uint32_t wd[4] = {wv[t].x, wv[t].y, wv[t].z, wv[t].w};
+            f32x4_t d = off;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t p[4];
+                unpack_word(wd[j], p);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p[0], p[1], p[2], p[3]),
+                                                             xb[j], d, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[t][r] = fmaf(sv[r], d[r], acc[t][r]);
+        }
+    }
+
+    if (KS > 1) {
+        if (ks != 0) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                red[wave][t][lane] = acc[t];
+        }
+        __syncthreads();
+        if (ks != 0)
+            return;
+#pragma unroll
+        for (int k2 = 1; k2 < KS; ++k2)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                acc[t] += red[rg * KS + k2][t][lane];
+    }
+    if (!xon)
+        return;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = row0 + t * 16 + 4 * g + r;
+            if (row < N)
+                Y[(int64_t)i * ldy + row] = acc[t][r];
+        }
+}
+
+// ------------------------------------------------------------------------------------------
+// Test support: the signed value of every nibble, decoded with the same unpack_word as the GEMVs.
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+unpack_kernel(const uint32_t *__restrict__ qw, int8_t *__restrict__ out, int64_t words)
+{
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words;
+         w += (int64_t)gridDim.x * blockDim.x) {
+        uint32_t p[4];
+        unpack_word(qw[w], p);
+        int8_t q[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            q[i] = (int8_t)((int)bf16_bits_to_float(p[i] & 0xFFFFu) - 136);
+            q[i + 4] = (int8_t)((int)bf16_bits_to_float(p[i] >> 16) - 136);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            out[8 * w + i] = q[i];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers
+// ------------------------------------------------------------------------------------------
+template <int MT, int L, int V, int U, bool MOE>
+static hipError_t launch_valu_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
+{
+    auto kern = gemv_valu_kernel<MT, L, V, U, MOE>;
+    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X,  (void *)&a.ldx,
+                    (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.ids, (void *)&a.topk,
+                    (void *)&a.E,       (void *)&a.N,      (void *)&a.K};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(p.threads),
+                           args, (size_t)p.lds_bytes, stream);
+}
+
+template <int T, int KS>
+static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
+{
+    auto kern = gemv_mfma_kernel<T, KS>;
+    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X, (void *)&a.ldx,
+                    (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.M, (void *)&a.N,
+                    (void *)&a.K};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(256), args,
+                           0, stream);
+}
+
+#define W4A16_VALU_CASE(MT_, L_, V_, U_)                                                     \
+    if (p.MT == MT_ && p.L == L_ && p.V == V_ && p.U == U_)                                  \
+        return p.moe ? launch_valu_t<MT_, L_, V_, U_, true>(a, p, stream)                    \
+                     : launch_valu_t<MT_, L_, V_, U_, false>(a, p, stream);
+
+#define W4A16_MFMA_CASE(T_, KS_)                                                             \
+    if (p.T == T_ && p.KS == KS_)                                                            \
+        return launch_mfma_t<T_, KS_>(a, p, stream);
+
+hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream)
+{
+    if (p.kind == PLAN_VALU) {
+        W4A16_VALU_CONFIGS(W4A16_VALU_CASE)
+    } else if (p.kind == PLAN_MFMA) {
+        W4A16_MFMA_CONFIGS(W4A16_MFMA_CASE)
+    }
+    return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_unpack(const uint32_t *qw, int8_t *out, int64_t words, int cus,
+                         hipStream_t stream)
+{
+    int64_t blocks = (words + 255) / 256;
+    const int64_t cap = (int64_t)cus * 16;
+    if (blocks > cap)
+        blocks = cap;
+    if (blocks < 1)
+        blocks = 1;
+    void *args[] = {(void *)&qw, (void *)&out, (void *)&words};
+    return hipLaunchKernel(reinterpret_cast<const void *>(unpack_kernel), dim3((unsigned)blocks),
+                           dim3(256), args, 0, stream);
+}
+
+}  // namespace w4a16

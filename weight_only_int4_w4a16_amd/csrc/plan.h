@@ -1,0 +1,68 @@
+// Host-side launch planning for the W4A16 kernels. Pure C++ (no HIP types) so the choice of
+// kernel and launch shape can be inspected without a device.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2 };
+
+// Instantiated VALU kernels: X(tokens, lanes per row, chunks per lane per item, row steps per item).
+#define W4A16_VALU_CONFIGS(X)                                                                \
+    X(1, 64, 1, 2) X(1, 64, 1, 4) X(1, 64, 2, 2) X(1, 64, 2, 4) X(1, 64, 4, 2) X(1, 64, 7, 1)  \
+    X(1, 32, 1, 4) X(1, 32, 2, 2) X(1, 32, 2, 4) X(1, 32, 4, 2) X(1, 32, 7, 1)                \
+    X(1, 16, 1, 4) X(1, 16, 2, 2) X(1, 16, 4, 1) X(1, 16, 4, 2)                               \
+    X(1, 8, 1, 2) X(1, 8, 3, 1) X(1, 8, 3, 2) X(1, 8, 9, 1)                                   \
+    X(1, 4, 1, 2) X(1, 4, 2, 1) X(1, 4, 2, 2)                                                 \
+    X(2, 64, 1, 2) X(2, 64, 2, 2) X(2, 64, 1, 4) X(2, 32, 1, 4) X(2, 8, 3, 1) X(2, 4, 2, 1)    \
+    X(3, 64, 1, 2) X(3, 64, 2, 2) X(3, 32, 1, 2) X(3, 8, 3, 1) X(3, 4, 2, 1)                  \
+    X(4, 64, 1, 2) X(4, 64, 2, 2) X(4, 32, 1, 2) X(4, 8, 3, 1) X(4, 4, 2, 1)
+
+// Instantiated MFMA kernels: X(16-row tiles per wave, waves splitting K).
+#define W4A16_MFMA_CONFIGS(X) X(1, 1) X(2, 1) X(4, 1) X(1, 2) X(2, 2) X(1, 4) X(2, 4)
+
+struct Plan {
+    int kind;
+    int MT, L, V, U;   // VALU: tokens, lanes per row, chunks per lane per item, row steps per item
+    int T, KS;         // MFMA: 16-row tiles per wave, waves splitting K
+    bool moe;
+    int threads;       // work-group size
+    int64_t blocks;    // grid size
+    int64_t lds_bytes; // dynamic LDS per work-group
+};
+
+struct GemvArgs {
+    const void *qweight;   // uint32 words, viewed as 16-byte chunks by the kernels
+    const void *scales;    // fp16 bits
+    const void *X;         // bf16 bits, M rows of stride ldx
+    int64_t ldx;
+    void *Y;               // fp32, M rows of stride ldy (MoE: [topk][N], ldy = N)
+    int64_t ldy;
+    const void *ids;       // MoE expert ids (device), else null
+    int32_t topk;
+    int32_t E;
+    int64_t N;
+    int32_t K;
+    int32_t M;
+};
+
+// Largest K handled by the VALU kernel for MT tokens (activations staged in LDS).
+int64_t valu_max_k(int MT, int64_t lds_limit);
+
+// True if the (kind, MT, L, V, U) or (T, KS) tuple is an instantiated kernel.
+bool plan_instantiated(const Plan &p);
+
+// Fill `p` with the kernel and launch shape for a call (topk = 0 for dense calls).
+// Returns false when no kernel covers the shape.
+bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit, Plan *p);
+
+// Launch-shape override for tuning: keeps the caller's kernel choice, fills in grid and LDS.
+bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit,
+                 int blocks_per_cu, Plan *p);
+
+// Human-readable one-line description; returns the number of characters written.
+int describe_plan(const Plan &p, char *buf, size_t len);
+
+}  // namespace w4a16
