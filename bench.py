@@ -1,0 +1,268 @@
+"""W4A16 decode GEMV benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
+
+Workload: the MLP-shaped GEMV pair at M = 1 (one decode token): a 28672 x 4096 fused gate+up
+projection followed by a 4096 x 14336 down projection, INT4 weights packed 8 per uint32 along K,
+one fp16 scale per 128-wide group, bf16 activations, fp32 outputs; seeded synthetic operands.
+One step runs both GEMVs. The weights of a step rotate through enough copies (12 x 91 MB) that
+the 256 MB memory-side cache cannot hold them, so every step streams its weights from HBM.
+The K timed steps are captured in one HIP graph, replayed once between two HIP events on the
+launch stream, with device synchronisation on both sides.
+
+Prints one JSON line. `value` is algorithmic bytes (packed weights + fp16 scales + bf16
+activations) per second over the whole step, in GB/s. `roofline` is for the dominant kernel
+(the 28672 x 4096 GEMV): the same bytes over its own average duration, timed the same way on a
+graph of back-to-back launches. `cpu_baseline` is the CPU oracle (single thread, float64) timed
+on whole steps of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMV achieved HBM GB/s (% of MI355X peak) and µs/call at M=1"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_28672x4096.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "weight_only_int4_w4a16_amd", "csrc", f)
+                  for f in ("kernels.hip", "plan.cpp", "plan.h", "api.hip")]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload table (all five shapes) in the JSON line")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time for the oracle baseline (whole steps, at least one)")
+    return ap.parse_args()
+
+
+def to_dev(d, dev, torch, np):
+    qw = torch.from_numpy(np.ascontiguousarray(d.qweight).view(np.int32)).to(dev)
+    sc = torch.from_numpy(np.ascontiguousarray(d.scales).view(np.float16)).to(dev)
+    x = torch.from_numpy(np.ascontiguousarray(d.x).view(np.int16)).to(dev).view(torch.bfloat16)
+    return qw, sc, x
+
+
+def graph_avg_us(torch, fn, n):
+    """Average µs per fn() call over a HIP graph of n back-to-back calls (events on its stream)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n, g
+
+
+def traffic_for(digest, nbytes_alg):
+    """HBM bytes per launch of the dominant kernel from committed counter runs, if current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_digest") != digest:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the GEMV has no multi-GPU path here)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synthetic
+    import weight_only_int4_w4a16_amd as w
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    # ---- operands: seed 0 of the gate+up and down shapes, rotated copies on the device
+    da = synthetic.config("c3a", 0)
+    db = synthetic.config("c3b", 0)
+    qa, sa, xa = to_dev(da, dev, torch, np)
+    qb, sb, xb = to_dev(db, dev, torch, np)
+    bytes_a = synthetic.algorithmic_bytes(da.N, da.K)
+    bytes_b = synthetic.algorithmic_bytes(db.N, db.K)
+    step_weight_bytes = qa.numel() * 4 + sa.numel() * 2 + qb.numel() * 4 + sb.numel() * 2
+    R = max(2, -(-ROTATE_BYTES // step_weight_bytes))
+    copies = [(qa, sa, qb, sb)] + [(qa.clone(), sa.clone(), qb.clone(), sb.clone())
+                                   for _ in range(R - 1)]
+    ya = torch.empty(da.N, dtype=torch.float32, device=dev)
+    yb = torch.empty(db.N, dtype=torch.float32, device=dev)
+    xa1, xb1 = xa[0], xb[0]
+
+    def step(i):
+        c = copies[i % R]
+        w.gemv(c[0], c[1], xa1, out=ya)
+        w.gemv(c[2], c[3], xb1, out=yb)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps in one graph
+    step_us, _ = graph_avg_us(torch, step, args.steps)
+    ms_per_step = step_us / 1e3
+    value = (bytes_a + bytes_b) / (step_us * 1e-6) / 1e9
+
+    # ---- dominant kernel alone (28672 x 4096), same rotation, same timing method
+    gate_us, _ = graph_avg_us(torch, lambda i: w.gemv(copies[i % R][0], copies[i % R][1], xa1,
+                                                       out=ya), args.steps)
+    down_us, _ = graph_avg_us(torch, lambda i: w.gemv(copies[i % R][2], copies[i % R][3], xb1,
+                                                       out=yb), args.steps)
+    achieved = bytes_a / (gate_us * 1e-6) / 1e9
+    digest = kernel_source_digest()
+    traffic = traffic_for(digest, bytes_a)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded int4 weights uniform in [-8,7], fp16 scales uniform in "
+                "[0.001,0.01], bf16 activations ~N(0,1))",
+        "config": {
+            "workload": "MLP GEMV pair at M=1: 28672x4096 gate+up then 4096x14336 down, "
+                        "int4 weights (8 per uint32 along K), fp16 scale per 128-group, bf16 x",
+            "M": 1,
+            "shapes": [[da.N, da.K], [db.N, db.K]],
+            "bytes_per_step": bytes_a + bytes_b,
+            "rotated_weight_copies": R,
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "us_per_call": {"gate_up_28672x4096": round(gate_us, 3),
+                            "down_4096x14336": round(down_us, 3)},
+            "plans": {"gate_up": w.describe_plan(1, da.N, da.K, 0, props.multi_processor_count),
+                      "down": w.describe_plan(1, db.N, db.K, 0, props.multi_processor_count)},
+            "device": f"{props.name} {getattr(props, 'gcnArchName', '')} "
+                      f"{props.multi_processor_count} CUs",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "w4a16_gemv 28672x4096",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bytes_a,
+            "avg_launch_us": round(gate_us, 3),
+            "kernel_source_digest": digest,
+        },
+    }
+
+    if not args.no_configs:
+        out["per_workload"] = per_workload(torch, np, w, synthetic, dev)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(da, db, bytes_a + bytes_b, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+def per_workload(torch, np, w, synthetic, dev):
+    """µs per call and GB/s for every workload shape (graph-timed, rotated copies)."""
+    res = {}
+
+    def rot(nbytes):
+        return max(2, -(-ROTATE_BYTES // nbytes))
+
+    for name in ("c1", "c2", "c3a", "c3b", "c5a", "c5b"):
+        for M in ((1, 16) if name in ("c5a", "c5b") else (1,)):
+            d = synthetic.config(name, 0, M=M)
+            qw, sc, x = to_dev(d, dev, torch, np)
+            R = rot(qw.numel() * 4 + sc.numel() * 2)
+            cp = [(qw, sc)] + [(qw.clone(), sc.clone()) for _ in range(R - 1)]
+            y = torch.empty((M, d.N), dtype=torch.float32, device=dev)
+            if M == 1:
+                fn = lambda i: w.gemv(cp[i % R][0], cp[i % R][1], x[0], out=y[0])  # noqa: E731
+            else:
+                fn = lambda i: w.gemv_batched(cp[i % R][0], cp[i % R][1], x, out=y)  # noqa: E731
+            fn(0)
+            us, _ = graph_avg_us(torch, fn, max(2 * R, 64))
+            b = synthetic.algorithmic_bytes(d.N, d.K, M)
+            res[f"{name}_M{M}"] = {"N": d.N, "K": d.K, "us_per_call": round(us, 3),
+                                   "GB_s": round(b / us / 1e3, 1),
+                                   "pct_of_peak": round(100 * b / us / 1e3 / HBM_PEAK_GBS, 1)}
+            del cp, qw, sc
+            torch.cuda.empty_cache()
+    m = synthetic.config("c4", 0)
+    qw = torch.from_numpy(m.qweight.view(np.int32)).to(dev)
+    sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
+    cp = [(qw, sc), (qw.clone(), sc.clone())]
+    x = torch.from_numpy(m.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    rng = np.random.default_rng([4, 1])
+    idsets = [torch.from_numpy(rng.choice(m.E, m.topk, replace=False).astype(np.int32)).to(dev)
+              for _ in range(64)]
+    y = torch.empty((m.topk, m.N), dtype=torch.float32, device=dev)
+    fn = lambda i: w.moe_gemv(cp[i % 2][0], cp[i % 2][1], idsets[i % 64], x, out=y)  # noqa: E731
+    fn(0)
+    us, _ = graph_avg_us(torch, fn, 128)
+    b = m.topk * (m.N * m.K // 2 + m.N * (m.K // 128) * 2) + m.K * 2
+    res["c4_moe_top8_of_256"] = {"N": m.N, "K": m.K, "us_per_call": round(us, 3),
+                                 "GB_s": round(b / us / 1e3, 1),
+                                 "pct_of_peak": round(100 * b / us / 1e3 / HBM_PEAK_GBS, 1)}
+    return res
+
+
+def cpu_baseline(da, db, bytes_per_step, target_s):
+    """The CPU oracle (one thread, float64) on whole steps of the same workload."""
+    import oracle
+    orc = oracle.default()
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        orc.gemv(da.qweight, da.scales, da.x[0], da.K)
+        orc.gemv(db.qweight, db.scales, db.x[0], db.K)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or steps >= 8:
+            break
+    return {"value": round(bytes_per_step * steps / el / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole steps (28672x4096 + 4096x14336 GEMV, every row), "
+                      f"{el:.1f} s, single-threaded C oracle in float64",
+            "ms_per_step": round(el / steps * 1e3, 1)}
+
+
+if __name__ == "__main__":
+    main()

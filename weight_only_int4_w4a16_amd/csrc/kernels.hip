@@ -83,8 +83,35 @@ __device__ __forceinline__ uint4 pair_activations(uint4 v)
     return o;
 }
 
+#ifndef W4A16_SHIFT64
+#define W4A16_SHIFT64 1
+#endif
+
 __device__ __forceinline__ float chunk_dot(uint4 wv, const uint4 xq[4], float acc)
 {
+#if W4A16_SHIFT64
+    // One 64-bit shift moves the nibbles of two words at once; bits that cross from the high
+    // word land in bits 28-31 of the low word, which the 0x000F000F mask never keeps.
+    const uint64_t d2[2] = {((uint64_t)wv.y << 32) | wv.x, ((uint64_t)wv.w << 32) | wv.z};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint64_t s4, s8, s12;
+        const uint64_t s0 = d2[h];
+        asm("v_lshrrev_b64 %0, 4, %1" : "=v"(s4) : "v"(s0));
+        asm("v_lshrrev_b64 %0, 8, %1" : "=v"(s8) : "v"(s0));
+        asm("v_lshrrev_b64 %0, 12, %1" : "=v"(s12) : "v"(s0));
+        const uint4 &xa = xq[2 * h], &xb = xq[2 * h + 1];
+        acc = dot2(((uint32_t)s0 & kMask) ^ kMagic, xa.x, acc);
+        acc = dot2(((uint32_t)s4 & kMask) ^ kMagic, xa.y, acc);
+        acc = dot2(((uint32_t)s8 & kMask) ^ kMagic, xa.z, acc);
+        acc = dot2(((uint32_t)s12 & kMask) ^ kMagic, xa.w, acc);
+        acc = dot2(((uint32_t)(s0 >> 32) & kMask) ^ kMagic, xb.x, acc);
+        acc = dot2(((uint32_t)(s4 >> 32) & kMask) ^ kMagic, xb.y, acc);
+        acc = dot2(((uint32_t)(s8 >> 32) & kMask) ^ kMagic, xb.z, acc);
+        acc = dot2(((uint32_t)(s12 >> 32) & kMask) ^ kMagic, xb.w, acc);
+    }
+    return acc;
+#else
     const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -96,6 +123,72 @@ __device__ __forceinline__ float chunk_dot(uint4 wv, const uint4 xq[4], float ac
         acc = dot2(p[3], xq[j].w, acc);
     }
     return acc;
+#endif
+}
+
+
+// Cross-lane exchange across lane-index bit `bit` without LDS: DPP within a 16-lane row for bits
+// 0-3 (quad permutes, then the half-row and row mirrors, each a bijection between the two halves of
+// the group), v_permlane16_swap / v_permlane32_swap for bits 4 and 5.
+__device__ __forceinline__ float dpp_partner(float v, int bit)
+{
+    const int x = __builtin_bit_cast(int, v);
+    int r;
+    switch (bit) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true); break;   // quad_perm 1,0,3,2
+    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true); break;   // quad_perm 2,3,0,1
+    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true); break;  // row_half_mirror
+    default: r = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, true); break; // row_mirror
+    }
+    return __builtin_bit_cast(float, r);
+}
+
+// Swap the halves selected by lane bit 4 or 5 between a and b: afterwards a + b holds, in lanes with
+// the bit clear, a + partner's a, and in lanes with the bit set, b + partner's b.
+// The instruction rewrites both of its registers, so it is issued directly with both operands
+// read-write (the compiler builtin for it returns the first register twice on this toolchain).
+__device__ __forceinline__ float swap_fold(float a, float b, int bit)
+{
+    if (bit == 5)
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    else
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return a + b;
+}
+
+// Sum U per-lane values over groups of L lanes (L, U powers of two, U <= L). Rows are folded while
+// lanes are halved: at each of the first log2(U) steps a lane keeps half of its rows (the upper half
+// if its lane bit is set) and adds its partner's copy of them, so U rows cost U-1 exchanges plus
+// log2(L/U) plain ones instead of U*log2(L). On return v[0] holds the full sum of row `row`; the lanes
+// with (lane % (L/U)) == 0 hold distinct rows and together cover all U of them.
+template <int L, int U>
+__device__ __forceinline__ int fold_rows(float (&v)[U], int lane)
+{
+    static_assert(U <= L, "fold_rows needs U <= L");
+    constexpr int LB = __builtin_ctz(L);
+    constexpr int UB = __builtin_ctz(U);
+    int row = 0;
+#pragma unroll
+    for (int k = 0; k < UB; ++k) {
+        const int bit = LB - 1 - k;
+        const int m = U >> (k + 1);
+        const bool upper = (lane >> bit) & 1;
+#pragma unroll
+        for (int i = 0; i < m; ++i) {
+            if (bit >= 4) {
+                v[i] = swap_fold(v[i], v[i + m], bit);
+            } else {
+                const float lo = v[i] + dpp_partner(v[i], bit);
+                const float hi = v[i + m] + dpp_partner(v[i + m], bit);
+                v[i] = upper ? hi : lo;
+            }
+        }
+        row += upper ? m : 0;
+    }
+#pragma unroll
+    for (int bit = LB - 1 - UB; bit >= 0; --bit)
+        v[0] = bit >= 4 ? swap_fold(v[0], v[0], bit) : v[0] + dpp_partner(v[0], bit);
+    return row;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -128,28 +221,6 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     uint4 *xs = smem;                                          // [MT][4][CPR]
     float *bs = reinterpret_cast<float *>(smem + MT * KW);    // [MT][CPR]
 
-    // ---- stage activations: re-pair, transpose to [j][c], and form per-chunk offsets
-    for (int t = 0; t < MT; ++t) {
-        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
-        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
-            const uint4 v = xg[w];
-            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
-            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-            float sum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sum += bf16_bits_to_float(d[e] & 0xFFFFu);
-                sum += bf16_bits_to_float(d[e] >> 16);
-            }
-            // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
-            sum += __shfl_xor(sum, 1);
-            sum += __shfl_xor(sum, 2);
-            if ((w & 3) == 0)
-                bs[t * CPR + (w >> 2)] = -kOffset * sum;
-        }
-    }
-    __syncthreads();
-
     const int lane = threadIdx.x & 63;
     const int pr = lane & (L - 1);
     const int rr = lane / L;
@@ -159,8 +230,7 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     const int64_t rows_total = MOE ? (int64_t)topk * N : N;
     const int64_t n_super = (rows_total + ROWS - 1) / ROWS;
     const int nb = CPR / (L * V);
-    if (gw >= n_super)
-        return;
+    const bool active = gw < n_super;
 
     // Row pointers of a row block for loading.
     struct Rows {
@@ -237,19 +307,13 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
 
     auto finish = [&](int64_t st) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int t = 0; t < MT; ++t) {
+            float v[U];
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                float v = acc[u][t];
-#pragma unroll
-                for (int off = L / 2; off >= 1; off >>= 1)
-                    v += __shfl_xor(v, off);
-                acc[u][t] = v;
-            }
-        }
-        if (pr == 0) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < U; ++u)
+                v[u] = acc[u][t];
+            const int u = fold_rows<L, U>(v, pr);
+            if ((pr & (L / U - 1)) == 0) {
                 const int64_t vrow = st * ROWS + u * R + rr;
                 if (vrow < rows_total) {
                     bool zero = false;
@@ -257,9 +321,7 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                         const int32_t e = ids[vrow / N];
                         zero = e < 0 || e >= E;
                     }
-#pragma unroll
-                    for (int t = 0; t < MT; ++t)
-                        Y[t * ldy + vrow] = zero ? 0.0f : acc[u][t];
+                    Y[t * ldy + vrow] = zero ? 0.0f : v[0];
                 }
             }
         }
@@ -270,13 +332,40 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 acc[u][t] = 0.0f;
     };
 
-    // Flat walk over (row block, batch) items with one item of prefetch.
+    // Flat walk over (row block, batch) items with one item of prefetch. The first item's
+    // weights are requested before the activations are staged, so both fetches overlap.
     int64_t st = gw;
     int b = 0;
     Rows cur;
-    rows_of(st, cur);
     ValuBuf<L, V, U> bufA, bufB;
-    load(cur, 0, bufA);
+    if (active) {
+        rows_of(st, cur);
+        load(cur, 0, bufA);
+    }
+
+    // ---- stage activations: re-pair, transpose to [j][c], and form per-chunk offsets
+    for (int t = 0; t < MT; ++t) {
+        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
+        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
+            const uint4 v = xg[w];
+            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+            float sum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sum += bf16_bits_to_float(d[e] & 0xFFFFu);
+                sum += bf16_bits_to_float(d[e] >> 16);
+            }
+            // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            if ((w & 3) == 0)
+                bs[t * CPR + (w >> 2)] = -kOffset * sum;
+        }
+    }
+    __syncthreads();
+    if (!active)
+        return;
     auto step = [&](ValuBuf<L, V, U> &now, ValuBuf<L, V, U> &next) -> bool {
         int64_t nst = st;
         int nbb = b + 1;
@@ -302,6 +391,161 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             break;
         if (!step(bufB, bufA))
             break;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Split-K VALU GEMV. The W = CPR / (L*CL) waves of a work-group share one contiguous range of
+// rows and split K: wave w owns the K slice of chunks [w*L*CL, (w+1)*L*CL). Inside a wave, L lanes
+// walk a row (lane p owns chunks p, p+L, ... of the slice) and R = 64/L rows sit side by side, so
+// every load instruction covers R runs of L*16 contiguous bytes. Each lane keeps its CL chunks of
+// activations (re-paired) and their -136*sum(x) offsets in registers for the whole kernel: they
+// are fetched from global memory right after the first weight loads, with no LDS staging and no
+// barrier before the stream starts. Rows go U*R at a time with one item of prefetch; per-row
+// partial sums of the W slices meet in LDS once, after the last row, and are added in slice order.
+// ------------------------------------------------------------------------------------------
+template <int MT, int L, int CL, int U, bool MOE>
+__global__ void __launch_bounds__(512)
+gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
+                   const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
+                   const int32_t *__restrict__ ids, int32_t topk, int32_t E, int64_t N, int32_t K,
+                   int32_t rows_per_block)
+{
+    constexpr int R = 64 / L;
+    constexpr int ROWS = U * R;
+    extern __shared__ float red[];      // [MT][rows_per_block][W]
+    const int CPR = K >> 5;
+    const int GPR = K >> 7;
+    const int W = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int pr = lane & (L - 1);
+    const int rr = lane / L;
+    const int cbase = wave * (L * CL) + pr;            // chunk j of this lane: cbase + L*j
+    const int64_t rows_total = MOE ? (int64_t)topk * N : N;
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+    int64_t rcount = rows_total - r0;
+    if (rcount > rows_per_block)
+        rcount = rows_per_block;
+    const int n_items = rcount > 0 ? (int)((rcount + ROWS - 1) / ROWS) : 0;
+
+    struct Buf {
+        uint4 w[CL][U];
+        uint16_t s[CL][U];
+    };
+    auto load = [&](int item, Buf &buf) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int lr = item * ROWS + u * R + rr;       // row within the block
+            const int64_t vrow = r0 + lr;
+            bool ok = lr < rcount;
+            int64_t row = 0;
+            if (MOE) {
+                const int64_t slot = ok ? vrow / N : 0;
+                const int32_t e = ok ? ids[slot] : -1;
+                ok = ok && e >= 0 && e < E;
+                row = ok ? (int64_t)e * N + (vrow - slot * N) : 0;
+            } else {
+                row = ok ? vrow : 0;
+            }
+            const uint4 *wr = qw + row * CPR;
+            const uint16_t *sr = sc + row * GPR;
+#pragma unroll
+            for (int j = 0; j < CL; ++j) {
+                const int c = cbase + L * j;
+                if (ok) {
+                    buf.w[j][u] = load_weights(wr + c);
+                    buf.s[j][u] = sr[c >> 2];
+                } else {
+                    buf.w[j][u] = make_uint4(0, 0, 0, 0);
+                    buf.s[j][u] = 0;
+                }
+            }
+        }
+    };
+
+    Buf bufA, bufB;
+    if (n_items > 0)
+        load(0, bufA);
+
+    // Activations of this lane's chunks, re-paired, and their offsets.
+    uint4 xq[MT][CL][4];
+    float off[MT][CL];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
+#pragma unroll
+        for (int j = 0; j < CL; ++j) {
+            const int c = cbase + L * j;
+            float sum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 v = xg[4 * c + q];
+                xq[t][j][q] = pair_activations(v);
+                sum = dot2(v.x, 0x3F803F80u, sum);
+                sum = dot2(v.y, 0x3F803F80u, sum);
+                sum = dot2(v.z, 0x3F803F80u, sum);
+                sum = dot2(v.w, 0x3F803F80u, sum);
+            }
+            off[t][j] = -kOffset * sum;
+        }
+    }
+
+    auto compute = [&](int item, const Buf &buf) {
+        float acc[U][MT];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                acc[u][t] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CL; ++j)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float s = half_bits_to_float(buf.s[j][u]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[u][t] = fmaf(s, chunk_dot(buf.w[j][u], xq[t][j], off[t][j]), acc[u][t]);
+            }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = acc[u][t];
+            const int u = fold_rows<L, U>(v, pr);
+            if ((pr & (L / U - 1)) == 0) {
+                const int lr = item * ROWS + u * R + rr;
+                if (lr < rcount)
+                    red[((int64_t)t * rows_per_block + lr) * W + wave] = v[0];
+            }
+        }
+    };
+
+    for (int it = 0; it < n_items; it += 2) {
+        if (it + 1 < n_items)
+            load(it + 1, bufB);
+        compute(it, bufA);
+        if (it + 2 < n_items)
+            load(it + 2, bufA);
+        if (it + 1 < n_items)
+            compute(it + 1, bufB);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < MT * rcount; i += blockDim.x) {
+        const int t = i / (int)rcount;
+        const int lr = i - t * (int)rcount;
+        const float *pp = red + ((int64_t)t * rows_per_block + lr) * W;
+        float v = 0.0f;
+        for (int q = 0; q < W; ++q)
+            v += pp[q];
+        const int64_t vrow = r0 + lr;
+        if (MOE) {
+            const int32_t e = ids[vrow / N];
+            if (e < 0 || e >= E)
+                v = 0.0f;
+        }
+        Y[t * ldy + vrow] = v;
     }
 }
 
@@ -365,28 +609,38 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     for (int t = 0; t < T; ++t)
         acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int s = s0; s < s1; ++s) {
-        uint4 wv[T];
+    // Everything one group needs from memory: weights of T tiles, their scales (D-layout rows),
+    // and the token's 32 activations at this lane's K slot.
+    struct GroupBuf {
+        uint4 w[T];
+        uint16_t sc[T][4];
+        uint4 x[4];
+    };
+    auto gload = [&](int s, GroupBuf &g) {
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-            wv[t] = load_weights(wp[t] + 4 * s);
+        for (int t = 0; t < T; ++t) {
+            g.w[t] = load_weights(wp[t] + 4 * s);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                g.sc[t][r] = sp[t][r][s];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            g.x[j] = xon ? xp[16 * s + j] : make_uint4(0, 0, 0, 0);
+    };
+    auto gcompute = [&](const GroupBuf &g) {
         bf16x8_t xb[4];
         f32x4_t off = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint4 raw = xon ? xp[16 * s + j] : make_uint4(0, 0, 0, 0);
-            const uint4 pq = pair_activations(raw);
+            const uint4 pq = pair_activations(g.x[j]);
             xb[j] = as_bf16x8(pq.x, pq.y, pq.z, pq.w);
             off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c136, xb[j], off, 0, 0, 0);
         }
         off = -off;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            float sv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sv[r] = half_bits_to_float(sp[t][r][s]);
-            const uint32_t wd[4] = {wv[t].x, wv[t].y, wv[t].z, wv[t].w};
+            const uint32_t wd[4] = {g.w[t].x, g.w[t].y, g.w[t].z, g.w[t].w};
             f32x4_t d = off;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -397,8 +651,22 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                acc[t][r] = fmaf(sv[r], d[r], acc[t][r]);
+                acc[t][r] = fmaf(half_bits_to_float(g.sc[t][r]), d[r], acc[t][r]);
         }
+    };
+
+    // Two groups in flight: load s+1 while s is multiplied.
+    GroupBuf ga, gb;
+    if (s0 < s1)
+        gload(s0, ga);
+    for (int s = s0; s < s1; s += 2) {
+        if (s + 1 < s1)
+            gload(s + 1, gb);
+        gcompute(ga);
+        if (s + 2 < s1)
+            gload(s + 2, ga);
+        if (s + 1 < s1)
+            gcompute(gb);
     }
 
     if (KS > 1) {
@@ -464,6 +732,18 @@ static hipError_t launch_valu_t(const GemvArgs &a, const Plan &p, hipStream_t st
                            args, (size_t)p.lds_bytes, stream);
 }
 
+template <int MT, int L, int CL, int U, bool MOE>
+static hipError_t launch_splitk_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
+{
+    auto kern = gemv_splitk_kernel<MT, L, CL, U, MOE>;
+    int32_t rpb = (int32_t)p.rows_per_block;
+    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X,  (void *)&a.ldx,
+                    (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.ids, (void *)&a.topk,
+                    (void *)&a.E,       (void *)&a.N,      (void *)&a.K,   (void *)&rpb};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(p.threads),
+                           args, (size_t)p.lds_bytes, stream);
+}
+
 template <int T, int KS>
 static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
@@ -475,10 +755,16 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
                            0, stream);
 }
 
+// The grouped-expert form exists for one token only, so MoE variants are built only for MT == 1.
 #define W4A16_VALU_CASE(MT_, L_, V_, U_)                                                     \
     if (p.MT == MT_ && p.L == L_ && p.V == V_ && p.U == U_)                                  \
-        return p.moe ? launch_valu_t<MT_, L_, V_, U_, true>(a, p, stream)                    \
+        return p.moe ? launch_valu_t<MT_, L_, V_, U_, (MT_ == 1)>(a, p, stream)              \
                      : launch_valu_t<MT_, L_, V_, U_, false>(a, p, stream);
+
+#define W4A16_SPLITK_CASE(MT_, L_, CL_, U_)                                                  \
+    if (p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_)                                 \
+        return p.moe ? launch_splitk_t<MT_, L_, CL_, U_, (MT_ == 1)>(a, p, stream)           \
+                     : launch_splitk_t<MT_, L_, CL_, U_, false>(a, p, stream);
 
 #define W4A16_MFMA_CASE(T_, KS_)                                                             \
     if (p.T == T_ && p.KS == KS_)                                                            \
@@ -488,6 +774,8 @@ hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
     if (p.kind == PLAN_VALU) {
         W4A16_VALU_CONFIGS(W4A16_VALU_CASE)
+    } else if (p.kind == PLAN_SPLITK) {
+        W4A16_SPLITK_CONFIGS(W4A16_SPLITK_CASE)
     } else if (p.kind == PLAN_MFMA) {
         W4A16_MFMA_CONFIGS(W4A16_MFMA_CASE)
     }

@@ -21,11 +21,16 @@ bool plan_instantiated(const Plan &p)
 #define W4A16_VALU_MATCH(MT_, L_, V_, U_)                                                     \
     if (p.kind == PLAN_VALU && p.MT == MT_ && p.L == L_ && p.V == V_ && p.U == U_)             \
         return true;
+#define W4A16_SPLITK_MATCH(MT_, L_, CL_, U_)                                                  \
+    if (p.kind == PLAN_SPLITK && p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_)          \
+        return true;
 #define W4A16_MFMA_MATCH(T_, KS_)                                                            \
     if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_)                                      \
         return true;
     W4A16_VALU_CONFIGS(W4A16_VALU_MATCH)
     W4A16_MFMA_CONFIGS(W4A16_MFMA_MATCH)
+    W4A16_SPLITK_CONFIGS(W4A16_SPLITK_MATCH)
+#undef W4A16_SPLITK_MATCH
 #undef W4A16_VALU_MATCH
 #undef W4A16_MFMA_MATCH
     return false;
@@ -73,6 +78,36 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
         p->blocks = blocks < cap ? blocks : cap;
         return p->blocks >= 1;
     }
+    if (p->kind == PLAN_SPLITK) {
+        // V holds the chunks per lane; the number of waves follows from K.
+        const int64_t per_wave = (int64_t)p->L * p->V;
+        if (p->MT != M || cpr % per_wave != 0)
+            return false;
+        const int64_t waves = cpr / per_wave;
+        if (waves < 1 || waves > 8)
+            return false;
+        p->threads = (int)(64 * waves);
+        const int64_t rows = p->moe ? (int64_t)topk * N : N;
+        int per_cu = blocks_per_cu;
+        if (per_cu * waves > kMaxWavesPerCu)
+            per_cu = (int)(kMaxWavesPerCu / waves);
+        if (per_cu < 1)
+            per_cu = 1;
+        int64_t blocks = (int64_t)cus * per_cu;
+        const int64_t step = (int64_t)p->U * (64 / p->L);     // rows per item
+        int64_t rpb = (rows + blocks - 1) / blocks;
+        rpb = (rpb + step - 1) / step * step;
+        const int64_t max_rpb = lds_limit / (4 * waves * p->MT);
+        if (rpb > max_rpb)
+            rpb = max_rpb / step * step;
+        if (rpb < step)
+            return false;
+        blocks = (rows + rpb - 1) / rpb;
+        p->rows_per_block = rpb;
+        p->blocks = blocks;
+        p->lds_bytes = 4 * waves * p->MT * rpb;
+        return blocks >= 1 && blocks < (1LL << 31);
+    }
     if (p->kind == PLAN_MFMA) {
         if (gpr % p->KS != 0)
             return false;
@@ -85,6 +120,56 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
     return false;
 }
 
+// Dispatch rules, from launch-shape sweeps on MI355X with weights rotated through more than
+// 1 GiB of copies (so the 256 MB memory-side cache cannot serve them):
+//  * one token, K a multiple of 2048 up to 16384: split-K, 64 lanes per row, 8 rows per item,
+//    except K = 4096, where the staged kernel wins on tall matrices (>= 16384 rows) and a 16-lane
+//    split-K on short ones, and K = 2048 (one 64-lane item covers the row);
+//  * one token, other K: staged kernel with the widest power-of-two lanes per row dividing the
+//    row's 16-byte chunks; rows of 72 chunks (K = 2304) use 8 lanes, 3 chunks per item, 2 steps,
+//    and the grouped-expert call takes a whole row per item;
+//  * 2-4 tokens: split-K (64 lanes, 4 rows per item) when K is a multiple of 2048 up to 16384,
+//    else the staged kernel; 5-16 tokens: MFMA.
+namespace {
+
+int pow2_lanes(int64_t cpr)
+{
+    for (int L = 64; L >= 4; L >>= 1)
+        if (cpr % L == 0)
+            return L;
+    return 0;
+}
+
+bool try_plan(Plan c, int bpc, int M, int64_t N, int64_t K, int topk, int cus, int64_t lds,
+              Plan *p)
+{
+    if (!plan_instantiated(c) || !finish_plan(M, N, K, topk, cus, lds, bpc, &c))
+        return false;
+    *p = c;
+    return true;
+}
+
+Plan valu(int MT, int L, int V, int U, bool moe)
+{
+    Plan c{};
+    c.kind = PLAN_VALU;
+    c.MT = MT;
+    c.L = L;
+    c.V = V;
+    c.U = U;
+    c.moe = moe;
+    return c;
+}
+
+Plan splitk(int MT, int L, int CL, int U, bool moe)
+{
+    Plan c = valu(MT, L, CL, U, moe);
+    c.kind = PLAN_SPLITK;
+    return c;
+}
+
+}  // namespace
+
 bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit, Plan *p)
 {
     *p = Plan{};
@@ -94,41 +179,53 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     if (moe && M != 1)
         return false;
     const int64_t cpr = K / 32;
-    const int64_t gpr = K / 128;
+    const int64_t rows = moe ? (int64_t)topk * N : N;
+    const int L = pow2_lanes(cpr);
+    const int64_t c64 = cpr / 64;
+    const bool k2048 = cpr % 64 == 0;
 
-    const bool valu = M <= 4 && K <= valu_max_k(M, lds_limit);
-    if (valu) {
-        const int L = lanes_per_row(cpr);
-        const int64_t C = cpr / L;
-        // Preferred (V, U) per token count: about eight 16-byte loads in flight per lane.
-        static const int pref1[][2] = {{2, 4}, {4, 2}, {9, 1}, {7, 1}, {3, 2}, {1, 4},
-                                       {2, 2}, {3, 1}, {1, 2}, {2, 1}};
-        static const int prefn[][2] = {{2, 2}, {1, 4}, {3, 1}, {1, 2}, {2, 1}};
-        const int(*pref)[2] = M == 1 ? pref1 : prefn;
-        const int npref = M == 1 ? (int)(sizeof(pref1) / sizeof(pref1[0]))
-                                 : (int)(sizeof(prefn) / sizeof(prefn[0]));
-        for (int i = 0; i < npref; ++i) {
-            Plan c{};
-            c.kind = PLAN_VALU;
-            c.MT = M;
-            c.L = L;
-            c.V = pref[i][0];
-            c.U = pref[i][1];
-            c.moe = moe;
-            if (C % c.V != 0 || !plan_instantiated(c))
-                continue;
-            if (finish_plan(M, N, K, topk, cus, lds_limit, 8, &c)) {
-                *p = c;
+    if (M == 1) {
+        if (k2048 && c64 >= 2 && c64 <= 8) {
+            if (K == 4096 && rows >= 16384 &&
+                try_plan(valu(1, 32, 1, 2, moe), 8, M, N, K, topk, cus, lds_limit, p))
                 return true;
-            }
+            if (K == 4096 && try_plan(splitk(1, 16, 1, 2, moe), 3, M, N, K, topk, cus, lds_limit, p))
+                return true;
+            if (try_plan(splitk(1, 64, 1, 8, moe), 6, M, N, K, topk, cus, lds_limit, p))
+                return true;
         }
-        if (moe)
-            return false;
+        if (k2048 && c64 > 8) {
+            if (try_plan(splitk(1, 64, 2, 4, moe), 6, M, N, K, topk, cus, lds_limit, p) ||
+                try_plan(splitk(1, 64, 4, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
+                return true;
+        }
+        if (L == 8) {
+            if (moe && cpr == 72 && try_plan(valu(1, 8, 9, 1, true), 8, M, N, K, topk, cus, lds_limit, p))
+                return true;
+            const int V = (cpr / 8) % 3 == 0 ? 3 : 1;
+            if (try_plan(valu(1, 8, V, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
+                return true;
+        }
+        if (L == 64 && c64 == 1 && try_plan(valu(1, 64, 1, 1, moe), 2, M, N, K, topk, cus, lds_limit, p))
+            return true;
+        if (L >= 16 && try_plan(valu(1, L == 64 ? 32 : L, 1, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
+            return true;
+        if (L == 4 && try_plan(valu(1, 4, 1, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
+            return true;
+        return try_plan(valu(1, L, 1, 1, moe), 6, M, N, K, topk, cus, lds_limit, p);
     }
-    if (moe)
-        return false;
+    if (M <= 4) {
+        if (k2048 && c64 >= 2 && c64 <= 8 &&
+            try_plan(splitk(M, 64, 1, 4, false), 2, M, N, K, topk, cus, lds_limit, p))
+            return true;
+        if (M == 2 && L == 8 && try_plan(valu(2, 8, 1, 2, false), 4, M, N, K, topk, cus, lds_limit, p))
+            return true;
+        if (try_plan(valu(M, L, 1, 1, false), M == 2 ? 4 : 8, M, N, K, topk, cus, lds_limit, p))
+            return true;
+    }
     // MFMA: two 16-row tiles per wave; split K across waves when rows alone leave CUs idle.
     static const int mf[][2] = {{2, 1}, {2, 2}, {1, 2}, {1, 4}, {1, 1}};
+    const int64_t gpr = K / 128;
     for (int i = 0; i < (int)(sizeof(mf) / sizeof(mf[0])); ++i) {
         Plan c{};
         c.kind = PLAN_MFMA;
@@ -141,10 +238,8 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
         const bool last = i == (int)(sizeof(mf) / sizeof(mf[0])) - 1;
         if (blocks < 2LL * cus && !last)
             continue;
-        if (finish_plan(M, N, K, topk, cus, lds_limit, 1, &c)) {
-            *p = c;
+        if (try_plan(c, 1, M, N, K, topk, cus, lds_limit, p))
             return true;
-        }
     }
     return false;
 }
@@ -160,6 +255,12 @@ int describe_plan(const Plan &p, char *buf, size_t len)
                      "threads=%d blocks=%lld lds=%lld",
                      p.moe ? "_moe" : "", p.MT, p.L, p.V, p.U, p.threads, (long long)p.blocks,
                      (long long)p.lds_bytes);
+    else if (p.kind == PLAN_SPLITK)
+        n = snprintf(buf, len,
+                     "splitk%s tokens=%d lanes_per_row=%d chunks_per_lane=%d row_steps=%d "
+                     "threads=%d blocks=%lld rows_per_block=%lld lds=%lld",
+                     p.moe ? "_moe" : "", p.MT, p.L, p.V, p.U, p.threads, (long long)p.blocks,
+                     (long long)p.rows_per_block, (long long)p.lds_bytes);
     else if (p.kind == PLAN_MFMA)
         n = snprintf(buf, len, "mfma16x16x32 tiles_per_wave=%d k_split=%d threads=%d blocks=%lld",
                      p.T, p.KS, p.threads, (long long)p.blocks);

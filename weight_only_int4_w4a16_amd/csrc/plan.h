@@ -7,21 +7,34 @@
 
 namespace w4a16 {
 
-enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2 };
+enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3 };
 
-// Instantiated VALU kernels: X(tokens, lanes per row, chunks per lane per item, row steps per item).
+// Instantiated kernels. A build may supply its own lists (for launch-shape sweeps) by defining
+// the macros first.
+//
+// Staged-activation VALU kernels: X(tokens, lanes per row, chunks per lane per item, row steps).
+// Every (tokens, L, 1, 1) with L in {4..64} is present so that any K that is a multiple of 128
+// has a kernel; the others are the shapes the dispatch rules pick.
+#ifndef W4A16_VALU_CONFIGS
 #define W4A16_VALU_CONFIGS(X)                                                                \
-    X(1, 64, 1, 2) X(1, 64, 1, 4) X(1, 64, 2, 2) X(1, 64, 2, 4) X(1, 64, 4, 2) X(1, 64, 7, 1)  \
-    X(1, 32, 1, 4) X(1, 32, 2, 2) X(1, 32, 2, 4) X(1, 32, 4, 2) X(1, 32, 7, 1)                \
-    X(1, 16, 1, 4) X(1, 16, 2, 2) X(1, 16, 4, 1) X(1, 16, 4, 2)                               \
-    X(1, 8, 1, 2) X(1, 8, 3, 1) X(1, 8, 3, 2) X(1, 8, 9, 1)                                   \
-    X(1, 4, 1, 2) X(1, 4, 2, 1) X(1, 4, 2, 2)                                                 \
-    X(2, 64, 1, 2) X(2, 64, 2, 2) X(2, 64, 1, 4) X(2, 32, 1, 4) X(2, 8, 3, 1) X(2, 4, 2, 1)    \
-    X(3, 64, 1, 2) X(3, 64, 2, 2) X(3, 32, 1, 2) X(3, 8, 3, 1) X(3, 4, 2, 1)                  \
-    X(4, 64, 1, 2) X(4, 64, 2, 2) X(4, 32, 1, 2) X(4, 8, 3, 1) X(4, 4, 2, 1)
+    X(1, 64, 1, 1) X(1, 32, 1, 1) X(1, 16, 1, 1) X(1, 8, 1, 1) X(1, 4, 1, 1)                 \
+    X(1, 32, 1, 2) X(1, 16, 1, 2) X(1, 8, 1, 2) X(1, 8, 3, 2) X(1, 8, 9, 1) X(1, 4, 1, 2)     \
+    X(2, 64, 1, 1) X(2, 32, 1, 1) X(2, 16, 1, 1) X(2, 8, 1, 1) X(2, 4, 1, 1) X(2, 8, 1, 2)    \
+    X(3, 64, 1, 1) X(3, 32, 1, 1) X(3, 16, 1, 1) X(3, 8, 1, 1) X(3, 4, 1, 1)                 \
+    X(4, 64, 1, 1) X(4, 32, 1, 1) X(4, 16, 1, 1) X(4, 8, 1, 1) X(4, 4, 1, 1)
+#endif
 
-// Instantiated MFMA kernels: X(16-row tiles per wave, waves splitting K).
+// Split-K VALU kernels: X(tokens, lanes per row, chunks per lane, row steps per item).
+#ifndef W4A16_SPLITK_CONFIGS
+#define W4A16_SPLITK_CONFIGS(X)                                                              \
+    X(1, 64, 1, 8) X(1, 64, 2, 4) X(1, 64, 4, 2) X(1, 16, 1, 2)                               \
+    X(2, 64, 1, 4) X(3, 64, 1, 4) X(4, 64, 1, 4)
+#endif
+
+// MFMA kernels: X(16-row tiles per wave, waves splitting K).
+#ifndef W4A16_MFMA_CONFIGS
 #define W4A16_MFMA_CONFIGS(X) X(1, 1) X(2, 1) X(4, 1) X(1, 2) X(2, 2) X(1, 4) X(2, 4)
+#endif
 
 struct Plan {
     int kind;
@@ -31,6 +44,7 @@ struct Plan {
     int threads;       // work-group size
     int64_t blocks;    // grid size
     int64_t lds_bytes; // dynamic LDS per work-group
+    int64_t rows_per_block; // split-K: rows owned by one work-group
 };
 
 struct GemvArgs {
