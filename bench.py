@@ -54,6 +54,9 @@ def parse():
                     help="skip the per-workload table (all five shapes) in the JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline (whole steps, at least one)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy 5 times (reference "
+                         "kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -105,6 +108,15 @@ def main():
 
     import synthetic
     import weight_only_int4_w4a16_amd as w
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "launches": 5}))
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -62,6 +62,16 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16)
     return __builtin_bit_cast(float, b16 << 16);
 }
 
+// a if take else b, computed with masks so it never becomes a branch (branches around the loads
+// make the compiler fall back to waiting for every outstanding load at the join).
+template <typename T>
+__device__ __forceinline__ const T *pick(bool take, const T *a, const T *b)
+{
+    const uintptr_t m = (uintptr_t)0 - (uintptr_t)take;
+    return reinterpret_cast<const T *>((reinterpret_cast<uintptr_t>(a) & m) |
+                                       (reinterpret_cast<uintptr_t>(b) & ~m));
+}
+
 // Nibble pairs (0,4) (1,5) (2,6) (3,7) of w as bf16 pairs holding 136 + q.
 __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t p[4])
 {
@@ -192,13 +202,18 @@ __device__ __forceinline__ int fold_rows(float (&v)[U], int lane)
 }
 
 // ------------------------------------------------------------------------------------------
-// VALU GEMV: MT tokens (1..4), one wave streams U*R rows at a time, R = 64/L rows side by side,
-// L lanes per row. Lane p of a row owns the 16-byte chunks p, p+L, p+2L, ... of that row, so each
-// load instruction of the wave covers R runs of L*16 contiguous bytes (whole cache lines).
-// Activations live in LDS, re-paired, laid out [token][word-in-chunk j][chunk c] so the L lanes of a
-// row read consecutive 16-byte slots; per-chunk offsets -136*sum(x) follow them.
-// A wave walks a flat sequence of (row block, chunk batch) items and prefetches the next item's
-// weights and scales before computing the current one. No global scratch, no atomics.
+// Staged VALU GEMV: MT tokens (1..4). A wave streams U*R rows at a time, R = 64/L rows side by
+// side, L lanes per row; lane p of a row owns the 16-byte chunks p, p+L, p+2L, ... of that row, so
+// each load instruction covers R runs of L*16 contiguous bytes (whole cache lines). Activations are
+// staged once per work-group in LDS, re-paired and laid out [token][word-in-chunk j][chunk c] so
+// the L lanes of a row read consecutive 16-byte slots, followed by the per-chunk offsets
+// -136*sum(x) and, for the grouped-expert form, the expert ids (so id lookups never wait on
+// outstanding weight loads). A wave walks a flat sequence of (row block, chunk batch) items with
+// one item of prefetch. Every load is unconditional: rows past the end re-read the last row,
+// rows of an out-of-range expert read the activation row (valid memory of at least K*2 bytes, so
+// no other expert is touched), and waves without work re-read a valid item; results of all these
+// are discarded or written as zero. Straight-line loads let the compiler wait for each load on
+// its own, so early rows are multiplied while later ones are in flight.
 // ------------------------------------------------------------------------------------------
 template <int L, int V, int U>
 struct ValuBuf {
@@ -218,8 +233,9 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     const int KW = K >> 3;    // words per row
     const int CPR = K >> 5;   // 16-byte chunks per row
     const int GPR = K >> 7;   // scale groups per row
-    uint4 *xs = smem;                                          // [MT][4][CPR]
-    float *bs = reinterpret_cast<float *>(smem + MT * KW);    // [MT][CPR]
+    uint4 *xs = smem;                                            // [MT][4][CPR]
+    float *bs = reinterpret_cast<float *>(smem + MT * KW);      // [MT][CPR]
+    int32_t *ids_s = reinterpret_cast<int32_t *>(bs + MT * CPR);  // [topk] (grouped form)
 
     const int lane = threadIdx.x & 63;
     const int pr = lane & (L - 1);
@@ -231,49 +247,81 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     const int64_t n_super = (rows_total + ROWS - 1) / ROWS;
     const int nb = CPR / (L * V);
     const bool active = gw < n_super;
+    const int64_t gw_c = active ? gw : n_super - 1;
+    const int64_t n_items = ((n_super - 1 - gw_c) / GW + 1) * nb;
 
-    // Row pointers of a row block for loading.
     struct Rows {
         const uint4 *w[U];
         const uint16_t *s[U];
-        bool ok[U];
     };
     auto rows_of = [&](int64_t st, Rows &r) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t vrow = st * ROWS + u * R + rr;
-            int64_t row = 0;
-            bool ok = vrow < rows_total;
+            int64_t vrow = st * ROWS + u * R + rr;
+            vrow = vrow < rows_total ? vrow : rows_total - 1;
             if (MOE) {
-                const int64_t slot = ok ? vrow / N : 0;
-                const int64_t n = vrow - slot * N;
-                const int32_t e = ok ? ids[slot] : -1;
-                ok = ok && e >= 0 && e < E;
-                row = ok ? (int64_t)e * N + n : 0;
+                const int64_t slot = vrow / N;
+                const int32_t e = ids_s[slot];
+                const bool ok = e >= 0 && e < E;
+                const int64_t row = (int64_t)(ok ? e : 0) * N + (vrow - slot * N);
+                r.w[u] = pick(ok, qw + row * CPR, reinterpret_cast<const uint4 *>(X));
+                r.s[u] = pick(ok, sc + row * GPR, X);
             } else {
-                row = ok ? vrow : 0;
+                r.w[u] = qw + vrow * CPR;
+                r.s[u] = sc + vrow * GPR;
             }
-            r.w[u] = qw + row * CPR;
-            r.s[u] = sc + row * GPR;
-            r.ok[u] = ok;
         }
     };
-    auto load = [&](const Rows &r, int b, ValuBuf<L, V, U> &buf) {
+    // Loads and computes each walk the items in order with their own cursor (row block, batch).
+    int64_t ld_st = gw_c;
+    int ld_b = 0;
+    auto load = [&](ValuBuf<L, V, U> &buf) {
+        Rows r;
+        rows_of(ld_st, r);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            const int c = pr + L * (v + V * b);
+            const int c = pr + L * (v + V * ld_b);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (r.ok[u]) {
-                    buf.w[v][u] = load_weights(r.w[u] + c);
-                    buf.s[v][u] = r.s[u][c >> 2];
-                } else {
-                    buf.w[v][u] = make_uint4(0, 0, 0, 0);
-                    buf.s[v][u] = 0;
-                }
+                buf.w[v][u] = load_weights(r.w[u] + c);
+                buf.s[v][u] = r.s[u][c >> 2];
             }
         }
+        const bool wrap = ld_b + 1 == nb;
+        ld_b = wrap ? 0 : ld_b + 1;
+        ld_st += wrap ? GW : 0;
     };
+
+    ValuBuf<L, V, U> bufA, bufB;
+    if (!MOE)
+        load(bufA);     // overlaps the first weights with the activation fetch below
+
+    // ---- stage activations: re-pair, transpose to [j][c], and form per-chunk offsets
+    for (int t = 0; t < MT; ++t) {
+        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
+        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
+            const uint4 v = xg[w];
+            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
+            float sum = 0.0f;
+            sum = dot2(v.x, 0x3F803F80u, sum);
+            sum = dot2(v.y, 0x3F803F80u, sum);
+            sum = dot2(v.z, 0x3F803F80u, sum);
+            sum = dot2(v.w, 0x3F803F80u, sum);
+            // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
+            sum += dpp_partner(sum, 0);
+            sum += dpp_partner(sum, 1);
+            if ((w & 3) == 0)
+                bs[t * CPR + (w >> 2)] = -kOffset * sum;
+        }
+    }
+    if (MOE)
+        for (int i = threadIdx.x; i < topk; i += blockDim.x)
+            ids_s[i] = ids[i];
+    __syncthreads();
+    if (!active)
+        return;
+    if (MOE)
+        load(bufA);
 
     float acc[U][MT];
 #pragma unroll
@@ -282,10 +330,39 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         for (int t = 0; t < MT; ++t)
             acc[u][t] = 0.0f;
 
-    auto compute = [&](int b, const ValuBuf<L, V, U> &buf) {
+    auto finish = [&](int64_t st) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = acc[u][t];
+            const int u = fold_rows<L, U>(v, pr);
+            if ((pr & (L / U - 1)) == 0) {
+                const int64_t vrow = st * ROWS + u * R + rr;
+                if (vrow < rows_total) {
+                    bool zero = false;
+                    if (MOE) {
+                        const int32_t e = ids_s[vrow / N];
+                        zero = e < 0 || e >= E;
+                    }
+                    Y[t * ldy + vrow] = zero ? 0.0f : v[0];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                acc[u][t] = 0.0f;
+    };
+
+    int64_t cp_st = gw_c;
+    int cp_b = 0;
+    auto compute = [&](const ValuBuf<L, V, U> &buf) {
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            const int c = pr + L * (v + V * b);
+            const int c = pr + L * (v + V * cp_b);
             uint4 xq[MT][4];
             float off[MT];
 #pragma unroll
@@ -303,113 +380,48 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                     acc[u][t] = fmaf(s, chunk_dot(buf.w[v][u], xq[t], off[t]), acc[u][t]);
             }
         }
+        if (cp_b == nb - 1)
+            finish(cp_st);
+        const bool wrap = cp_b + 1 == nb;
+        cp_b = wrap ? 0 : cp_b + 1;
+        cp_st += wrap ? GW : 0;
     };
 
-    auto finish = [&](int64_t st) {
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            float v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                v[u] = acc[u][t];
-            const int u = fold_rows<L, U>(v, pr);
-            if ((pr & (L / U - 1)) == 0) {
-                const int64_t vrow = st * ROWS + u * R + rr;
-                if (vrow < rows_total) {
-                    bool zero = false;
-                    if (MOE) {
-                        const int32_t e = ids[vrow / N];
-                        zero = e < 0 || e >= E;
-                    }
-                    Y[t * ldy + vrow] = zero ? 0.0f : v[0];
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int t = 0; t < MT; ++t)
-                acc[u][t] = 0.0f;
-    };
-
-    // Flat walk over (row block, batch) items with one item of prefetch. The first item's
-    // weights are requested before the activations are staged, so both fetches overlap.
-    int64_t st = gw;
-    int b = 0;
-    Rows cur;
-    ValuBuf<L, V, U> bufA, bufB;
-    if (active) {
-        rows_of(st, cur);
-        load(cur, 0, bufA);
+    // Items alternate between the two buffers; each block of code issues the next item's loads
+    // and then consumes the previous ones.
+    int64_t i = 0;
+    for (; i + 2 < n_items; i += 2) {
+        load(bufB);
+        compute(bufA);
+        load(bufA);
+        compute(bufB);
     }
-
-    // ---- stage activations: re-pair, transpose to [j][c], and form per-chunk offsets
-    for (int t = 0; t < MT; ++t) {
-        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
-        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
-            const uint4 v = xg[w];
-            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
-            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-            float sum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sum += bf16_bits_to_float(d[e] & 0xFFFFu);
-                sum += bf16_bits_to_float(d[e] >> 16);
-            }
-            // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
-            sum += __shfl_xor(sum, 1);
-            sum += __shfl_xor(sum, 2);
-            if ((w & 3) == 0)
-                bs[t * CPR + (w >> 2)] = -kOffset * sum;
-        }
-    }
-    __syncthreads();
-    if (!active)
-        return;
-    auto step = [&](ValuBuf<L, V, U> &now, ValuBuf<L, V, U> &next) -> bool {
-        int64_t nst = st;
-        int nbb = b + 1;
-        if (nbb == nb) {
-            nbb = 0;
-            nst += GW;
-        }
-        const bool more = nst < n_super;
-        if (more) {
-            if (nst != st)
-                rows_of(nst, cur);
-            load(cur, nbb, next);
-        }
-        compute(b, now);
-        if (b == nb - 1)
-            finish(st);
-        st = nst;
-        b = nbb;
-        return more;
-    };
-    for (;;) {
-        if (!step(bufA, bufB))
-            break;
-        if (!step(bufB, bufA))
-            break;
+    if (i + 1 < n_items) {
+        load(bufB);
+        compute(bufA);
+        compute(bufB);
+    } else {
+        compute(bufA);
     }
 }
 
 // ------------------------------------------------------------------------------------------
-// Split-K VALU GEMV. The W = CPR / (L*CL) waves of a work-group share one contiguous range of
-// rows and split K: wave w owns the K slice of chunks [w*L*CL, (w+1)*L*CL). Inside a wave, L lanes
-// walk a row (lane p owns chunks p, p+L, ... of the slice) and R = 64/L rows sit side by side, so
-// every load instruction covers R runs of L*16 contiguous bytes. Each lane keeps its CL chunks of
-// activations (re-paired) and their -136*sum(x) offsets in registers for the whole kernel: they
-// are fetched from global memory right after the first weight loads, with no LDS staging and no
-// barrier before the stream starts. Rows go U*R at a time with one item of prefetch; per-row
-// partial sums of the W slices meet in LDS once, after the last row, and are added in slice order.
+// Split-K VALU GEMV (dense calls). The W = CPR / (L*CL) waves of a work-group share one contiguous
+// range of rows and split K: wave w owns the K slice of chunks [w*L*CL, (w+1)*L*CL). Inside a wave,
+// L lanes walk a row (lane p owns chunks p, p+L, ... of the slice) and R = 64/L rows sit side by
+// side, so every load instruction covers R runs of L*16 contiguous bytes. Each lane keeps its CL
+// chunks of activations (re-paired) and their -136*sum(x) offsets in registers for the whole
+// kernel; they are requested before the first weights, so they are ready while the weights are
+// still in flight, with no LDS staging and no barrier before the stream starts. Rows go U*R at a
+// time with one item of prefetch and unconditional loads (rows past the block's end re-read its
+// last row); per-row partial sums of the W slices meet in LDS once, after the last row, and are
+// added in slice order.
 // ------------------------------------------------------------------------------------------
-template <int MT, int L, int CL, int U, bool MOE>
+template <int MT, int L, int CL, int U>
 __global__ void __launch_bounds__(512)
 gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                    const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
-                   const int32_t *__restrict__ ids, int32_t topk, int32_t E, int64_t N, int32_t K,
-                   int32_t rows_per_block)
+                   int64_t N, int32_t K, int32_t rows_per_block)
 {
     constexpr int R = 64 / L;
     constexpr int ROWS = U * R;
@@ -422,76 +434,69 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
     const int pr = lane & (L - 1);
     const int rr = lane / L;
     const int cbase = wave * (L * CL) + pr;            // chunk j of this lane: cbase + L*j
-    const int64_t rows_total = MOE ? (int64_t)topk * N : N;
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
-    int64_t rcount = rows_total - r0;
-    if (rcount > rows_per_block)
-        rcount = rows_per_block;
-    const int n_items = rcount > 0 ? (int)((rcount + ROWS - 1) / ROWS) : 0;
+    const int64_t left = N - r0;
+    const int rcount = (int)(left < rows_per_block ? left : rows_per_block);   // >= 1
+    const int n_items = (rcount + ROWS - 1) / ROWS;
 
     struct Buf {
         uint4 w[CL][U];
         uint16_t s[CL][U];
     };
-    auto load = [&](int item, Buf &buf) {
+    int ld_item = 0;
+    auto load = [&](Buf &buf) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int lr = item * ROWS + u * R + rr;       // row within the block
-            const int64_t vrow = r0 + lr;
-            bool ok = lr < rcount;
-            int64_t row = 0;
-            if (MOE) {
-                const int64_t slot = ok ? vrow / N : 0;
-                const int32_t e = ok ? ids[slot] : -1;
-                ok = ok && e >= 0 && e < E;
-                row = ok ? (int64_t)e * N + (vrow - slot * N) : 0;
-            } else {
-                row = ok ? vrow : 0;
-            }
+            int lr = ld_item * ROWS + u * R + rr;           // row within the block
+            lr = lr < rcount ? lr : rcount - 1;
+            const int64_t row = r0 + lr;
             const uint4 *wr = qw + row * CPR;
             const uint16_t *sr = sc + row * GPR;
 #pragma unroll
             for (int j = 0; j < CL; ++j) {
                 const int c = cbase + L * j;
-                if (ok) {
-                    buf.w[j][u] = load_weights(wr + c);
-                    buf.s[j][u] = sr[c >> 2];
-                } else {
-                    buf.w[j][u] = make_uint4(0, 0, 0, 0);
-                    buf.s[j][u] = 0;
-                }
+                buf.w[j][u] = load_weights(wr + c);
+                buf.s[j][u] = sr[c >> 2];
             }
         }
+        ++ld_item;
     };
 
-    Buf bufA, bufB;
-    if (n_items > 0)
-        load(0, bufA);
-
-    // Activations of this lane's chunks, re-paired, and their offsets.
+    // Activations first: load completions are counted in issue order.
     uint4 xq[MT][CL][4];
-    float off[MT][CL];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
 #pragma unroll
+        for (int j = 0; j < CL; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xq[t][j][q] = xg[4 * (cbase + L * j) + q];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the activation loads ahead of the weight loads
+    Buf bufA, bufB;
+    load(bufA);
+    float off[MT][CL];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+#pragma unroll
         for (int j = 0; j < CL; ++j) {
-            const int c = cbase + L * j;
             float sum = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint4 v = xg[4 * c + q];
-                xq[t][j][q] = pair_activations(v);
+                const uint4 v = xq[t][j][q];
                 sum = dot2(v.x, 0x3F803F80u, sum);
                 sum = dot2(v.y, 0x3F803F80u, sum);
                 sum = dot2(v.z, 0x3F803F80u, sum);
                 sum = dot2(v.w, 0x3F803F80u, sum);
+                xq[t][j][q] = pair_activations(v);
             }
             off[t][j] = -kOffset * sum;
         }
     }
 
-    auto compute = [&](int item, const Buf &buf) {
+    int cp_item = 0;
+    auto compute = [&](const Buf &buf) {
         float acc[U][MT];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -515,37 +520,37 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
                 v[u] = acc[u][t];
             const int u = fold_rows<L, U>(v, pr);
             if ((pr & (L / U - 1)) == 0) {
-                const int lr = item * ROWS + u * R + rr;
+                const int lr = cp_item * ROWS + u * R + rr;
                 if (lr < rcount)
                     red[((int64_t)t * rows_per_block + lr) * W + wave] = v[0];
             }
         }
+        ++cp_item;
     };
 
-    for (int it = 0; it < n_items; it += 2) {
-        if (it + 1 < n_items)
-            load(it + 1, bufB);
-        compute(it, bufA);
-        if (it + 2 < n_items)
-            load(it + 2, bufA);
-        if (it + 1 < n_items)
-            compute(it + 1, bufB);
+    int i = 0;
+    for (; i + 2 < n_items; i += 2) {
+        load(bufB);
+        compute(bufA);
+        load(bufA);
+        compute(bufB);
+    }
+    if (i + 1 < n_items) {
+        load(bufB);
+        compute(bufA);
+        compute(bufB);
+    } else {
+        compute(bufA);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < MT * rcount; i += blockDim.x) {
-        const int t = i / (int)rcount;
-        const int lr = i - t * (int)rcount;
+    for (int k = threadIdx.x; k < MT * rcount; k += blockDim.x) {
+        const int t = k / rcount;
+        const int lr = k - t * rcount;
         const float *pp = red + ((int64_t)t * rows_per_block + lr) * W;
         float v = 0.0f;
         for (int q = 0; q < W; ++q)
             v += pp[q];
-        const int64_t vrow = r0 + lr;
-        if (MOE) {
-            const int32_t e = ids[vrow / N];
-            if (e < 0 || e >= E)
-                v = 0.0f;
-        }
-        Y[t * ldy + vrow] = v;
+        Y[t * ldy + r0 + lr] = v;
     }
 }
 
@@ -624,9 +629,10 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             for (int r = 0; r < 4; ++r)
                 g.sc[t][r] = sp[t][r][s];
         }
+        // Lanes past M read token 0: their output columns are never stored.
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            g.x[j] = xon ? xp[16 * s + j] : make_uint4(0, 0, 0, 0);
+            g.x[j] = xp[16 * s + j];
     };
     auto gcompute = [&](const GroupBuf &g) {
         bf16x8_t xb[4];
@@ -732,14 +738,14 @@ static hipError_t launch_valu_t(const GemvArgs &a, const Plan &p, hipStream_t st
                            args, (size_t)p.lds_bytes, stream);
 }
 
-template <int MT, int L, int CL, int U, bool MOE>
+template <int MT, int L, int CL, int U>
 static hipError_t launch_splitk_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
-    auto kern = gemv_splitk_kernel<MT, L, CL, U, MOE>;
+    auto kern = gemv_splitk_kernel<MT, L, CL, U>;
     int32_t rpb = (int32_t)p.rows_per_block;
-    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X,  (void *)&a.ldx,
-                    (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.ids, (void *)&a.topk,
-                    (void *)&a.E,       (void *)&a.N,      (void *)&a.K,   (void *)&rpb};
+    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X, (void *)&a.ldx,
+                    (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.N, (void *)&a.K,
+                    (void *)&rpb};
     return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(p.threads),
                            args, (size_t)p.lds_bytes, stream);
 }
@@ -762,9 +768,8 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
                      : launch_valu_t<MT_, L_, V_, U_, false>(a, p, stream);
 
 #define W4A16_SPLITK_CASE(MT_, L_, CL_, U_)                                                  \
-    if (p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_)                                 \
-        return p.moe ? launch_splitk_t<MT_, L_, CL_, U_, (MT_ == 1)>(a, p, stream)           \
-                     : launch_splitk_t<MT_, L_, CL_, U_, false>(a, p, stream);
+    if (p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_ && !p.moe)                       \
+        return launch_splitk_t<MT_, L_, CL_, U_>(a, p, stream);
 
 #define W4A16_MFMA_CASE(T_, KS_)                                                             \
     if (p.T == T_ && p.KS == KS_)                                                            \

@@ -58,7 +58,7 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
             p->threads = 256;
         if (p->threads % 64 || p->threads < 64 || p->threads > 256)
             return false;
-        p->lds_bytes = (int64_t)p->MT * (K * 2 + cpr * 4);
+        p->lds_bytes = (int64_t)p->MT * (K * 2 + cpr * 4) + (p->moe ? 4LL * topk : 0);
         if (p->lds_bytes > lds_limit)
             return false;
         const int64_t rows = p->moe ? (int64_t)topk * N : N;
@@ -79,9 +79,9 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
         return p->blocks >= 1;
     }
     if (p->kind == PLAN_SPLITK) {
-        // V holds the chunks per lane; the number of waves follows from K.
+        // V holds the chunks per lane; the number of waves follows from K. Dense calls only.
         const int64_t per_wave = (int64_t)p->L * p->V;
-        if (p->MT != M || cpr % per_wave != 0)
+        if (p->MT != M || p->moe || cpr % per_wave != 0)
             return false;
         const int64_t waves = cpr / per_wave;
         if (waves < 1 || waves > 8)
@@ -122,14 +122,14 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
 
 // Dispatch rules, from launch-shape sweeps on MI355X with weights rotated through more than
 // 1 GiB of copies (so the 256 MB memory-side cache cannot serve them):
-//  * one token, K a multiple of 2048 up to 16384: split-K, 64 lanes per row, 8 rows per item,
-//    except K = 4096, where the staged kernel wins on tall matrices (>= 16384 rows) and a 16-lane
-//    split-K on short ones, and K = 2048 (one 64-lane item covers the row);
-//  * one token, other K: staged kernel with the widest power-of-two lanes per row dividing the
-//    row's 16-byte chunks; rows of 72 chunks (K = 2304) use 8 lanes, 3 chunks per item, 2 steps,
-//    and the grouped-expert call takes a whole row per item;
-//  * 2-4 tokens: split-K (64 lanes, 4 rows per item) when K is a multiple of 2048 up to 16384,
-//    else the staged kernel; 5-16 tokens: MFMA.
+//  * dense, 1-4 tokens, K a multiple of 2048 up to 16384: split-K with 64 lanes per row and 4 rows
+//    per item, about 8 waves per CU (one work-group of K/2048 waves, 8/W groups per CU); very short
+//    one-token matrices (<= 16 rows per CU) use 32 lanes and 2-row items instead; K above 16384
+//    uses 2 or 4 chunks per lane so that a work-group stays within 8 waves;
+//  * other K, and every grouped-expert call: the staged kernel with the widest power-of-two lanes
+//    per row dividing the row's 16-byte chunks; rows of 72 chunks (K = 2304) use 8 lanes with
+//    3 chunks per item;
+//  * 5-16 tokens: MFMA.
 namespace {
 
 int pow2_lanes(int64_t cpr)
@@ -184,28 +184,25 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     const int64_t c64 = cpr / 64;
     const bool k2048 = cpr % 64 == 0;
 
+    const int split_bpc = (int)(c64 >= 8 ? 1 : 8 / (c64 > 0 ? c64 : 1));
+    if (!moe && k2048 && c64 >= 2 && c64 <= 8 && M <= 4) {
+        if (M == 1 && rows <= 16LL * cus &&
+            try_plan(splitk(1, 32, 1, 2, false), 2, M, N, K, topk, cus, lds_limit, p))
+            return true;
+        if (try_plan(splitk(M, 64, 1, 4, false), split_bpc, M, N, K, topk, cus, lds_limit, p))
+            return true;
+    }
+    if (!moe && k2048 && c64 > 8 && M == 1) {
+        if (try_plan(splitk(1, 64, 2, 4, false), 1, M, N, K, topk, cus, lds_limit, p) ||
+            try_plan(splitk(1, 64, 4, 2, false), 1, M, N, K, topk, cus, lds_limit, p))
+            return true;
+    }
     if (M == 1) {
-        if (k2048 && c64 >= 2 && c64 <= 8) {
-            if (K == 4096 && rows >= 16384 &&
-                try_plan(valu(1, 32, 1, 2, moe), 8, M, N, K, topk, cus, lds_limit, p))
-                return true;
-            if (K == 4096 && try_plan(splitk(1, 16, 1, 2, moe), 3, M, N, K, topk, cus, lds_limit, p))
-                return true;
-            if (try_plan(splitk(1, 64, 1, 8, moe), 6, M, N, K, topk, cus, lds_limit, p))
-                return true;
-        }
-        if (k2048 && c64 > 8) {
-            if (try_plan(splitk(1, 64, 2, 4, moe), 6, M, N, K, topk, cus, lds_limit, p) ||
-                try_plan(splitk(1, 64, 4, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
-                return true;
-        }
-        if (L == 8) {
-            if (moe && cpr == 72 && try_plan(valu(1, 8, 9, 1, true), 8, M, N, K, topk, cus, lds_limit, p))
-                return true;
-            const int V = (cpr / 8) % 3 == 0 ? 3 : 1;
-            if (try_plan(valu(1, 8, V, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
-                return true;
-        }
+        if (L == 8 && (cpr / 8) % 3 == 0 &&
+            try_plan(valu(1, 8, 3, 1, moe), moe ? 8 : 2, M, N, K, topk, cus, lds_limit, p))
+            return true;
+        if (L == 8 && try_plan(valu(1, 8, 1, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
+            return true;
         if (L == 64 && c64 == 1 && try_plan(valu(1, 64, 1, 1, moe), 2, M, N, K, topk, cus, lds_limit, p))
             return true;
         if (L >= 16 && try_plan(valu(1, L == 64 ? 32 : L, 1, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
@@ -215,9 +212,6 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
         return try_plan(valu(1, L, 1, 1, moe), 6, M, N, K, topk, cus, lds_limit, p);
     }
     if (M <= 4) {
-        if (k2048 && c64 >= 2 && c64 <= 8 &&
-            try_plan(splitk(M, 64, 1, 4, false), 2, M, N, K, topk, cus, lds_limit, p))
-            return true;
         if (M == 2 && L == 8 && try_plan(valu(2, 8, 1, 2, false), 4, M, N, K, topk, cus, lds_limit, p))
             return true;
         if (try_plan(valu(M, L, 1, 1, false), M == 2 ? 4 : 8, M, N, K, topk, cus, lds_limit, p))

@@ -18,16 +18,16 @@ enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3 };
 #ifndef W4A16_VALU_CONFIGS
 #define W4A16_VALU_CONFIGS(X)                                                                \
     X(1, 64, 1, 1) X(1, 32, 1, 1) X(1, 16, 1, 1) X(1, 8, 1, 1) X(1, 4, 1, 1)                 \
-    X(1, 32, 1, 2) X(1, 16, 1, 2) X(1, 8, 1, 2) X(1, 8, 3, 2) X(1, 8, 9, 1) X(1, 4, 1, 2)     \
+    X(1, 32, 1, 2) X(1, 16, 1, 2) X(1, 8, 1, 2) X(1, 8, 3, 1) X(1, 4, 1, 2)                  \
     X(2, 64, 1, 1) X(2, 32, 1, 1) X(2, 16, 1, 1) X(2, 8, 1, 1) X(2, 4, 1, 1) X(2, 8, 1, 2)    \
     X(3, 64, 1, 1) X(3, 32, 1, 1) X(3, 16, 1, 1) X(3, 8, 1, 1) X(3, 4, 1, 1)                 \
     X(4, 64, 1, 1) X(4, 32, 1, 1) X(4, 16, 1, 1) X(4, 8, 1, 1) X(4, 4, 1, 1)
 #endif
 
-// Split-K VALU kernels: X(tokens, lanes per row, chunks per lane, row steps per item).
+// Split-K VALU kernels (dense calls): X(tokens, lanes per row, chunks per lane, row steps).
 #ifndef W4A16_SPLITK_CONFIGS
 #define W4A16_SPLITK_CONFIGS(X)                                                              \
-    X(1, 64, 1, 8) X(1, 64, 2, 4) X(1, 64, 4, 2) X(1, 16, 1, 2)                               \
+    X(1, 64, 1, 4) X(1, 32, 1, 2) X(1, 64, 2, 4) X(1, 64, 4, 2)                               \
     X(2, 64, 1, 4) X(3, 64, 1, 4) X(4, 64, 1, 4)
 #endif
 
