@@ -57,6 +57,11 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 5 times (reference "
                          "kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--profile-workload", default=None,
+                    choices=["c1", "c2", "c3a", "c3b", "c4", "c5a", "c5b"],
+                    help="only launch this workload's GEMV --steps times on rotated copies "
+                         "(for profiler runs; prints a short JSON line, no timing)")
+    ap.add_argument("--batch", type=int, default=1, help="tokens M for --profile-workload")
     return ap.parse_args()
 
 
@@ -65,6 +70,14 @@ def to_dev(d, dev, torch, np):
     sc = torch.from_numpy(np.ascontiguousarray(d.scales).view(np.float16)).to(dev)
     x = torch.from_numpy(np.ascontiguousarray(d.x).view(np.int16)).to(dev).view(torch.bfloat16)
     return qw, sc, x
+
+
+def rotated(torch, t, R):
+    """R copies of t in one contiguous allocation (views), so every copy is separate memory."""
+    big = torch.empty((R,) + tuple(t.shape), dtype=t.dtype, device=t.device)
+    for r in range(R):
+        big[r].copy_(t)
+    return [big[r] for r in range(R)]
 
 
 def graph_avg_us(torch, fn, n):
@@ -122,6 +135,11 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
 
+    if args.profile_workload:
+        profile_workload(torch, np, w, synthetic, dev, args.profile_workload, args.batch,
+                         args.steps)
+        return
+
     # ---- operands: seed 0 of the gate+up and down shapes, rotated copies on the device
     da = synthetic.config("c3a", 0)
     db = synthetic.config("c3b", 0)
@@ -131,8 +149,8 @@ def main():
     bytes_b = synthetic.algorithmic_bytes(db.N, db.K)
     step_weight_bytes = qa.numel() * 4 + sa.numel() * 2 + qb.numel() * 4 + sb.numel() * 2
     R = max(2, -(-ROTATE_BYTES // step_weight_bytes))
-    copies = [(qa, sa, qb, sb)] + [(qa.clone(), sa.clone(), qb.clone(), sb.clone())
-                                   for _ in range(R - 1)]
+    copies = list(zip(rotated(torch, qa, R), rotated(torch, sa, R), rotated(torch, qb, R),
+                      rotated(torch, sb, R)))
     ya = torch.empty(da.N, dtype=torch.float32, device=dev)
     yb = torch.empty(db.N, dtype=torch.float32, device=dev)
     xa1, xb1 = xa[0], xb[0]
@@ -224,7 +242,7 @@ def per_workload(torch, np, w, synthetic, dev):
             d = synthetic.config(name, 0, M=M)
             qw, sc, x = to_dev(d, dev, torch, np)
             R = rot(qw.numel() * 4 + sc.numel() * 2)
-            cp = [(qw, sc)] + [(qw.clone(), sc.clone()) for _ in range(R - 1)]
+            cp = list(zip(rotated(torch, qw, R), rotated(torch, sc, R)))
             y = torch.empty((M, d.N), dtype=torch.float32, device=dev)
             if M == 1:
                 fn = lambda i: w.gemv(cp[i % R][0], cp[i % R][1], x[0], out=y[0])  # noqa: E731
@@ -241,7 +259,8 @@ def per_workload(torch, np, w, synthetic, dev):
     m = synthetic.config("c4", 0)
     qw = torch.from_numpy(m.qweight.view(np.int32)).to(dev)
     sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
-    cp = [(qw, sc), (qw.clone(), sc.clone())]
+    cp = list(zip(rotated(torch, qw, 2), rotated(torch, sc, 2)))
+    del qw, sc
     x = torch.from_numpy(m.x.view(np.int16)).to(dev).view(torch.bfloat16)
     rng = np.random.default_rng([4, 1])
     idsets = [torch.from_numpy(rng.choice(m.E, m.topk, replace=False).astype(np.int32)).to(dev)
@@ -255,6 +274,37 @@ def per_workload(torch, np, w, synthetic, dev):
                                  "GB_s": round(b / us / 1e3, 1),
                                  "pct_of_peak": round(100 * b / us / 1e3 / HBM_PEAK_GBS, 1)}
     return res
+
+
+def profile_workload(torch, np, w, synthetic, dev, name, M, steps):
+    """Launch one workload's GEMV `steps` times on rotated copies (no timing): a fixed command
+    for rocprofv3 counter and trace runs."""
+    if name == "c4":
+        m = synthetic.config("c4", 0)
+        qw = torch.from_numpy(m.qweight.view(np.int32)).to(dev)
+        sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
+        cp = list(zip(rotated(torch, qw, 2), rotated(torch, sc, 2)))
+        del qw, sc
+        x = torch.from_numpy(m.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        ids = torch.from_numpy(m.ids).to(dev)
+        y = torch.empty((m.topk, m.N), dtype=torch.float32, device=dev)
+        for i in range(steps):
+            w.moe_gemv(cp[i % 2][0], cp[i % 2][1], ids, x, out=y)
+        plan = w.describe_plan(1, m.N, m.K, m.topk)
+    else:
+        d = synthetic.config(name, 0, M=M)
+        qw, sc, x = to_dev(d, dev, torch, np)
+        R = max(2, -(-ROTATE_BYTES // (qw.numel() * 4 + sc.numel() * 2)))
+        cp = list(zip(rotated(torch, qw, R), rotated(torch, sc, R)))
+        y = torch.empty((M, d.N), dtype=torch.float32, device=dev)
+        for i in range(steps):
+            if M == 1:
+                w.gemv(cp[i % R][0], cp[i % R][1], x[0], out=y[0])
+            else:
+                w.gemv_batched(cp[i % R][0], cp[i % R][1], x, out=y)
+        plan = w.describe_plan(M, d.N, d.K)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_workload": name, "M": M, "launches": steps, "plan": plan}))
 
 
 def cpu_baseline(da, db, bytes_per_step, target_s):

@@ -100,7 +100,8 @@ w4a16_status_t w4a16_moe_gemv(const uint32_t *qweight, const uint16_t *scales,
 
 /*
  * Test support: q_out int8[N][K] receives the signed value of every packed nibble, so the
- * unpacking can be checked bit for bit. 1 <= N, 8 <= K, K % 8 == 0; qweight 16-byte aligned.
+ * unpacking can be checked bit for bit. 1 <= N, 8 <= K, K % 8 == 0; qweight 4-byte aligned
+ * (one word per thread); otherwise W4A16_ERR_MISALIGNED.
  */
 w4a16_status_t w4a16_unpack_debug(const uint32_t *qweight, int8_t *q_out, int64_t N, int64_t K,
                                   hipStream_t stream);

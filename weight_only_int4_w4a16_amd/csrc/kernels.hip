@@ -38,6 +38,10 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+#ifndef W4A16_SHIFT64
+#define W4A16_SHIFT64 1
+#endif
+
 // Weights are read exactly once per call: stream them past the caches when asked to.
 #ifndef W4A16_STREAM_LOADS
 #define W4A16_STREAM_LOADS 1
@@ -81,6 +85,37 @@ __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t p[4])
     p[3] = ((w >> 12) & kMask) ^ kMagic;
 }
 
+// Words 0-1 and 2-3 of a 16-byte chunk unpacked with one 64-bit shift per nibble position
+// (bits crossing from the high word land in bits 28-31 of the low word, which the mask drops):
+// p[j][0..3] are the four bf16 pairs of word j, as unpack_word would give.
+__device__ __forceinline__ void unpack_chunk(uint4 wv, uint32_t p[4][4])
+{
+#if W4A16_SHIFT64
+    const uint64_t d2[2] = {((uint64_t)wv.y << 32) | wv.x, ((uint64_t)wv.w << 32) | wv.z};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint64_t s4, s8, s12;
+        const uint64_t s0 = d2[h];
+        asm("v_lshrrev_b64 %0, 4, %1" : "=v"(s4) : "v"(s0));
+        asm("v_lshrrev_b64 %0, 8, %1" : "=v"(s8) : "v"(s0));
+        asm("v_lshrrev_b64 %0, 12, %1" : "=v"(s12) : "v"(s0));
+        p[2 * h][0] = ((uint32_t)s0 & kMask) ^ kMagic;
+        p[2 * h][1] = ((uint32_t)s4 & kMask) ^ kMagic;
+        p[2 * h][2] = ((uint32_t)s8 & kMask) ^ kMagic;
+        p[2 * h][3] = ((uint32_t)s12 & kMask) ^ kMagic;
+        p[2 * h + 1][0] = ((uint32_t)(s0 >> 32) & kMask) ^ kMagic;
+        p[2 * h + 1][1] = ((uint32_t)(s4 >> 32) & kMask) ^ kMagic;
+        p[2 * h + 1][2] = ((uint32_t)(s8 >> 32) & kMask) ^ kMagic;
+        p[2 * h + 1][3] = ((uint32_t)(s12 >> 32) & kMask) ^ kMagic;
+    }
+#else
+    unpack_word(wv.x, p[0]);
+    unpack_word(wv.y, p[1]);
+    unpack_word(wv.z, p[2]);
+    unpack_word(wv.w, p[3]);
+#endif
+}
+
 // Eight consecutive bf16 activations (x0..x7 in natural order) re-paired as
 // (x0,x4) (x1,x5) (x2,x6) (x3,x7) to match unpack_word.
 __device__ __forceinline__ uint4 pair_activations(uint4 v)
@@ -92,10 +127,6 @@ __device__ __forceinline__ uint4 pair_activations(uint4 v)
     o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
     return o;
 }
-
-#ifndef W4A16_SHIFT64
-#define W4A16_SHIFT64 1
-#endif
 
 __device__ __forceinline__ float chunk_dot(uint4 wv, const uint4 xq[4], float acc)
 {
@@ -241,7 +272,8 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     const int pr = lane & (L - 1);
     const int rr = lane / L;
     const int wpb = blockDim.x >> 6;
-    const int64_t gw = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6);
+    // The wave index is the same in every lane; saying so lets row bases live in scalar registers.
+    const int64_t gw = (int64_t)blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t GW = (int64_t)gridDim.x * wpb;
     const int64_t rows_total = MOE ? (int64_t)topk * N : N;
     const int64_t n_super = (rows_total + ROWS - 1) / ROWS;
@@ -250,6 +282,27 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     const int64_t gw_c = active ? gw : n_super - 1;
     const int64_t n_items = ((n_super - 1 - gw_c) / GW + 1) * nb;
 
+    // Dense rows: a wave-uniform base row plus fixed per-lane offsets. The last row block is pulled
+    // back to end at the last row (rows computed twice get identical bits); with fewer rows than
+    // one block the lane rows are clamped instead.
+    const bool full = rows_total >= ROWS;
+    uint32_t woff[U], soff[U];
+    int lrow[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int r = u * R + rr;
+        if (!full && r > rows_total - 1)
+            r = (int)rows_total - 1;
+        lrow[u] = r;
+        woff[u] = (uint32_t)((r * CPR + pr) * 16);
+        soff[u] = (uint32_t)((r * GPR + (pr >> 2)) * 2);
+    }
+    auto st_row0 = [&](int64_t st) -> int64_t {
+        if (!full)
+            return 0;
+        const int64_t r0 = st * ROWS;
+        return r0 + ROWS <= rows_total ? r0 : rows_total - ROWS;
+    };
     struct Rows {
         const uint4 *w[U];
         const uint16_t *s[U];
@@ -276,16 +329,31 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     int64_t ld_st = gw_c;
     int ld_b = 0;
     auto load = [&](ValuBuf<L, V, U> &buf) {
-        Rows r;
-        rows_of(ld_st, r);
+        if constexpr (MOE) {
+            Rows r;
+            rows_of(ld_st, r);
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const int c = pr + L * (v + V * ld_b);
+            for (int v = 0; v < V; ++v) {
+                const int c = pr + L * (v + V * ld_b);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                buf.w[v][u] = load_weights(r.w[u] + c);
-                buf.s[v][u] = r.s[u][c >> 2];
+                for (int u = 0; u < U; ++u) {
+                    buf.w[v][u] = load_weights(r.w[u] + c);
+                    buf.s[v][u] = r.s[u][c >> 2];
+                }
             }
+        } else {
+            const int64_t r0 = st_row0(ld_st);
+            const char *wb = reinterpret_cast<const char *>(qw + r0 * CPR + L * V * ld_b);
+            const char *sb = reinterpret_cast<const char *>(sc + r0 * GPR + (L / 4) * V * ld_b);
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    buf.w[v][u] = load_weights(
+                        reinterpret_cast<const uint4 *>(wb + woff[u] + 16 * L * v));
+                    buf.s[v][u] =
+                        *reinterpret_cast<const uint16_t *>(sb + soff[u] + 2 * (L / 4) * v);
+                }
         }
         const bool wrap = ld_b + 1 == nb;
         ld_b = wrap ? 0 : ld_b + 1;
@@ -339,7 +407,7 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 v[u] = acc[u][t];
             const int u = fold_rows<L, U>(v, pr);
             if ((pr & (L / U - 1)) == 0) {
-                const int64_t vrow = st * ROWS + u * R + rr;
+                const int64_t vrow = MOE ? st * ROWS + u * R + rr : st_row0(st) + lrow[u];
                 if (vrow < rows_total) {
                     bool zero = false;
                     if (MOE) {
@@ -429,7 +497,7 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
     const int CPR = K >> 5;
     const int GPR = K >> 7;
     const int W = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int pr = lane & (L - 1);
     const int rr = lane / L;
@@ -443,22 +511,39 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
         uint4 w[CL][U];
         uint16_t s[CL][U];
     };
+    // Item rows: a uniform first row plus fixed per-lane offsets; the block's last item is pulled
+    // back to end at its last row (rows computed twice get identical bits), and a block with fewer
+    // rows than one item clamps the lane rows instead.
+    const bool full = rcount >= ROWS;
+    uint32_t woff[U], soff[U];
+    int lrow[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int r = u * R + rr;
+        if (!full && r > rcount - 1)
+            r = rcount - 1;
+        lrow[u] = r;
+        woff[u] = (uint32_t)((r * CPR + cbase) * 16);
+        soff[u] = (uint32_t)((r * GPR + (cbase >> 2)) * 2);
+    }
+    auto item_row0 = [&](int item) -> int {
+        if (!full)
+            return 0;
+        const int r = item * ROWS;
+        return r + ROWS <= rcount ? r : rcount - ROWS;
+    };
     int ld_item = 0;
     auto load = [&](Buf &buf) {
+        const int64_t row0 = r0 + item_row0(ld_item);
+        const char *wb = reinterpret_cast<const char *>(qw + row0 * CPR);
+        const char *sb = reinterpret_cast<const char *>(sc + row0 * GPR);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int lr = ld_item * ROWS + u * R + rr;           // row within the block
-            lr = lr < rcount ? lr : rcount - 1;
-            const int64_t row = r0 + lr;
-            const uint4 *wr = qw + row * CPR;
-            const uint16_t *sr = sc + row * GPR;
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < CL; ++j) {
-                const int c = cbase + L * j;
-                buf.w[j][u] = load_weights(wr + c);
-                buf.s[j][u] = sr[c >> 2];
+                buf.w[j][u] = load_weights(reinterpret_cast<const uint4 *>(wb + woff[u] + 16 * L * j));
+                buf.s[j][u] = *reinterpret_cast<const uint16_t *>(sb + soff[u] + 2 * (L / 4) * j);
             }
-        }
         ++ld_item;
     };
 
@@ -520,9 +605,8 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
                 v[u] = acc[u][t];
             const int u = fold_rows<L, U>(v, pr);
             if ((pr & (L / U - 1)) == 0) {
-                const int lr = cp_item * ROWS + u * R + rr;
-                if (lr < rcount)
-                    red[((int64_t)t * rows_per_block + lr) * W + wave] = v[0];
+                const int lr = item_row0(cp_item) + lrow[u];
+                red[((int64_t)t * rows_per_block + lr) * W + wave] = v[0];
             }
         }
         ++cp_item;
@@ -555,14 +639,21 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
 }
 
 // ------------------------------------------------------------------------------------------
-// MFMA GEMV for 2..16 tokens (v_mfma_f32_16x16x32_bf16). A = 16 weight rows x 32 K values: lane
-// (i = l%16, g = l/16) unpacks word j of chunk 4s+g of row i into 8 bf16 (136+q, re-paired); B = the
-// same K positions of token i's activations (loaded from global memory and re-paired in registers);
-// D[4g+r][i] accumulates over the 4 words of the group. The 136 offset is removed by starting D at
-// -(136 * column sums), themselves one MFMA chain against a constant-136 A operand per group, shared
-// by every tile. The group total is scaled by the row's fp16 scale in fp32.
-// A wave owns T tiles of 16 rows; KS waves of a block split the groups of K and their partial sums
-// are added through LDS in a fixed order.
+// MFMA GEMV for 2..16 tokens (v_mfma_f32_16x16x32_bf16), computed as D = X * W^T so that each
+// lane's four outputs belong to one weight row: lane (i = l%16, g = l/16) supplies, for word j of
+// chunk 4s+g of a group s, the 8 activations of token i (A operand, re-paired) and the 8 decoded
+// weights 136+q of row i (B operand); D[4g+r][i] is token 4g+r of row i. The 136 offset is removed
+// by starting each group's D at -136 * (the token's sum over the group), and the group total is
+// scaled by row i's fp16 scale in fp32 -- one 2-byte scale load per tile and group.
+//
+// XLDS (K*32 bytes fit in LDS): the activations of all 16 token slots are staged once per work-group
+// in fragment order ([group][word][lane], 16 bytes each) together with the per-(group, token)
+// offsets; work-groups are persistent and stream tiles of 16 rows in a flat (row block, group)
+// sequence with one item of prefetch. Otherwise each wave reads its activation fragments from
+// global memory with its weights, KS waves of a work-group split the groups of K, and their
+// partial sums are added through LDS in a fixed order.
+// Token slots past M read token M-1 (their outputs are never stored); rows past N re-read row
+// N-1 (never stored). Every load is unconditional.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
@@ -570,136 +661,297 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int T, int KS>
-__global__ void __launch_bounds__(256)
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return as_bf16x8(v.x, v.y, v.z, v.w); }
+
+template <int T, int GU, bool XLDS>
+struct MfmaBuf {
+    uint4 w[GU][T];
+    uint16_t s[GU][T];
+    uint4 x[XLDS ? 1 : GU][4];     // activation fragments (global-memory mode only)
+};
+
+// The GU scales of one row for groups s..s+GU-1. With GU even (and so the group count of a row
+// even, and s even) they are 4-byte aligned and come in GU/2 dword loads.
+template <int GU>
+__device__ __forceinline__ void load_scales(const char *p, uint16_t (&out)[GU])
+{
+    if constexpr (GU % 2 == 0) {
+#pragma unroll
+        for (int k = 0; k < GU / 2; ++k) {
+            const uint32_t v = reinterpret_cast<const uint32_t *>(p)[k];
+            out[2 * k] = (uint16_t)(v & 0xFFFFu);
+            out[2 * k + 1] = (uint16_t)(v >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < GU; ++k)
+            out[k] = reinterpret_cast<const uint16_t *>(p)[k];
+    }
+}
+
+template <int T, int KS, bool XLDS, int GU, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
 gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                  const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
                  int32_t M, int64_t N, int32_t K)
 {
-    constexpr int RG = 4 / KS;   // row groups per block
-    __shared__ f32x4_t red[KS > 1 ? 4 : 1][T][64];
+    static_assert(WPB % KS == 0, "waves per block must be a multiple of the K split");
+    constexpr int RG = WPB / KS;               // row groups (waves with distinct rows) per block
+    constexpr int TROWS = 16 * T;              // rows per wave item
+    using Buf = MfmaBuf<T, GU, XLDS>;
+    extern __shared__ uint4 lds[];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15;
     const int g = lane >> 4;
     const int ks = wave % KS;
     const int rg = wave / KS;
     const int CPR = K >> 5;
     const int GPR = K >> 7;
-    const int gpk = GPR / KS;
-    const int s0 = ks * gpk;
-    const int s1 = s0 + gpk;
-    const int64_t row0 = ((int64_t)blockIdx.x * RG + rg) * (16 * T);
-
-    const uint4 *wp[T];
-    const uint16_t *sp[T][4];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        int64_t ra = row0 + t * 16 + i;
-        ra = ra < N ? ra : N - 1;
-        wp[t] = qw + ra * CPR + g;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int64_t rd = row0 + t * 16 + 4 * g + r;
-            rd = rd < N ? rd : N - 1;
-            sp[t][r] = sc + rd * GPR;
-        }
-    }
-    const bool xon = i < M;
-    const uint4 *xp = reinterpret_cast<const uint4 *>(X + (int64_t)(xon ? i : 0) * ldx) + 4 * g;
+    const int tok = i < M ? i : M - 1;
     const bf16x8_t c136 = as_bf16x8(0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u);
 
-    f32x4_t acc[T];
+    // Rows of a wave: base(rb) + lane_row[t] for tile t. The base of the last row block is pulled
+    // back so that the block ends at row N-1 (rows computed twice get identical bits); when N is
+    // smaller than one row block the lane rows are clamped instead. Addresses are a wave-uniform
+    // base plus a per-lane 32-bit byte offset fixed for the whole kernel.
+    const int64_t RGT = RG * TROWS;
+    const int64_t n_rb = (N + RGT - 1) / RGT;
+    const bool full = N >= RGT;
+    uint32_t woff[T], soff[T];
+    int lane_row[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-        acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // Everything one group needs from memory: weights of T tiles, their scales (D-layout rows),
-    // and the token's 32 activations at this lane's K slot.
-    struct GroupBuf {
-        uint4 w[T];
-        uint16_t sc[T][4];
-        uint4 x[4];
+    for (int t = 0; t < T; ++t) {
+        int r = rg * TROWS + 16 * t + i;
+        if (!full && r > N - 1)
+            r = (int)N - 1;
+        lane_row[t] = r;
+        woff[t] = (uint32_t)((r * CPR + g) * 16);
+        soff[t] = (uint32_t)(r * GPR * 2);
+    }
+    auto rb_row0 = [&](int64_t rb) -> int64_t {
+        if (!full)
+            return 0;
+        const int64_t r0 = rb * RGT;
+        return r0 + RGT <= N ? r0 : N - RGT;
     };
-    auto gload = [&](int s, GroupBuf &g) {
+    auto mma_group = [&](const uint4 (&wv)[T], const uint16_t (&sv)[T], const bf16x8_t xb[4],
+                         f32x4_t off, f32x4_t (&acc)[T]) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            g.w[t] = load_weights(wp[t] + 4 * s);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                g.sc[t][r] = sp[t][r][s];
-        }
-        // Lanes past M read token 0: their output columns are never stored.
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            g.x[j] = xp[16 * s + j];
-    };
-    auto gcompute = [&](const GroupBuf &g) {
-        bf16x8_t xb[4];
-        f32x4_t off = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint4 pq = pair_activations(g.x[j]);
-            xb[j] = as_bf16x8(pq.x, pq.y, pq.z, pq.w);
-            off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c136, xb[j], off, 0, 0, 0);
-        }
-        off = -off;
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const uint32_t wd[4] = {g.w[t].x, g.w[t].y, g.w[t].z, g.w[t].w};
+            uint32_t p[4][4];
+            unpack_chunk(wv[t], p);
             f32x4_t d = off;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t p[4];
-                unpack_word(wd[j], p);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p[0], p[1], p[2], p[3]),
-                                                             xb[j], d, 0, 0, 0);
-            }
+            for (int j = 0; j < 4; ++j)
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    xb[j], as_bf16x8(p[j][0], p[j][1], p[j][2], p[j][3]), d, 0, 0, 0);
+            const float scv = half_bits_to_float(sv[t]);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                acc[t][r] = fmaf(half_bits_to_float(g.sc[t][r]), d[r], acc[t][r]);
+                acc[t][r] = fmaf(scv, d[r], acc[t][r]);
         }
     };
-
-    // Two groups in flight: load s+1 while s is multiplied.
-    GroupBuf ga, gb;
-    if (s0 < s1)
-        gload(s0, ga);
-    for (int s = s0; s < s1; s += 2) {
-        if (s + 1 < s1)
-            gload(s + 1, gb);
-        gcompute(ga);
-        if (s + 2 < s1)
-            gload(s + 2, ga);
-        if (s + 1 < s1)
-            gcompute(gb);
-    }
-
-    if (KS > 1) {
-        if (ks != 0) {
+    auto store = [&](int64_t rb, const f32x4_t (&acc)[T]) {
+        const int64_t r0 = rb_row0(rb);
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                red[wave][t][lane] = acc[t];
+        for (int t = 0; t < T; ++t) {
+            const int64_t row = r0 + lane_row[t];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * g + r;
+                if (m < M)
+                    Y[(int64_t)m * ldy + row] = acc[t][r];
+            }
+        }
+    };
+    auto wbase = [&](int64_t rb, int s_) {
+        return reinterpret_cast<const char *>(qw + rb_row0(rb) * CPR + 4 * s_);
+    };
+    auto sbase = [&](int64_t rb, int s_) {
+        return reinterpret_cast<const char *>(sc + rb_row0(rb) * GPR + s_);
+    };
+
+    if constexpr (XLDS) {
+        static_assert(KS == 1, "staged activations serve whole rows");
+        uint4 *xl = lds;                                             // [GPR][4][64]
+        float *offl = reinterpret_cast<float *>(lds + GPR * 256);   // [GPR][16]
+        // A flat sequence of (row block, run of GU groups) items for this work-group.
+        const int cpr_items = GPR / GU;
+        const bool active = blockIdx.x < n_rb;
+        const int64_t rb_first = active ? blockIdx.x : n_rb - 1;
+        const int64_t n_items = ((n_rb - 1 - rb_first) / gridDim.x + 1) * cpr_items;
+        int64_t ld_rb = rb_first;
+        int ld_s = 0;
+        auto load = [&](Buf &buf) {
+            const int64_t rb = ld_rb < n_rb ? ld_rb : n_rb - 1;
+            const char *wb = wbase(rb, ld_s);
+            const char *sb = sbase(rb, ld_s);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+#pragma unroll
+                for (int u = 0; u < GU; ++u)
+                    buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + woff[t] + 64 * u));
+                uint16_t sv[GU];
+                load_scales<GU>(sb + soff[t], sv);
+#pragma unroll
+                for (int u = 0; u < GU; ++u)
+                    buf.s[u][t] = sv[u];
+            }
+            const bool wrap = ld_s + GU == GPR;
+            ld_s = wrap ? 0 : ld_s + GU;
+            ld_rb += wrap ? gridDim.x : 0;
+        };
+        Buf bufA, bufB;
+        load(bufA);
+
+        // Stage the fragments of all 16 token slots and the per-(group, token) offsets.
+        for (int idx = threadIdx.x; idx < GPR * 256; idx += blockDim.x) {
+            const int s = idx >> 8, j = (idx >> 6) & 3, l = idx & 63;
+            const int m = l & 15, gg = l >> 4;
+            const int tm = m < M ? m : M - 1;
+            const uint4 v = reinterpret_cast<const uint4 *>(X + (int64_t)tm * ldx)[16 * s + 4 * gg + j];
+            xl[idx] = pair_activations(v);
+        }
+        for (int idx = threadIdx.x; idx < GPR * 16; idx += blockDim.x) {
+            const int s = idx >> 4, m = idx & 15;
+            const int tm = m < M ? m : M - 1;
+            const uint4 *xr = reinterpret_cast<const uint4 *>(X + (int64_t)tm * ldx) + 16 * s;
+            float sum = 0.0f;
+            for (int q = 0; q < 16; ++q) {
+                const uint4 v = xr[q];
+                sum = dot2(v.x, 0x3F803F80u, sum);
+                sum = dot2(v.y, 0x3F803F80u, sum);
+                sum = dot2(v.z, 0x3F803F80u, sum);
+                sum = dot2(v.w, 0x3F803F80u, sum);
+            }
+            offl[idx] = -kOffset * sum;
         }
         __syncthreads();
-        if (ks != 0)
+        if (!active)
             return;
+
+        f32x4_t acc[T];
 #pragma unroll
-        for (int k2 = 1; k2 < KS; ++k2)
+        for (int t = 0; t < T; ++t)
+            acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        int64_t cp_rb = rb_first;
+        int cp_s = 0;
+        auto compute = [&](const Buf &buf) {
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                acc[t] += red[rg * KS + k2][t][lane];
-    }
-    if (!xon)
-        return;
+            for (int u = 0; u < GU; ++u) {
+                const int s = cp_s + u;
+                bf16x8_t xb[4];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+                for (int j = 0; j < 4; ++j)
+                    xb[j] = as_bf16x8(xl[(s * 4 + j) * 64 + lane]);
+                const float4 o4 = *reinterpret_cast<const float4 *>(offl + s * 16 + 4 * g);
+                const f32x4_t off = {o4.x, o4.y, o4.z, o4.w};
+                mma_group(buf.w[u], buf.s[u], xb, off, acc);
+            }
+            if (cp_s + GU == GPR) {
+                store(cp_rb, acc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t row = row0 + t * 16 + 4 * g + r;
-            if (row < N)
-                Y[(int64_t)i * ldy + row] = acc[t][r];
+                for (int t = 0; t < T; ++t)
+                    acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            const bool wrap = cp_s + GU == GPR;
+            cp_s = wrap ? 0 : cp_s + GU;
+            cp_rb += wrap ? gridDim.x : 0;
+        };
+        int64_t it = 0;
+        for (; it + 2 < n_items; it += 2) {
+            load(bufB);
+            compute(bufA);
+            load(bufA);
+            compute(bufB);
         }
+        if (it + 1 < n_items) {
+            load(bufB);
+            compute(bufA);
+            compute(bufB);
+        } else {
+            compute(bufA);
+        }
+    } else {
+        // One row block per work-group; KS waves split the groups of K into runs of GU.
+        f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);           // [WPB][T][64]
+        const int64_t rb = blockIdx.x;
+        const int gpk = GPR / KS;
+        const int n_items = gpk / GU;
+        const uint4 *xp = reinterpret_cast<const uint4 *>(X + (int64_t)tok * ldx) + 4 * g;
+        int ld_s = ks * gpk;
+        auto load = [&](Buf &buf) {
+            const char *wb = wbase(rb, ld_s);
+            const char *sb = sbase(rb, ld_s);
+#pragma unroll
+            for (int u = 0; u < GU; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    buf.x[u][j] = xp[16 * (ld_s + u) + j];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+#pragma unroll
+                for (int u = 0; u < GU; ++u)
+                    buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + woff[t] + 64 * u));
+                uint16_t sv[GU];
+                load_scales<GU>(sb + soff[t], sv);
+#pragma unroll
+                for (int u = 0; u < GU; ++u)
+                    buf.s[u][t] = sv[u];
+            }
+            ld_s += GU;
+        };
+        f32x4_t acc[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        auto compute = [&](const Buf &buf) {
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                bf16x8_t xb[4];
+                f32x4_t off = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xb[j] = as_bf16x8(pair_activations(buf.x[u][j]));
+                    off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], c136, off, 0, 0, 0);
+                }
+                mma_group(buf.w[u], buf.s[u], xb, -off, acc);
+            }
+        };
+        Buf bufA, bufB;
+        load(bufA);
+        int it = 0;
+        for (; it + 2 < n_items; it += 2) {
+            load(bufB);
+            compute(bufA);
+            load(bufA);
+            compute(bufB);
+        }
+        if (it + 1 < n_items) {
+            load(bufB);
+            compute(bufA);
+            compute(bufB);
+        } else {
+            compute(bufA);
+        }
+        if (KS > 1) {
+            if (ks != 0) {
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    red[(wave * T + t) * 64 + lane] = acc[t];
+            }
+            __syncthreads();
+            if (ks != 0)
+                return;
+#pragma unroll
+            for (int k2 = 1; k2 < KS; ++k2)
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    acc[t] += red[((rg * KS + k2) * T + t) * 64 + lane];
+        }
+        store(rb, acc);
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -750,18 +1002,17 @@ static hipError_t launch_splitk_t(const GemvArgs &a, const Plan &p, hipStream_t 
                            args, (size_t)p.lds_bytes, stream);
 }
 
-template <int T, int KS>
+template <int T, int KS, bool XLDS, int GU, int WPB>
 static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
-    auto kern = gemv_mfma_kernel<T, KS>;
+    auto kern = gemv_mfma_kernel<T, KS, XLDS, GU, WPB>;
     void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X, (void *)&a.ldx,
                     (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.M, (void *)&a.N,
                     (void *)&a.K};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(256), args,
-                           0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(64 * WPB),
+                           args, (size_t)p.lds_bytes, stream);
 }
 
-// The grouped-expert form exists for one token only, so MoE variants are built only for MT == 1.
 #define W4A16_VALU_CASE(MT_, L_, V_, U_)                                                     \
     if (p.MT == MT_ && p.L == L_ && p.V == V_ && p.U == U_)                                  \
         return p.moe ? launch_valu_t<MT_, L_, V_, U_, (MT_ == 1)>(a, p, stream)              \
@@ -771,9 +1022,9 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
     if (p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_ && !p.moe)                       \
         return launch_splitk_t<MT_, L_, CL_, U_>(a, p, stream);
 
-#define W4A16_MFMA_CASE(T_, KS_)                                                             \
-    if (p.T == T_ && p.KS == KS_)                                                            \
-        return launch_mfma_t<T_, KS_>(a, p, stream);
+#define W4A16_MFMA_CASE(T_, KS_, XL_, GU_, WPB_)                                             \
+    if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) && p.V == GU_ && p.threads == 64 * WPB_) \
+        return launch_mfma_t<T_, KS_, (XL_ != 0), GU_, WPB_>(a, p, stream);
 
 hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {

@@ -24,8 +24,9 @@ bool plan_instantiated(const Plan &p)
 #define W4A16_SPLITK_MATCH(MT_, L_, CL_, U_)                                                  \
     if (p.kind == PLAN_SPLITK && p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_)          \
         return true;
-#define W4A16_MFMA_MATCH(T_, KS_)                                                            \
-    if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_)                                      \
+#define W4A16_MFMA_MATCH(T_, KS_, XL_, GU_, WPB_)                                            \
+    if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) &&            \
+        p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))                             \
         return true;
     W4A16_VALU_CONFIGS(W4A16_VALU_MATCH)
     W4A16_MFMA_CONFIGS(W4A16_MFMA_MATCH)
@@ -109,12 +110,33 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
         return blocks >= 1 && blocks < (1LL << 31);
     }
     if (p->kind == PLAN_MFMA) {
-        if (gpr % p->KS != 0)
+        if (p->threads == 0)
+            p->threads = 256;
+        const int wpb = p->threads / 64;
+        if (p->threads % 64 || wpb < 1 || wpb % p->KS != 0 || !plan_instantiated(*p))
             return false;
-        p->threads = 256;
-        p->lds_bytes = 0;
-        const int64_t rows_per_block = 16LL * p->T * (4 / p->KS);
-        p->blocks = (N + rows_per_block - 1) / rows_per_block;
+        if (p->V < 1 || gpr % p->KS != 0 || (gpr / p->KS) % p->V != 0 || (p->xlds && p->KS != 1))
+            return false;
+        const int64_t rows_per_block = 16LL * p->T * (wpb / p->KS);
+        const int64_t row_blocks = (N + rows_per_block - 1) / rows_per_block;
+        if (p->xlds) {
+            // 16 token slots of activation fragments (16 bytes per lane, word and group) plus
+            // one fp32 offset per (group, token).
+            p->lds_bytes = gpr * 4096 + gpr * 64;
+            if (p->lds_bytes > lds_limit)
+                return false;
+            int per_cu = blocks_per_cu;
+            const int64_t by_lds = lds_limit / p->lds_bytes;
+            if (per_cu > by_lds)
+                per_cu = (int)by_lds;
+            if (per_cu < 1)
+                per_cu = 1;
+            const int64_t cap = (int64_t)cus * per_cu;
+            p->blocks = row_blocks < cap ? row_blocks : cap;
+        } else {
+            p->lds_bytes = p->KS > 1 ? (int64_t)wpb * p->T * 64 * 16 : 0;
+            p->blocks = row_blocks;
+        }
         return p->blocks >= 1 && p->blocks < (1LL << 31);
     }
     return false;
@@ -124,8 +146,10 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
 // 1 GiB of copies (so the 256 MB memory-side cache cannot serve them):
 //  * dense, 1-4 tokens, K a multiple of 2048 up to 16384: split-K with 64 lanes per row and 4 rows
 //    per item, about 8 waves per CU (one work-group of K/2048 waves, 8/W groups per CU); very short
-//    one-token matrices (<= 16 rows per CU) use 32 lanes and 2-row items instead; K above 16384
-//    uses 2 or 4 chunks per lane so that a work-group stays within 8 waves;
+//    one-token matrices (<= 16 rows per CU) use 32 lanes and 2-row items instead, and tall
+//    one-token matrices with K = 4096 (>= 16384 rows) the staged kernel with 32 lanes per row and
+//    2 chunks per item; K above 16384 uses 2 or 4 chunks per lane so that a work-group stays
+//    within 8 waves;
 //  * other K, and every grouped-expert call: the staged kernel with the widest power-of-two lanes
 //    per row dividing the row's 16-byte chunks; rows of 72 chunks (K = 2304) use 8 lanes with
 //    3 chunks per item;
@@ -185,6 +209,9 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     const bool k2048 = cpr % 64 == 0;
 
     const int split_bpc = (int)(c64 >= 8 ? 1 : 8 / (c64 > 0 ? c64 : 1));
+    if (!moe && M == 1 && K == 4096 && rows >= 16384 &&
+        try_plan(valu(1, 32, 2, 1, false), 8, M, N, K, topk, cus, lds_limit, p))
+        return true;
     if (!moe && k2048 && c64 >= 2 && c64 <= 8 && M <= 4) {
         if (M == 1 && rows <= 16LL * cus &&
             try_plan(splitk(1, 32, 1, 2, false), 2, M, N, K, topk, cus, lds_limit, p))
@@ -217,20 +244,41 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
         if (try_plan(valu(M, L, 1, 1, false), M == 2 ? 4 : 8, M, N, K, topk, cus, lds_limit, p))
             return true;
     }
-    // MFMA: two 16-row tiles per wave; split K across waves when rows alone leave CUs idle.
-    static const int mf[][2] = {{2, 1}, {2, 2}, {1, 2}, {1, 4}, {1, 1}};
+    // MFMA. A lane's 16-byte weight load covers half of a 128-byte line of its row, so an item always
+    // spans an even number of groups when it can: both halves of every line are requested back to
+    // back. Activations staged in LDS when 16 token slots of K fit in half the LDS (persistent
+    // 8-wave work-groups, one 16-row tile per wave, 6/4/2 groups per item); otherwise activations
+    // come from global memory: two tiles per wave, K split over 4 (or 2, or 1) waves while that
+    // keeps at least 2 work-groups per CU.
     const int64_t gpr = K / 128;
+    if (gpr * 4160 <= lds_limit / 2) {
+        static const int gus[] = {6, 4, 2, 1};
+        for (int gu : gus) {
+            Plan c{};
+            c.kind = PLAN_MFMA;
+            c.T = 1;
+            c.KS = 1;
+            c.V = gu;
+            c.xlds = true;
+            c.threads = 512;
+            if (gpr % gu == 0 && try_plan(c, 1, M, N, K, topk, cus, lds_limit, p))
+                return true;
+        }
+    }
+    static const int mf[][3] = {{2, 4, 2}, {2, 2, 2}, {2, 1, 2}, {1, 1, 2}, {1, 1, 1}};
     for (int i = 0; i < (int)(sizeof(mf) / sizeof(mf[0])); ++i) {
         Plan c{};
         c.kind = PLAN_MFMA;
         c.T = mf[i][0];
         c.KS = mf[i][1];
-        if (gpr % c.KS != 0)
+        c.V = mf[i][2];
+        c.threads = 256;
+        if (gpr % c.KS != 0 || (gpr / c.KS) % c.V != 0)
             continue;
         const int64_t rows_per_block = 16LL * c.T * (4 / c.KS);
         const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
         const bool last = i == (int)(sizeof(mf) / sizeof(mf[0])) - 1;
-        if (blocks < 2LL * cus && !last)
+        if (blocks < 2LL * cus && c.KS == 1 && !last)
             continue;
         if (try_plan(c, 1, M, N, K, topk, cus, lds_limit, p))
             return true;
@@ -256,8 +304,11 @@ int describe_plan(const Plan &p, char *buf, size_t len)
                      p.moe ? "_moe" : "", p.MT, p.L, p.V, p.U, p.threads, (long long)p.blocks,
                      (long long)p.rows_per_block, (long long)p.lds_bytes);
     else if (p.kind == PLAN_MFMA)
-        n = snprintf(buf, len, "mfma16x16x32 tiles_per_wave=%d k_split=%d threads=%d blocks=%lld",
-                     p.T, p.KS, p.threads, (long long)p.blocks);
+        n = snprintf(buf, len,
+                     "mfma16x16x32%s tiles_per_wave=%d k_split=%d groups_per_item=%d threads=%d "
+                     "blocks=%lld lds=%lld",
+                     p.xlds ? "_lds" : "", p.T, p.KS, p.V, p.threads, (long long)p.blocks,
+                     (long long)p.lds_bytes);
     else
         n = snprintf(buf, len, "none");
     return n;

@@ -18,7 +18,7 @@ enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3 };
 #ifndef W4A16_VALU_CONFIGS
 #define W4A16_VALU_CONFIGS(X)                                                                \
     X(1, 64, 1, 1) X(1, 32, 1, 1) X(1, 16, 1, 1) X(1, 8, 1, 1) X(1, 4, 1, 1)                 \
-    X(1, 32, 1, 2) X(1, 16, 1, 2) X(1, 8, 1, 2) X(1, 8, 3, 1) X(1, 4, 1, 2)                  \
+    X(1, 32, 1, 2) X(1, 32, 2, 1) X(1, 16, 1, 2) X(1, 8, 1, 2) X(1, 8, 3, 1) X(1, 4, 1, 2)   \
     X(2, 64, 1, 1) X(2, 32, 1, 1) X(2, 16, 1, 1) X(2, 8, 1, 1) X(2, 4, 1, 1) X(2, 8, 1, 2)    \
     X(3, 64, 1, 1) X(3, 32, 1, 1) X(3, 16, 1, 1) X(3, 8, 1, 1) X(3, 4, 1, 1)                 \
     X(4, 64, 1, 1) X(4, 32, 1, 1) X(4, 16, 1, 1) X(4, 8, 1, 1) X(4, 4, 1, 1)
@@ -31,15 +31,19 @@ enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3 };
     X(2, 64, 1, 4) X(3, 64, 1, 4) X(4, 64, 1, 4)
 #endif
 
-// MFMA kernels: X(16-row tiles per wave, waves splitting K).
+// MFMA kernels: X(16-row tiles per wave, waves splitting K, activations staged in LDS,
+// groups per item, waves per work-group).
 #ifndef W4A16_MFMA_CONFIGS
-#define W4A16_MFMA_CONFIGS(X) X(1, 1) X(2, 1) X(4, 1) X(1, 2) X(2, 2) X(1, 4) X(2, 4)
+#define W4A16_MFMA_CONFIGS(X)                                                                \
+    X(1, 1, 1, 6, 8) X(1, 1, 1, 4, 8) X(1, 1, 1, 2, 8) X(1, 1, 1, 1, 8)                       \
+    X(2, 4, 0, 2, 4) X(2, 2, 0, 2, 4) X(2, 1, 0, 2, 4) X(1, 1, 0, 2, 4) X(1, 1, 0, 1, 4)
 #endif
 
 struct Plan {
     int kind;
     int MT, L, V, U;   // VALU: tokens, lanes per row, chunks per lane per item, row steps per item
-    int T, KS;         // MFMA: 16-row tiles per wave, waves splitting K
+    int T, KS;         // MFMA: 16-row tiles per wave, waves splitting K (V: groups per item)
+    bool xlds;         // MFMA: activations of all 16 token slots staged in LDS
     bool moe;
     int threads;       // work-group size
     int64_t blocks;    // grid size
