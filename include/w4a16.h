@@ -107,6 +107,17 @@ w4a16_status_t w4a16_unpack_debug(const uint32_t *qweight, int8_t *q_out, int64_
                                   hipStream_t stream);
 
 /*
+ * Measurement support: reads `bytes` bytes of device memory at `buf` once with 16-byte
+ * streaming loads (blocks work-groups of 256 lanes, `unroll` loads in flight per lane per step)
+ * and writes one XOR digest word per wave to out[0 .. blocks*4 - 1]. It is the plain
+ * bandwidth ceiling a GEMV over the same bytes is compared with; it computes nothing of the
+ * GEMV. bytes >= 16, bytes % 16 == 0; 1 <= blocks <= 2^20; unroll in {1, 2, 4, 8};
+ * buf 16-byte aligned, out 4-byte aligned; the caller owns both.
+ */
+w4a16_status_t w4a16_stream_read(const void *buf, int64_t bytes, uint32_t *out, int32_t blocks,
+                                 int32_t unroll, hipStream_t stream);
+
+/*
  * Host-only introspection: writes into buf (at most len bytes, NUL-terminated) the kernel and
  * launch shape the entry points would choose for (M, N, K, topk) on a device with `cus` compute
  * units; topk = 0 means a dense call. Returns W4A16_OK or W4A16_ERR_BAD_SHAPE. Touches no device.

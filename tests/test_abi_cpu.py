@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("w4a16_gemv", "w4a16_gemv_batched", "w4a16_moe_gemv", "w4a16_unpack_debug",
-              "w4a16_describe_plan", "w4a16_status_string", "w4a16_abi_version"):
+              "w4a16_describe_plan", "w4a16_status_string", "w4a16_abi_version",
+              "w4a16_stream_read"):
         assert n in names
 
 
@@ -100,6 +101,18 @@ def test_unpack_validation():
     assert lib.w4a16_unpack_debug(A + 2, A, 4, 64, None) == ALIGN
 
 
+def test_stream_read_validation():
+    lib = w.library()
+    assert lib.w4a16_stream_read(None, 64, A, 1, 4, None) == NULLP
+    assert lib.w4a16_stream_read(A, 64, None, 1, 4, None) == NULLP
+    assert lib.w4a16_stream_read(A, 8, A, 1, 4, None) == SHAPE
+    assert lib.w4a16_stream_read(A, 72, A, 1, 4, None) == SHAPE
+    assert lib.w4a16_stream_read(A, 64, A, 0, 4, None) == SHAPE
+    assert lib.w4a16_stream_read(A, 64, A, 1, 3, None) == SHAPE
+    assert lib.w4a16_stream_read(A + 4, 64, A, 1, 4, None) == ALIGN
+    assert lib.w4a16_stream_read(A, 64, A + 2, 1, 4, None) == ALIGN
+
+
 def test_valid_arguments_reach_the_device_check_only():
     # With well-formed arguments the call gets past validation; on a host without a gfx950 GPU
     # it must stop at the device check and enqueue nothing.
@@ -109,6 +122,7 @@ def test_valid_arguments_reach_the_device_check_only():
     assert gemv() == DEVICE
     assert batched() == DEVICE
     assert moe() == DEVICE
+    assert w.library().w4a16_stream_read(A, 64, A, 1, 4, None) == DEVICE
 
 
 @pytest.mark.parametrize("M,N,K,topk,kind", [

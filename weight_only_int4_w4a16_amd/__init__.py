@@ -22,7 +22,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["gemv", "gemv_batched", "moe_gemv", "unpack_debug", "describe_plan", "W4A16Error",
+__all__ = ["gemv", "gemv_batched", "moe_gemv", "unpack_debug", "describe_plan", "stream_read",
+           "W4A16Error",
            "library", "LIB_PATH", "GROUP_SIZE", "MAX_BATCH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")
@@ -53,11 +54,13 @@ def library() -> ctypes.CDLL:
     lib.w4a16_moe_gemv.argtypes = [P, P, P, i32, i32, P, P, i64, i64, i32, P]
     lib.w4a16_unpack_debug.argtypes = [P, P, i64, i64, P]
     lib.w4a16_describe_plan.argtypes = [i32, i64, i64, i32, i32, ctypes.c_char_p, i64]
+    lib.w4a16_stream_read.argtypes = [P, i64, P, i32, i32, P]
     lib.w4a16_status_string.argtypes = [ctypes.c_int]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_abi_version.argtypes = []
     for f in (lib.w4a16_gemv, lib.w4a16_gemv_batched, lib.w4a16_moe_gemv,
-              lib.w4a16_unpack_debug, lib.w4a16_describe_plan, lib.w4a16_abi_version):
+              lib.w4a16_unpack_debug, lib.w4a16_describe_plan, lib.w4a16_stream_read,
+              lib.w4a16_abi_version):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -176,3 +179,18 @@ def describe_plan(M: int, N: int, K: int, topk: int = 0, cus: int = 256) -> str:
     buf = ctypes.create_string_buffer(256)
     _ok(library().w4a16_describe_plan(M, N, K, topk, cus, buf, len(buf)), "w4a16_describe_plan")
     return buf.value.decode()
+
+
+def stream_read(buf: torch.Tensor, nbytes: int, out: torch.Tensor, blocks: int, unroll: int,
+                stream=None) -> None:
+    """Measurement support: stream `nbytes` bytes of `buf` once (the plain read ceiling).
+    out is a uint32-sized tensor (torch.int32) of at least blocks * 4 elements."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    _need(out, torch.int32, "out", 1)
+    if out.numel() < blocks * 4:
+        raise ValueError("out needs blocks * 4 elements")
+    _ok(library().w4a16_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, unroll,
+                                    _stream(stream)), "w4a16_stream_read")

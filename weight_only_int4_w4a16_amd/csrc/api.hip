@@ -13,6 +13,8 @@ namespace w4a16 {
 hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream);
 hipError_t launch_unpack(const uint32_t *qw, int8_t *out, int64_t words, int cus,
                          hipStream_t stream);
+hipError_t launch_stream_read(const void *buf, int64_t n16, uint32_t *out, int blocks,
+                              int unroll, hipStream_t stream);
 
 namespace {
 
@@ -147,6 +149,23 @@ w4a16_status_t w4a16_unpack_debug(const uint32_t *qweight, int8_t *q_out, int64_
     if (!dev)
         return W4A16_ERR_UNSUPPORTED_DEVICE;
     return launch_unpack(qweight, q_out, N * (K / 8), dev->cus, stream) == hipSuccess
+               ? W4A16_OK
+               : W4A16_ERR_LAUNCH;
+}
+
+w4a16_status_t w4a16_stream_read(const void *buf, int64_t bytes, uint32_t *out, int32_t blocks,
+                                 int32_t unroll, hipStream_t stream)
+{
+    if (!buf || !out)
+        return W4A16_ERR_NULL_POINTER;
+    if (bytes < 16 || bytes % 16 != 0 || blocks < 1 || blocks > (1 << 20) ||
+        (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8))
+        return W4A16_ERR_BAD_SHAPE;
+    if (!aligned(buf, 16) || !aligned(out, 4))
+        return W4A16_ERR_MISALIGNED;
+    if (!current_device())
+        return W4A16_ERR_UNSUPPORTED_DEVICE;
+    return launch_stream_read(buf, bytes / 16, out, blocks, unroll, stream) == hipSuccess
                ? W4A16_OK
                : W4A16_ERR_LAUNCH;
 }
