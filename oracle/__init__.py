@@ -7,8 +7,10 @@ and the two share no code: this side is plain single-threaded C in float64
 
 It computes y[n] = sum_k q[n,k] * s[n, k/128] * x[k] exactly as that sum reads (float64),
 plus mag[n] = sum_k |q s x|, the basis of the per-element tolerance
-|err| <= 1e-3 * mag + 1e-5. See w4a16_oracle.c for the storage format and the passage of
-the local-kimi README it follows.
+|err| <= 1e-3 * mag + 1e-5. For the expert tail it also computes the SwiGLU of the grouped
+gate+up product (h = silu(g) * u, rounded to bfloat16) and the router-weighted sum of the
+grouped down projection, out = sum_t w[t] * W_down[ids[t]] h[t]. See w4a16_oracle.c for
+the storage format and the passage of the local-kimi README it follows.
 
 Pins (tests/test_oracle_pins.py) tie it to facts other than itself: hand-computed worked
 examples, IEEE decodes checked against numpy's own conversions over every bit pattern,
@@ -75,8 +77,16 @@ class Oracle:
         lib.oracle_gemv.argtypes = [P, P, P, i64, i64, i32, P, i64, P, P]
         lib.oracle_gemv_batched.argtypes = [P, P, P, i64, i32, i64, i64, i32, P, i64, P, P]
         lib.oracle_moe_gemv.argtypes = [P, P, P, i32, i32, P, i64, i64, i32, P, i64, P, P]
+        lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_moe_swiglu.argtypes = [P, P, P, i32, i32, P, i64, i64, i32,
+                                          P, P, P, P, P, P]
+        lib.oracle_moe_down_combine.argtypes = [P, P, P, P, i32, i32, P, i64, i64, i32, P, i64,
+                                                P, P]
         for f in (lib.oracle_unpack, lib.oracle_gemv, lib.oracle_gemv_batched,
-                  lib.oracle_moe_gemv):
+                  lib.oracle_moe_gemv, lib.oracle_moe_swiglu, lib.oracle_moe_down_combine):
             f.restype = ctypes.c_int
         self.lib = lib
 
@@ -137,6 +147,46 @@ class Oracle:
             raise ValueError("oracle_moe_gemv: bad arguments")
         return y, mag
 
+    def double_to_bf16(self, v: float) -> int:
+        return int(self.lib.oracle_double_to_bf16(float(v)))
+
+    def silu(self, g: float) -> float:
+        return self.lib.oracle_silu(float(g))
+
+    def moe_swiglu(self, qweight, scales, ids, x, K: int, group: int = 128) -> dict:
+        """Gate+up product of the selected experts (qweight [E][2I][K/8]) and SwiGLU.
+        Returns float64 [topk][I] arrays h, g, u, mag_g, mag_u and uint16 h_bf16."""
+        qw, sc = _c(qweight, np.uint32), _c(scales, np.uint16)
+        ii, xx = _c(ids, np.int32).reshape(-1), _c(x, np.uint16).reshape(-1)
+        E, N2 = qw.shape[0], qw.shape[1]
+        if N2 % 2:
+            raise ValueError("gate+up weights need an even row count")
+        I, T = N2 // 2, ii.size
+        out = {k: np.empty((T, I)) for k in ("h", "g", "u", "mag_g", "mag_u")}
+        out["h_bf16"] = np.empty((T, I), np.uint16)
+        if self.lib.oracle_moe_swiglu(_ptr(qw), _ptr(sc), _ptr(ii), T, E, _ptr(xx), I, K, group,
+                                      _ptr(out["h"]), _ptr(out["h_bf16"]), _ptr(out["g"]),
+                                      _ptr(out["u"]), _ptr(out["mag_g"]), _ptr(out["mag_u"])):
+            raise ValueError("oracle_moe_swiglu: bad arguments")
+        return out
+
+    def moe_down_combine(self, qweight, scales, ids, weights, h, group: int = 128,
+                         rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """(out, mag) float64 [rows]: sum_t w[t] * W_down[ids[t]] h[t], qweight [E][H][I/8]."""
+        qw, sc = _c(qweight, np.uint32), _c(scales, np.uint16)
+        ii, ww = _c(ids, np.int32).reshape(-1), _c(weights, np.float32).reshape(-1)
+        hh = _c(h, np.uint16)
+        E, H, I = qw.shape[0], qw.shape[1], qw.shape[2] * 8
+        if ww.size != ii.size or hh.shape != (ii.size, I):
+            raise ValueError("ids, weights and h disagree")
+        r, nr = _rows(rows, H)
+        out, mag = np.empty(nr), np.empty(nr)
+        if self.lib.oracle_moe_down_combine(_ptr(qw), _ptr(sc), _ptr(ii), _ptr(ww), ii.size, E,
+                                            _ptr(hh), H, I, group, _ptr(r), nr, _ptr(out),
+                                            _ptr(mag)):
+            raise ValueError("oracle_moe_down_combine: bad arguments")
+        return out, mag
+
 
 _default: Optional[Oracle] = None
 
@@ -173,6 +223,22 @@ def gemv_batched(*a, **kw):
 
 def moe_gemv(*a, **kw):
     return default().moe_gemv(*a, **kw)
+
+
+def double_to_bf16(v):
+    return default().double_to_bf16(v)
+
+
+def silu(g):
+    return default().silu(g)
+
+
+def moe_swiglu(*a, **kw):
+    return default().moe_swiglu(*a, **kw)
+
+
+def moe_down_combine(*a, **kw):
+    return default().moe_down_combine(*a, **kw)
 
 
 def bound(mag: np.ndarray) -> np.ndarray:

@@ -191,3 +191,117 @@ int oracle_moe_gemv(const uint32_t *qweight, const uint16_t *scales, const int32
     }
     return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * The expert tail after the grouped gate+up product (the local-kimi README, technical-detail
+ * section, names a SwiGLU variant of the grouped kernel beside the plain one; the pages do not
+ * define it further). Readings taken here:
+ *   - an expert's gate+up weights hold 2I rows: rows [0, I) are the gate projection, rows
+ *     [I, 2I) the up projection;
+ *   - SwiGLU is h = silu(g) * u with silu(g) = g / (1 + e^-g);
+ *   - h is an activation, so it is stored as bfloat16 (round to nearest, ties to even) before
+ *     the down projection consumes it;
+ *   - the down projection of slot t uses expert ids[t]'s weights on h[t], and the slots are
+ *     summed with the router's weights w[t]: out = sum_t w[t] * W_down[ids[t]] h[t].
+ * ------------------------------------------------------------------------------------------ */
+
+/* double -> bfloat16 bit pattern, round to nearest with ties to even, decided in double. */
+uint16_t oracle_double_to_bf16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7FC0u);
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0)
+        return sign;
+    /* Spacing of bfloat16 values around a: 2^(e-7) for a normal a in [2^e, 2^(e+1)),
+     * 2^-133 below the smallest normal 2^-126. */
+    int ex;
+    frexp(a, &ex);                     /* a = m * 2^ex, m in [0.5, 1): leading bit 2^(ex-1) */
+    int qexp = ex - 1 - 7;
+    if (qexp < -133)
+        qexp = -133;
+    double r = rint(ldexp(a, -qexp));  /* default rounding mode: nearest, ties to even */
+    double q = ldexp(r, qexp);
+    if (q >= ldexp(1.0, 128))
+        return (uint16_t)(sign | 0x7F80u);
+    float f = (float)q;                /* exact: at most 8 significant bits, in float range */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(sign | (uint16_t)((bits >> 16) & 0x7FFFu));
+}
+
+double oracle_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/*
+ * Grouped gate+up product with the SwiGLU epilogue, all I outputs of every slot:
+ *   g = W_e[n] x, u = W_e[I + n] x (e = ids[t]), h = silu(g) * u,
+ * written as [topk][I] arrays: h (double), h_bf16 (its rounded bits), g, u and the tolerance
+ * bases mag_g = sum|q s x| over the gate row and mag_u over the up row. An id outside [0, E)
+ * gives zeros everywhere.
+ */
+int oracle_moe_swiglu(const uint32_t *qweight, const uint16_t *scales, const int32_t *ids,
+                      int32_t topk, int32_t E, const uint16_t *x, int64_t I, int64_t K,
+                      int32_t G, double *h, uint16_t *h_bf16, double *g, double *u,
+                      double *mag_g, double *mag_u)
+{
+    if (!qweight || !scales || !ids || !x || !h || !h_bf16 || !g || !u || !mag_g || !mag_u)
+        return ORACLE_BAD_ARG;
+    if (topk < 1 || E < 1 || I < 1 || K < 1 || G < 8 || G % 8 || K % G)
+        return ORACLE_BAD_ARG;
+    for (int32_t t = 0; t < topk; ++t) {
+        int32_t e = ids[t];
+        for (int64_t n = 0; n < I; ++n) {
+            int64_t o = (int64_t)t * I + n;
+            if (e < 0 || e >= E) {
+                h[o] = g[o] = u[o] = mag_g[o] = mag_u[o] = 0.0;
+                h_bf16[o] = 0;
+                continue;
+            }
+            int64_t rg = (int64_t)e * 2 * I + n, ru = rg + I;
+            dot_row(qweight + rg * (K / 8), scales + rg * (K / G), x, K, G, &g[o], &mag_g[o]);
+            dot_row(qweight + ru * (K / 8), scales + ru * (K / G), x, K, G, &u[o], &mag_u[o]);
+            h[o] = oracle_silu(g[o]) * u[o];
+            h_bf16[o] = oracle_double_to_bf16(h[o]);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Down projection of every slot's own activation row and the router-weighted sum:
+ *   out[r] = sum_t w[t] * sum_k q_e[n,k] s_e[n, k/G] h[t][k],  e = ids[t], n = rows[r],
+ * qweight uint32[E][H][I/8], scales fp16 bits [E][H][I/G], h bf16 bits [topk][I],
+ * w float[topk]. Slots whose id is outside [0, E) contribute nothing. mag[r] is
+ * sum_t |w[t]| * sum_k |q s h|.
+ */
+int oracle_moe_down_combine(const uint32_t *qweight, const uint16_t *scales, const int32_t *ids,
+                            const float *w, int32_t topk, int32_t E, const uint16_t *h,
+                            int64_t H, int64_t I, int32_t G, const int64_t *rows,
+                            int64_t n_rows, double *out, double *mag)
+{
+    if (check_dense(qweight, scales, h, H, I, G, rows, n_rows, out, mag))
+        return ORACLE_BAD_ARG;
+    if (!ids || !w || topk < 1 || E < 1 || (!rows && n_rows != H))
+        return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t n = rows ? rows[r] : r;
+        double acc = 0.0, m = 0.0;
+        for (int32_t t = 0; t < topk; ++t) {
+            int32_t e = ids[t];
+            if (e < 0 || e >= E)
+                continue;
+            double y, ym;
+            int64_t row = (int64_t)e * H + n;
+            dot_row(qweight + row * (I / 8), scales + row * (I / G), h + (int64_t)t * I, I, G,
+                    &y, &ym);
+            acc += (double)w[t] * y;
+            m += fabs((double)w[t]) * ym;
+        }
+        out[r] = acc;
+        mag[r] = m;
+    }
+    return ORACLE_OK;
+}

@@ -44,6 +44,9 @@ SHAPES: Dict[str, Tuple[int, int, int]] = {
 }
 MOE_EXPERTS = 256
 MOE_TOPK = 8
+# Expert tail after the grouped gate+up product: the c4 experts (2I = 2048 gate+up rows over
+# K = 2304) followed by down experts of H = 2304 rows over I = 1024.
+TAIL = {"config_id": 41, "E": MOE_EXPERTS, "I": 1024, "H": 2304, "K": 2304, "topk": MOE_TOPK}
 BATCH_SIZES = (1, 2, 4, 8, 16)
 
 
@@ -115,6 +118,49 @@ def moe(E: int, N: int, K: int, topk: int, seed: int, config_id: int = 0) -> Moe
     x = draw_acts(rng, (K,))
     ids = rng.choice(E, size=topk, replace=False).astype(np.int32)
     return Moe(qw, sc, x, ids, E, N, K, topk)
+
+
+@dataclasses.dataclass
+class MoeTail:
+    gu_qweight: np.ndarray    # uint32 [E][2I][K/8], rows [0, I) gate, [I, 2I) up
+    gu_scales: np.ndarray     # uint16 [E][2I][K/128]
+    x: np.ndarray             # uint16 (bf16) [K]
+    ids: np.ndarray           # int32 [topk]
+    route_w: np.ndarray       # float32 [topk], positive, summing to about 1
+    down_qweight: np.ndarray  # uint32 [E][H][I/8]
+    down_scales: np.ndarray   # uint16 [E][H][I/128]
+    h: np.ndarray             # uint16 (bf16) [topk][I], an activation draw for the down step alone
+    E: int
+    I: int
+    H: int
+    K: int
+    topk: int
+
+
+def moe_tail(E: int, I: int, H: int, K: int, topk: int, seed: int,
+             config_id: int = 0) -> MoeTail:
+    """Operands of the expert tail. Draw order: gate+up words, gate+up scales, x, ids, router
+    weights (uniform in [0.05, 1), then divided by their sum in float64 and stored as float32),
+    down words, down scales, h (standard normal rounded to bf16)."""
+    if K % GROUP or I % GROUP:
+        raise ValueError("K and I must be multiples of 128")
+    rng = rng_for(config_id, seed)
+    gq = draw_words(rng, (E, 2 * I, K // 8))
+    gs = draw_scales(rng, (E, 2 * I, K // GROUP))
+    x = draw_acts(rng, (K,))
+    ids = rng.choice(E, size=topk, replace=False).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, size=topk)
+    w = (w / w.sum()).astype(np.float32)
+    dq = draw_words(rng, (E, H, I // 8))
+    ds = draw_scales(rng, (E, H, I // GROUP))
+    h = draw_acts(rng, (topk, I))
+    return MoeTail(gq, gs, x, ids, w, dq, ds, h, E, I, H, K, topk)
+
+
+def tail_config(seed: int, experts: Optional[int] = None) -> MoeTail:
+    t = TAIL
+    return moe_tail(experts or t["E"], t["I"], t["H"], t["K"], t["topk"], seed,
+                    config_id=t["config_id"])
 
 
 def config(name: str, seed: int, M: int = 1, experts: Optional[int] = None):

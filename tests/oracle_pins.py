@@ -285,8 +285,172 @@ def pin_row_subset(orc):
     assert np.array_equal(ys, y[rows]) and np.array_equal(ms, mag[rows])
 
 
+# ---------------------------------------------------------------- expert tail
+def _bf16_value(bits: int) -> float:
+    """Exact value of a bfloat16 pattern through numpy's binary32 reading (independent)."""
+    return float(np.array([bits << 16], np.uint32).view(np.float32)[0])
+
+
+def brute_bf16_round(v: float) -> int:
+    """Nearest bfloat16 pattern to v, ties to the even pattern, by exact rational comparison of
+    the two neighbouring patterns found by bisection over the ordered positive patterns."""
+    from fractions import Fraction
+    if v != v:
+        raise ValueError("nan")
+    sign = 0x8000 if np.signbit(v) else 0
+    a = abs(v)
+    if a == 0:
+        return sign
+    if a == float("inf"):
+        return sign | 0x7F80
+    lo, hi = 0, 0x7F80                     # decode(lo) <= a < decode(hi), hi = +inf
+    if a >= _bf16_value(0x7F7F):
+        lo, hi = 0x7F7F, 0x7F80
+    else:
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if _bf16_value(mid) <= a:
+                lo = mid
+            else:
+                hi = mid
+    fa, flo = Fraction(a), Fraction(_bf16_value(lo))
+    if hi == 0x7F80:   # above the largest finite value: the next step up would be 2^128
+        fhi = Fraction(2) ** 128
+    else:
+        fhi = Fraction(_bf16_value(hi))
+    d_lo, d_hi = fa - flo, fhi - fa
+    if d_lo < d_hi or (d_lo == d_hi and lo % 2 == 0):
+        return sign | lo
+    return sign | hi
+
+
+def pin_bf16_round_brute(orc):
+    """double -> bfloat16 rounding equals the exact nearest-even choice on random magnitudes
+    (subnormal to overflow), on exact midpoints, and on signed zeros and infinities."""
+    rng = np.random.default_rng(31)
+    vals = list(np.exp2(rng.uniform(-140, 129, size=600)) * rng.choice([-1.0, 1.0], 600))
+    for b in rng.integers(0, 0x7F7F, size=300):
+        mid = (_bf16_value(int(b)) + _bf16_value(int(b) + 1)) / 2   # exact in double
+        vals += [mid, -mid]
+    vals += [0.0, -0.0, float("inf"), -float("inf"), 3.3895313892515355e38, 3.4e38]
+    for v in vals:
+        want = brute_bf16_round(float(v))
+        got = orc.double_to_bf16(float(v))
+        assert got == want, f"{v!r}: got {got:#06x} want {want:#06x}"
+
+
+def pin_bf16_round_ties(orc):
+    """Worked ties: halfway values go to the even pattern, in the normal and subnormal ranges."""
+    cases = {1 + 2.0 ** -8: 0x3F80, 1 + 3 * 2.0 ** -8: 0x3F82, -(1 + 2.0 ** -8): 0xBF80,
+             2.0 ** -133: 0x0001, 2.0 ** -134: 0x0000, 3 * 2.0 ** -134: 0x0002,
+             1.5: 0x3FC0, 1 + 2.0 ** -8 + 2.0 ** -30: 0x3F81}
+    for v, want in cases.items():
+        assert orc.double_to_bf16(v) == want, (v, hex(orc.double_to_bf16(v)), hex(want))
+    assert np.isnan(_bf16_value(orc.double_to_bf16(float("nan"))))
+
+
+def pin_silu(orc):
+    """silu(g) = g * sigmoid(g): zero at zero, silu(g) - silu(-g) = g, sigmoid(ln 3) = 3/4,
+    and the limits g and 0 far from zero."""
+    import math
+    assert orc.silu(0.0) == 0.0
+    for g in (1e-3, 0.25, 1.0, 2.5, 7.0, 30.0):
+        assert abs(orc.silu(g) - orc.silu(-g) - g) <= 1e-15 * g
+    assert abs(orc.silu(math.log(3.0)) - 0.75 * math.log(3.0)) <= 4e-16
+    assert orc.silu(800.0) == 800.0 and abs(orc.silu(-800.0)) == 0.0
+    assert orc.silu(-1.0) < 0 and orc.silu(1.0) > 0.5
+
+
+def pin_swiglu_golden(orc):
+    gold = _golden("w3_swiglu_gate_up_order.json")
+    words = np.zeros((1, 4, 16), np.uint32)
+    words[0, :, 0] = gold["word0"]
+    scales = np.full((1, 4, 1), 0x3C00, np.uint16)
+    x = np.zeros(128, np.uint16)
+    x[0] = 0x3F80
+    r = orc.moe_swiglu(words, scales, np.array([0], np.int32), x, 128)
+    assert np.allclose(r["h"][0], gold["h"], rtol=1e-15, atol=0)
+    assert list(r["h_bf16"][0]) == gold["h_bf16"]
+
+
+def _tail_case(E, I, H, K, seed):
+    rng = np.random.default_rng(seed)
+    qg = rng.integers(-8, 8, size=(E, 2 * I, K))
+    wg = np.stack([pack_nibbles(qg[e]) for e in range(E)])
+    sg = rng.uniform(0.001, 0.01, size=(E, 2 * I, K // 128)).astype(np.float16).view(np.uint16)
+    qd = rng.integers(-8, 8, size=(E, H, I))
+    wd = np.stack([pack_nibbles(qd[e]) for e in range(E)])
+    sd = rng.uniform(0.001, 0.01, size=(E, H, I // 128)).astype(np.float16).view(np.uint16)
+    x = (rng.standard_normal(K).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return qg, wg, sg, qd, wd, sd, x, rng
+
+
+def pin_swiglu_brute(orc):
+    """SwiGLU of the grouped product against an independent numpy dequantise + BLAS path:
+    g from the first I rows, u from the last I; invalid ids give zeros; h_bf16 is within half a
+    bfloat16 step of h."""
+    E, I, K = 3, 6, 256
+    qg, wg, sg, _, _, _, x, _ = _tail_case(E, I, 4, K, 32)
+    ids = np.array([2, -1, 0, 2], np.int32)
+    r = orc.moe_swiglu(wg, sg, ids, x, K)
+    xv = bf16_bits_to_f64(x)
+    for t, e in enumerate(ids):
+        if not 0 <= e < E:
+            assert all(np.all(r[k][t] == 0) for k in ("h", "g", "u", "mag_g", "mag_u"))
+            assert np.all(r["h_bf16"][t] == 0)
+            continue
+        W = numpy_dense_weights(wg[e], sg[e], K)
+        y = W @ xv
+        g, u = y[:I], y[I:]
+        h = g / (1.0 + np.exp(-g)) * u
+        assert np.allclose(r["g"][t], g, rtol=1e-12, atol=1e-14)
+        assert np.allclose(r["u"][t], u, rtol=1e-12, atol=1e-14)
+        assert np.allclose(r["h"][t], h, rtol=1e-12, atol=1e-14)
+        assert np.allclose(r["mag_g"][t], np.abs(W[:I] * xv).sum(1), rtol=1e-12)
+        hb = bf16_bits_to_f64(r["h_bf16"][t])
+        assert np.all(np.abs(hb - h) <= np.abs(h) * 2.0 ** -9 + 1e-40)
+
+
+def pin_down_combine(orc):
+    """The router-weighted down projection: a one-hot weight gives the plain product of that
+    slot's expert with its own h row; doubling w doubles out exactly; permuting slots changes
+    nothing; an invalid id contributes nothing; repeated ids add; numpy brute force agrees."""
+    E, I, H = 4, 256, 5
+    _, _, _, qd, wd, sd, _, rng = _tail_case(E, I, H, 128, 33)
+    T = 4
+    h = (rng.standard_normal((T, I)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ids = np.array([3, 1, 3, 0], np.int32)
+    w = rng.uniform(0.1, 1.0, size=T).astype(np.float32)
+    out, mag = orc.moe_down_combine(wd, sd, ids, w, h)
+    for t in range(T):
+        oh = np.zeros(T, np.float32)
+        oh[t] = 1.0
+        o1, m1 = orc.moe_down_combine(wd, sd, ids, oh, h)
+        ref, rm = orc.gemv(wd[ids[t]], sd[ids[t]], h[t], I)
+        assert np.array_equal(o1, ref) and np.array_equal(m1, rm)
+    o2, _ = orc.moe_down_combine(wd, sd, ids, 2 * w, h)
+    assert np.array_equal(o2, 2 * out)
+    o3, m3 = orc.moe_down_combine(wd, sd, ids, -w, h)
+    assert np.array_equal(o3, -out) and np.array_equal(m3, mag)
+    perm = np.array([2, 0, 3, 1])
+    op, mp = orc.moe_down_combine(wd, sd, ids[perm], w[perm], h[perm])
+    assert np.allclose(op, out, rtol=1e-12, atol=1e-14) and np.allclose(mp, mag, rtol=1e-12)
+    bad = ids.copy()
+    bad[1] = E
+    ob, _ = orc.moe_down_combine(wd, sd, bad, w, h)
+    keep = [0, 2, 3]
+    ok_, _ = orc.moe_down_combine(wd, sd, ids[keep], w[keep], h[keep])
+    assert np.allclose(ob, ok_, rtol=1e-13, atol=1e-15)
+    ref = np.zeros(H)
+    for t in range(T):
+        ref += float(w[t]) * (numpy_dense_weights(wd[ids[t]], sd[ids[t]], I) @ bf16_bits_to_f64(h[t]))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-14)
+    assert np.all(mag >= np.abs(out))
+
+
 ALL_PINS = [
     pin_f16_decode, pin_bf16_decode, pin_w1, pin_w2, pin_unpack, pin_unit_probes,
     pin_zero_scale_groups, pin_linearity, pin_negation, pin_constant_rows, pin_brute_force,
-    pin_mag_nonnegative, pin_batched, pin_moe, pin_row_subset,
+    pin_mag_nonnegative, pin_batched, pin_moe, pin_row_subset, pin_bf16_round_brute,
+    pin_bf16_round_ties, pin_silu, pin_swiglu_golden, pin_swiglu_brute, pin_down_combine,
 ]

@@ -29,6 +29,21 @@ MUTANTS = {
     "moe_slot_not_id": ("((int64_t)e * N + n) * (K / 8)", "((int64_t)t * N + n) * (K / 8)"),
     "batched_ignores_ldx": ("X + m * ldx", "X + m * K"),
     "word_index": ("row[k / 8]", "row[k / 8 + (k >= 8 ? -1 : 0)]"),
+    "swiglu_halves_swapped": ("int64_t rg = (int64_t)e * 2 * I + n, ru = rg + I;",
+                              "int64_t ru = (int64_t)e * 2 * I + n, rg = ru + I;"),
+    "silu_sign": ("g / (1.0 + exp(-g))", "g / (1.0 + exp(g))"),
+    "silu_missing_gate_factor": ("h[o] = oracle_silu(g[o]) * u[o];",
+                                 "h[o] = u[o] / (1.0 + exp(-g[o]));"),
+    "bf16_truncates": ("double r = rint(ldexp(a, -qexp));", "double r = floor(ldexp(a, -qexp));"),
+    "bf16_ties_away": ("double r = rint(ldexp(a, -qexp));", "double r = round(ldexp(a, -qexp));"),
+    "bf16_subnormal_step": ("if (qexp < -133)\n        qexp = -133;",
+                            "if (qexp < -140)\n        qexp = -140;"),
+    "bf16_saturates": ("if (q >= ldexp(1.0, 128))\n        return (uint16_t)(sign | 0x7F80u);",
+                       "if (q >= ldexp(1.0, 128))\n        return (uint16_t)(sign | 0x7F7Fu);"),
+    "combine_ignores_weight": ("acc += (double)w[t] * y;", "acc += y;"),
+    "down_slot_as_expert": ("int64_t row = (int64_t)e * H + n;", "int64_t row = (int64_t)t * H + n;"),
+    "down_shared_h_row": ("h + (int64_t)t * I, I, G,", "h, I, G,"),
+    "down_signed_mag": ("m += fabs((double)w[t]) * ym;", "m += (double)w[t] * ym;"),
 }
 
 
