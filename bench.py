@@ -351,7 +351,67 @@ def per_workload(torch, np, w, synthetic, dev, cus):
     record("c4_moe_top8_of_256", m.N, m.K, 1, b, stats, warm,
            stream_ceiling_us(torch, w, dev, b, rot(b), cus),
            w.describe_plan(1, m.N, m.K, m.topk, cus))
+    del m, x, y, idsets
+    torch.cuda.empty_cache()
+    res["c4_expert_tail_top8_of_256"] = expert_tail(torch, np, w, synthetic, dev, cus)
     return res
+
+
+def tail_bytes(d):
+    """Algorithmic bytes of the expert tail: the selected gate+up and down experts (packed weights
+    and scales), x, and h read by the down step (h written as bf16 is an output)."""
+    gu = 2 * d.I * d.K // 2 + 2 * d.I * (d.K // 128) * 2
+    dn = d.H * d.I // 2 + d.H * (d.I // 128) * 2
+    return d.topk * (gu + dn) + d.K * 2 + d.topk * d.I * 2
+
+
+def expert_tail(torch, np, w, synthetic, dev, cus):
+    """The MoE expert tail for one token: SwiGLU gate+up over the selected experts, then the
+    grouped down projection with the router-weighted sum. Two copies of every expert tensor and
+    64 id sets drawn from the seeded stream, so consecutive calls read different experts."""
+    d = synthetic.tail_config(0)
+    qg = torch.from_numpy(d.gu_qweight.view(np.int32)).to(dev)
+    sg = torch.from_numpy(d.gu_scales.view(np.float16)).to(dev)
+    qd = torch.from_numpy(d.down_qweight.view(np.int32)).to(dev)
+    sd = torch.from_numpy(d.down_scales.view(np.float16)).to(dev)
+    cp = list(zip(rotated(torch, qg, 2), rotated(torch, sg, 2), rotated(torch, qd, 2),
+                  rotated(torch, sd, 2)))
+    del qg, sg, qd, sd
+    x = torch.from_numpy(d.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    rw = torch.from_numpy(d.route_w).to(dev)
+    rng = np.random.default_rng([41, 1])
+    idsets = [torch.from_numpy(rng.choice(d.E, d.topk, replace=False).astype(np.int32)).to(dev)
+              for _ in range(64)]
+    h = torch.empty((d.topk, d.I), dtype=torch.bfloat16, device=dev)
+    out = torch.empty(d.H, dtype=torch.float32, device=dev)
+
+    def fn(i):
+        c, ids = cp[i % 2], idsets[i % 64]
+        w.moe_gemv_swiglu(c[0], c[1], ids, x, out=h)
+        w.moe_down_combine(c[2], c[3], ids, rw, h, out=out)
+
+    def gate(i):
+        c, ids = cp[i % 2], idsets[i % 64]
+        w.moe_gemv_swiglu(c[0], c[1], ids, x, out=h)
+
+    def down(i):
+        c, ids = cp[i % 2], idsets[i % 64]
+        w.moe_down_combine(c[2], c[3], ids, rw, h, out=out)
+    fn(0)
+    med, p10, p90 = graph_replay_stats(torch, fn, 128, 10)
+    g_us, _, _ = graph_replay_stats(torch, gate, 128, 5)
+    d_us, _, _ = graph_replay_stats(torch, down, 128, 5)
+    b = tail_bytes(d)
+    e = {"experts": d.E, "topk": d.topk, "gate_up": [2 * d.I, d.K], "down": [d.H, d.I],
+         "plans": {"swiglu": w.describe_tail_plan(0, 0, d.K, d.I, d.topk, cus),
+                   "down_combine": w.describe_tail_plan(1, d.H, 0, d.I, d.topk, cus)},
+         "bytes": b, "us_per_call": round(med, 3), "us_p10": round(p10, 3),
+         "us_p90": round(p90, 3), "us_swiglu": round(g_us, 3), "us_down_combine": round(d_us, 3),
+         "GB_s": round(b / med / 1e3, 1),
+         "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1)}
+    del cp
+    torch.cuda.empty_cache()
+    return e
 
 
 def profile_workload(torch, np, w, synthetic, dev, name, M, steps):

@@ -99,6 +99,41 @@ w4a16_status_t w4a16_moe_gemv(const uint32_t *qweight, const uint16_t *scales,
                               int32_t group_size, hipStream_t stream);
 
 /*
+ * Expert tail, step 1: the grouped gate+up product of one token with the SwiGLU epilogue. The
+ * local-kimi README, technical-detail section, lists a SwiGLU variant of the grouped W4A16 kernel
+ * beside the plain one; the split of an expert's rows and the rounding of h are this library's
+ * reading (the pages give neither):
+ *   qweight uint32[E][2I][K/8], scales fp16 bits [E][2I][K/128]: rows [0, I) of an expert are
+ *     the gate projection, rows [I, 2I) the up projection;
+ *   expert_ids int32[topk] in DEVICE memory; x bf16 bits [K];
+ *   h bf16 bits [topk][I] (output): h[t][n] = bf16(silu(g) * u) with g = W_e[n] x,
+ *     u = W_e[I + n] x, e = expert_ids[t], silu(g) = g / (1 + e^-g), evaluated in fp32 and
+ *     rounded to nearest-even bfloat16. An id outside [0, E) gives a row of +0.0.
+ *   1 <= I, 2I <= 2^31 - 1; K as for w4a16_gemv; 1 <= topk <= 1024; h 2-byte aligned.
+ */
+w4a16_status_t w4a16_moe_gemv_swiglu(const uint32_t *qweight, const uint16_t *scales,
+                                     const int32_t *expert_ids, int32_t topk, int32_t num_experts,
+                                     const uint16_t *x, uint16_t *h, int64_t I, int64_t K,
+                                     int32_t group_size, hipStream_t stream);
+
+/*
+ * Expert tail, step 2: the grouped down projection of every slot's own activation row, summed
+ * with the router's weights (the combine that follows the grouped expert kernels in an MoE
+ * decode step):
+ *   out[n] = sum_t route_weights[t] * sum_k q_e[n,k] * s_e[n, k/128] * h[t][k],  e = expert_ids[t]
+ *   qweight uint32[E][H][I/8], scales fp16 bits [E][H][I/128]; expert_ids int32[topk] and
+ *   route_weights float[topk] in DEVICE memory; h bf16 bits [topk][I], contiguous, 16-byte
+ *   aligned (the output of w4a16_moe_gemv_swiglu); out float[H], fully overwritten.
+ *   A slot whose id is outside [0, E) contributes nothing (expert 0's bytes may be read for it).
+ *   1 <= H <= 2^31 - 1; 128 <= I, I % 128 == 0; topk * I <= 65536; 1 <= topk <= 1024.
+ */
+w4a16_status_t w4a16_moe_down_combine(const uint32_t *qweight, const uint16_t *scales,
+                                      const int32_t *expert_ids, const float *route_weights,
+                                      int32_t topk, int32_t num_experts, const uint16_t *h,
+                                      float *out, int64_t H, int64_t I, int32_t group_size,
+                                      hipStream_t stream);
+
+/*
  * Test support: q_out int8[N][K] receives the signed value of every packed nibble, so the
  * unpacking can be checked bit for bit. 1 <= N, 8 <= K, K % 8 == 0; qweight 4-byte aligned
  * (one word per thread); otherwise W4A16_ERR_MISALIGNED.
@@ -124,6 +159,14 @@ w4a16_status_t w4a16_stream_read(const void *buf, int64_t bytes, uint32_t *out, 
  */
 w4a16_status_t w4a16_describe_plan(int32_t M, int64_t N, int64_t K, int32_t topk, int32_t cus,
                                    char *buf, int64_t len);
+
+/*
+ * Host-only introspection of the expert-tail launch: step 0 = w4a16_moe_gemv_swiglu for (I, K,
+ * topk), step 1 = w4a16_moe_down_combine for (rows = H, I, topk). Same conventions as
+ * w4a16_describe_plan.
+ */
+w4a16_status_t w4a16_describe_tail_plan(int32_t step, int64_t rows, int64_t K, int64_t I,
+                                        int32_t topk, int32_t cus, char *buf, int64_t len);
 
 /* Static, never-NULL description of a status code. */
 const char *w4a16_status_string(w4a16_status_t status);

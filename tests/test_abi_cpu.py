@@ -25,7 +25,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("w4a16_gemv", "w4a16_gemv_batched", "w4a16_moe_gemv", "w4a16_unpack_debug",
               "w4a16_describe_plan", "w4a16_status_string", "w4a16_abi_version",
-              "w4a16_stream_read"):
+              "w4a16_stream_read", "w4a16_moe_gemv_swiglu", "w4a16_moe_down_combine",
+              "w4a16_describe_tail_plan"):
         assert n in names
 
 
@@ -93,6 +94,46 @@ def test_moe_validation(kw, status):
     assert moe(**kw) == status
 
 
+def swiglu(qw=A, sc=A, ids=A, topk=8, E=16, x=A, h=A, I=1024, K=2304, G=128):
+    return w.library().w4a16_moe_gemv_swiglu(qw, sc, ids, topk, E, x, h, I, K, G, None)
+
+
+def down(qw=A, sc=A, ids=A, rw=A, topk=8, E=16, h=A, out=A, H=2304, I=1024, G=128):
+    return w.library().w4a16_moe_down_combine(qw, sc, ids, rw, topk, E, h, out, H, I, G, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qw=None), NULLP), (dict(sc=None), NULLP), (dict(ids=None), NULLP), (dict(x=None), NULLP),
+    (dict(h=None), NULLP), (dict(G=64), GROUP), (dict(I=0), SHAPE), (dict(I=1 << 30), SHAPE),
+    (dict(K=200), SHAPE), (dict(K=65536 + 128), SHAPE), (dict(topk=0), SHAPE),
+    (dict(topk=1025), SHAPE), (dict(E=0), SHAPE), (dict(qw=A + 4), ALIGN), (dict(x=A + 2), ALIGN),
+    (dict(h=A + 1), ALIGN), (dict(ids=A + 2), ALIGN),
+])
+def test_swiglu_validation(kw, status):
+    assert swiglu(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qw=None), NULLP), (dict(rw=None), NULLP), (dict(h=None), NULLP), (dict(out=None), NULLP),
+    (dict(G=256), GROUP), (dict(H=0), SHAPE), (dict(I=64), SHAPE), (dict(I=1000), SHAPE),
+    (dict(topk=0), SHAPE), (dict(topk=65, I=1024), SHAPE), (dict(E=0), SHAPE),
+    (dict(h=A + 8), ALIGN), (dict(out=A + 2), ALIGN), (dict(rw=A + 1), ALIGN),
+])
+def test_down_combine_validation(kw, status):
+    assert down(**kw) == status
+
+
+@pytest.mark.parametrize("step,rows,K,I,topk,want", [
+    (0, 0, 2304, 1024, 8, "valu_moe_swiglu tokens=1 lanes_per_row=8 chunks_per_item=3"),
+    (0, 0, 2048, 1408, 8, "valu_moe_swiglu tokens=1 lanes_per_row=32 chunks_per_item=1"),
+    (1, 2304, 0, 1024, 8, "valu_moe_combine tokens=1 lanes_per_row=32 chunks_per_item=1"),
+    (1, 7168, 0, 1408, 8, "valu_moe_combine tokens=1 lanes_per_row=4 chunks_per_item=1"),
+    (1, 5, 0, 128, 1, "valu_moe_combine tokens=1 lanes_per_row=4"),
+])
+def test_tail_dispatch(step, rows, K, I, topk, want):
+    assert w.describe_tail_plan(step, rows, K, I, topk).startswith(want)
+
+
 def test_unpack_validation():
     lib = w.library()
     assert lib.w4a16_unpack_debug(None, A, 4, 64, None) == NULLP
@@ -123,6 +164,8 @@ def test_valid_arguments_reach_the_device_check_only():
     assert batched() == DEVICE
     assert moe() == DEVICE
     assert w.library().w4a16_stream_read(A, 64, A, 1, 4, None) == DEVICE
+    assert swiglu() == DEVICE
+    assert down() == DEVICE
 
 
 @pytest.mark.parametrize("M,N,K,topk,kind", [

@@ -22,8 +22,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["gemv", "gemv_batched", "moe_gemv", "unpack_debug", "describe_plan", "stream_read",
-           "W4A16Error",
+__all__ = ["gemv", "gemv_batched", "moe_gemv", "moe_gemv_swiglu", "moe_down_combine",
+           "unpack_debug", "describe_plan", "describe_tail_plan", "stream_read", "W4A16Error",
            "library", "LIB_PATH", "GROUP_SIZE", "MAX_BATCH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")
@@ -55,12 +55,16 @@ def library() -> ctypes.CDLL:
     lib.w4a16_unpack_debug.argtypes = [P, P, i64, i64, P]
     lib.w4a16_describe_plan.argtypes = [i32, i64, i64, i32, i32, ctypes.c_char_p, i64]
     lib.w4a16_stream_read.argtypes = [P, i64, P, i32, i32, P]
+    lib.w4a16_moe_gemv_swiglu.argtypes = [P, P, P, i32, i32, P, P, i64, i64, i32, P]
+    lib.w4a16_moe_down_combine.argtypes = [P, P, P, P, i32, i32, P, P, i64, i64, i32, P]
+    lib.w4a16_describe_tail_plan.argtypes = [i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i64]
     lib.w4a16_status_string.argtypes = [ctypes.c_int]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_abi_version.argtypes = []
     for f in (lib.w4a16_gemv, lib.w4a16_gemv_batched, lib.w4a16_moe_gemv,
               lib.w4a16_unpack_debug, lib.w4a16_describe_plan, lib.w4a16_stream_read,
-              lib.w4a16_abi_version):
+              lib.w4a16_moe_gemv_swiglu, lib.w4a16_moe_down_combine,
+              lib.w4a16_describe_tail_plan, lib.w4a16_abi_version):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -162,6 +166,64 @@ def moe_gemv(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tens
     return out
 
 
+def moe_gemv_swiglu(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tensor,
+                    x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """h[t] = bf16(silu(W_e[:I] x) * (W_e[I:] x)), e = expert_ids[t], for gate+up experts
+    qweight [E, 2I, K/8]. Returns h as torch.bfloat16 [topk, I]."""
+    _need(qweight, torch.int32, "qweight", 3)
+    _need(scales, torch.float16, "scales", 3)
+    _need(expert_ids, torch.int32, "expert_ids", 1)
+    _need(x, torch.bfloat16, "x", 1)
+    E, N2, K = qweight.shape[0], qweight.shape[1], qweight.shape[2] * 8
+    if N2 % 2:
+        raise ValueError("gate+up experts need an even number of rows")
+    I, topk = N2 // 2, expert_ids.numel()
+    if not all(t.is_contiguous() for t in (qweight, scales, expert_ids, x)):
+        raise ValueError("qweight, scales, expert_ids and x must be contiguous")
+    if tuple(scales.shape) != (E, N2, K // GROUP_SIZE) or x.numel() != K:
+        raise ValueError("shape mismatch between qweight, scales and x")
+    if out is None:
+        out = torch.empty((topk, I), dtype=torch.bfloat16, device=qweight.device)
+    _need(out, torch.bfloat16, "out", 2)
+    if tuple(out.shape) != (topk, I) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [topk, I] tensor")
+    _ok(library().w4a16_moe_gemv_swiglu(qweight.data_ptr(), scales.data_ptr(),
+                                        expert_ids.data_ptr(), topk, E, x.data_ptr(),
+                                        out.data_ptr(), I, K, GROUP_SIZE, _stream(stream)),
+        "w4a16_moe_gemv_swiglu")
+    return out
+
+
+def moe_down_combine(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tensor,
+                     route_weights: torch.Tensor, h: torch.Tensor,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out = sum_t route_weights[t] * W_{expert_ids[t]} h[t] for down experts qweight [E, H, I/8]
+    and h bfloat16 [topk, I]. Returns float32 [H]."""
+    _need(qweight, torch.int32, "qweight", 3)
+    _need(scales, torch.float16, "scales", 3)
+    _need(expert_ids, torch.int32, "expert_ids", 1)
+    _need(route_weights, torch.float32, "route_weights", 1)
+    _need(h, torch.bfloat16, "h", 2)
+    E, H, I = qweight.shape[0], qweight.shape[1], qweight.shape[2] * 8
+    topk = expert_ids.numel()
+    if not all(t.is_contiguous() for t in (qweight, scales, expert_ids, route_weights, h)):
+        raise ValueError("all operands must be contiguous")
+    if (tuple(scales.shape) != (E, H, I // GROUP_SIZE) or tuple(h.shape) != (topk, I)
+            or route_weights.numel() != topk):
+        raise ValueError("shape mismatch between qweight, scales, h, ids and weights")
+    if out is None:
+        out = torch.empty(H, dtype=torch.float32, device=qweight.device)
+    _need(out, torch.float32, "out", 1)
+    if out.numel() != H or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [H] tensor")
+    _ok(library().w4a16_moe_down_combine(qweight.data_ptr(), scales.data_ptr(),
+                                         expert_ids.data_ptr(), route_weights.data_ptr(), topk,
+                                         E, h.data_ptr(), out.data_ptr(), H, I, GROUP_SIZE,
+                                         _stream(stream)), "w4a16_moe_down_combine")
+    return out
+
+
 def unpack_debug(qweight: torch.Tensor, stream=None) -> torch.Tensor:
     """int8 [N, K]: the signed value of every packed nibble, decoded by the GEMV unpack."""
     _need(qweight, torch.int32, "qweight", 2)
@@ -172,6 +234,15 @@ def unpack_debug(qweight: torch.Tensor, stream=None) -> torch.Tensor:
     _ok(library().w4a16_unpack_debug(qweight.data_ptr(), out.data_ptr(), N, K, _stream(stream)),
         "w4a16_unpack_debug")
     return out
+
+
+def describe_tail_plan(step: int, rows: int, K: int, I: int, topk: int, cus: int = 256) -> str:
+    """Launch shape of the expert-tail steps: 0 = SwiGLU gate+up (I, K), 1 = down + combine
+    (rows = H, I). Host-only."""
+    buf = ctypes.create_string_buffer(256)
+    _ok(library().w4a16_describe_tail_plan(step, rows, K, I, topk, cus, buf, len(buf)),
+        "w4a16_describe_tail_plan")
+    return buf.value.decode()
 
 
 def describe_plan(M: int, N: int, K: int, topk: int = 0, cus: int = 256) -> str:

@@ -136,6 +136,61 @@ w4a16_status_t w4a16_moe_gemv(const uint32_t *qweight, const uint16_t *scales,
     return run(a, 1, topk, stream);
 }
 
+w4a16_status_t w4a16_moe_gemv_swiglu(const uint32_t *qweight, const uint16_t *scales,
+                                     const int32_t *expert_ids, int32_t topk, int32_t num_experts,
+                                     const uint16_t *x, uint16_t *h, int64_t I, int64_t K,
+                                     int32_t group_size, hipStream_t stream)
+{
+    if (!qweight || !scales || !expert_ids || !x || !h)
+        return W4A16_ERR_NULL_POINTER;
+    if (group_size != W4A16_GROUP_SIZE)
+        return W4A16_ERR_BAD_GROUP;
+    if (I < 1 || 2 * I > kMaxN || K < W4A16_GROUP_SIZE || K % W4A16_GROUP_SIZE != 0 ||
+        K > kMaxKDense || topk < 1 || topk > kMaxTopk || num_experts < 1)
+        return W4A16_ERR_BAD_SHAPE;
+    if (!aligned(qweight, 16) || !aligned(x, 16) || !aligned(scales, 2) || !aligned(h, 2) ||
+        !aligned(expert_ids, 4))
+        return W4A16_ERR_MISALIGNED;
+    const DeviceInfo *dev = current_device();
+    if (!dev)
+        return W4A16_ERR_UNSUPPORTED_DEVICE;
+    Plan plan;
+    if (!make_tail_plan(PLAN_MODE_SWIGLU, 2 * I, K, K, topk, dev->cus, dev->lds_limit, &plan))
+        return W4A16_ERR_BAD_SHAPE;
+    GemvArgs a{qweight, scales, x, K, reinterpret_cast<float *>(h), I, expert_ids, topk,
+               num_experts, 2 * I, (int32_t)K, 1, nullptr, (int32_t)K};
+    return launch(a, plan, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+w4a16_status_t w4a16_moe_down_combine(const uint32_t *qweight, const uint16_t *scales,
+                                      const int32_t *expert_ids, const float *route_weights,
+                                      int32_t topk, int32_t num_experts, const uint16_t *h,
+                                      float *out, int64_t H, int64_t I, int32_t group_size,
+                                      hipStream_t stream)
+{
+    if (!qweight || !scales || !expert_ids || !route_weights || !h || !out)
+        return W4A16_ERR_NULL_POINTER;
+    if (group_size != W4A16_GROUP_SIZE)
+        return W4A16_ERR_BAD_GROUP;
+    if (H < 1 || H > kMaxN || I < W4A16_GROUP_SIZE || I % W4A16_GROUP_SIZE != 0 ||
+        I > kMaxKDense || topk < 1 || topk > kMaxTopk || num_experts < 1 ||
+        (int64_t)topk * I > kMaxKDense)
+        return W4A16_ERR_BAD_SHAPE;
+    if (!aligned(qweight, 16) || !aligned(h, 16) || !aligned(scales, 2) || !aligned(out, 4) ||
+        !aligned(expert_ids, 4) || !aligned(route_weights, 4))
+        return W4A16_ERR_MISALIGNED;
+    const DeviceInfo *dev = current_device();
+    if (!dev)
+        return W4A16_ERR_UNSUPPORTED_DEVICE;
+    Plan plan;
+    const int64_t K = (int64_t)topk * I;
+    if (!make_tail_plan(PLAN_MODE_COMBINE, H, K, I, topk, dev->cus, dev->lds_limit, &plan))
+        return W4A16_ERR_BAD_SHAPE;
+    GemvArgs a{qweight, scales, h, K, out, H, expert_ids, topk, num_experts, H, (int32_t)K, 1,
+               route_weights, (int32_t)I};
+    return launch(a, plan, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
 w4a16_status_t w4a16_unpack_debug(const uint32_t *qweight, int8_t *q_out, int64_t N, int64_t K,
                                   hipStream_t stream)
 {
@@ -179,6 +234,24 @@ w4a16_status_t w4a16_describe_plan(int32_t M, int64_t N, int64_t K, int32_t topk
     Plan plan;
     // 160 KiB of LDS per work-group, as on gfx950.
     if (cus < 1 || !make_plan(M, N, K, topk, cus, 160 * 1024, &plan))
+        return W4A16_ERR_BAD_SHAPE;
+    describe_plan(plan, buf, (size_t)len);
+    return W4A16_OK;
+}
+
+w4a16_status_t w4a16_describe_tail_plan(int32_t step, int64_t rows, int64_t K, int64_t I,
+                                        int32_t topk, int32_t cus, char *buf, int64_t len)
+{
+    if (!buf || len < 1)
+        return W4A16_ERR_NULL_POINTER;
+    buf[0] = '\0';
+    Plan plan;
+    const bool ok =
+        step == 0   ? make_tail_plan(PLAN_MODE_SWIGLU, 2 * I, K, K, topk, cus, 160 * 1024, &plan)
+        : step == 1 ? make_tail_plan(PLAN_MODE_COMBINE, rows, (int64_t)topk * I, I, topk, cus,
+                                     160 * 1024, &plan)
+                    : false;
+    if (cus < 1 || !ok)
         return W4A16_ERR_BAD_SHAPE;
     describe_plan(plan, buf, (size_t)len);
     return W4A16_OK;

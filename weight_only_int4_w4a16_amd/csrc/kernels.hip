@@ -245,28 +245,63 @@ __device__ __forceinline__ int fold_rows(float (&v)[U], int lane)
 // no other expert is touched), and waves without work re-read a valid item; results of all these
 // are discarded or written as zero. Straight-line loads let the compiler wait for each load on
 // its own, so early rows are multiplied while later ones are in flight.
+//
+// Modes (one token unless dense):
+//   VALU_DENSE    rows of one matrix.
+//   VALU_MOE      rows t*N + n of the experts ids[t] (grouped-expert form).
+//   VALU_SWIGLU   the grouped form over gate+up experts of 2I rows: a wave's R rows are HALF = R/2
+//                 gate rows n0.. and the matching up rows I+n0.., so after the row sums each gate
+//                 lane meets its up partner 32 lanes away and writes h = bf16(silu(g) * u).
+//   VALU_COMBINE  the grouped down projection with the router-weighted sum: the activation is
+//                 the concatenation of the topk rows h[t] (K = topk*I), and chunk batch b of a row
+//                 reads slot t = b*L*V / (I/32) from expert ids[t]'s row, its scales multiplied by
+//                 w[t], so the row sum is sum_t w[t] * W_{ids[t]}[n] h[t]. A batch never straddles
+//                 two slots ((I/32) % (L*V) == 0). An invalid id reads expert 0 with weight 0.
 // ------------------------------------------------------------------------------------------
+enum ValuMode { VALU_DENSE = 0, VALU_MOE = 1, VALU_SWIGLU = 2, VALU_COMBINE = 3 };
+
+// bf16 bit pattern nearest to f (ties to even); NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f)
+{
+    uint32_t b = __builtin_bit_cast(uint32_t, f);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((b >> 16) | 0x40u);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return (uint16_t)(b >> 16);
+}
+
 template <int L, int V, int U>
 struct ValuBuf {
     uint4 w[V][U];
     uint16_t s[V][U];
 };
 
-template <int MT, int L, int V, int U, bool MOE>
+template <int MT, int L, int V, int U, int MODE>
 __global__ void __launch_bounds__(256)
 gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                  const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
-                 const int32_t *__restrict__ ids, int32_t topk, int32_t E, int64_t N, int32_t K)
+                 const int32_t *__restrict__ ids, int32_t topk, int32_t E, int64_t N, int32_t K,
+                 const float *__restrict__ rw, int32_t KR)
 {
+    constexpr bool MOE = MODE == VALU_MOE || MODE == VALU_SWIGLU;   // rows through expert ids
+    constexpr bool TAIL = MODE == VALU_SWIGLU || MODE == VALU_COMBINE;
+    static_assert(!TAIL || (MT == 1 && U == 1), "expert-tail modes are single-token, U = 1");
+    static_assert(MODE != VALU_SWIGLU || L <= 32, "SwiGLU pairs need two row halves per wave");
     constexpr int R = 64 / L;
     constexpr int ROWS = U * R;
+    constexpr int HALF = R / 2;   // SwiGLU: gate rows per wave step
     extern __shared__ uint4 smem[];
-    const int KW = K >> 3;    // words per row
-    const int CPR = K >> 5;   // 16-byte chunks per row
-    const int GPR = K >> 7;   // scale groups per row
+    const int KW = K >> 3;    // activation words
+    const int CPR = K >> 5;   // activation chunks (16 bytes); chunks per weight row except combine
+    const int CPRW = (MODE == VALU_COMBINE ? KR : K) >> 5;   // 16-byte chunks per weight row
+    const int GPRW = (MODE == VALU_COMBINE ? KR : K) >> 7;   // scale groups per weight row
+    const int GPR = GPRW;
     uint4 *xs = smem;                                            // [MT][4][CPR]
     float *bs = reinterpret_cast<float *>(smem + MT * KW);      // [MT][CPR]
-    int32_t *ids_s = reinterpret_cast<int32_t *>(bs + MT * CPR);  // [topk] (grouped form)
+    int32_t *ids_s = reinterpret_cast<int32_t *>(bs + MT * CPR);  // [topk] (expert forms)
+    float *rw_s = reinterpret_cast<float *>(ids_s + topk);        // [topk] (combine)
+    const int64_t I = N >> 1;                                     // SwiGLU: outputs per slot
+    const int64_t bps = MODE == VALU_SWIGLU ? (I + HALF - 1) / HALF : 1;   // SwiGLU blocks per slot
 
     const int lane = threadIdx.x & 63;
     const int pr = lane & (L - 1);
@@ -275,8 +310,9 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     // The wave index is the same in every lane; saying so lets row bases live in scalar registers.
     const int64_t gw = (int64_t)blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t GW = (int64_t)gridDim.x * wpb;
-    const int64_t rows_total = MOE ? (int64_t)topk * N : N;
-    const int64_t n_super = (rows_total + ROWS - 1) / ROWS;
+    const int64_t rows_total = MODE == VALU_MOE ? (int64_t)topk * N : N;
+    const int64_t n_super =
+        MODE == VALU_SWIGLU ? (int64_t)topk * bps : (rows_total + ROWS - 1) / ROWS;
     const int nb = CPR / (L * V);
     const bool active = gw < n_super;
     const int64_t gw_c = active ? gw : n_super - 1;
@@ -294,8 +330,8 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         if (!full && r > rows_total - 1)
             r = (int)rows_total - 1;
         lrow[u] = r;
-        woff[u] = (uint32_t)((r * CPR + pr) * 16);
-        soff[u] = (uint32_t)((r * GPR + (pr >> 2)) * 2);
+        woff[u] = (uint32_t)((r * CPRW + pr) * 16);
+        soff[u] = (uint32_t)((r * GPRW + (pr >> 2)) * 2);
     }
     auto st_row0 = [&](int64_t st) -> int64_t {
         if (!full)
@@ -307,7 +343,26 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         const uint4 *w[U];
         const uint16_t *s[U];
     };
+    // SwiGLU: slot, output index of this lane's row pair, and whether the lane holds the up row.
+    auto swiglu_row = [&](int64_t st, int64_t &slot, int64_t &p) {
+        slot = st / bps;
+        const int64_t b = st - slot * bps;
+        int64_t p0 = b * HALF;
+        p0 = p0 + HALF <= I ? p0 : (I >= HALF ? I - HALF : 0);
+        p = p0 + (rr & (HALF - 1));
+        p = p < I ? p : I - 1;
+    };
     auto rows_of = [&](int64_t st, Rows &r) {
+        if constexpr (MODE == VALU_SWIGLU) {
+            int64_t slot, p;
+            swiglu_row(st, slot, p);
+            const int32_t e = ids_s[slot];
+            const bool ok = e >= 0 && e < E;
+            const int64_t row = (int64_t)(ok ? e : 0) * N + (rr >= HALF ? I : 0) + p;
+            r.w[0] = pick(ok, qw + row * CPR, reinterpret_cast<const uint4 *>(X));
+            r.s[0] = pick(ok, sc + row * GPR, X);
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int64_t vrow = st * ROWS + u * R + rr;
@@ -343,8 +398,19 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             }
         } else {
             const int64_t r0 = st_row0(ld_st);
-            const char *wb = reinterpret_cast<const char *>(qw + r0 * CPR + L * V * ld_b);
-            const char *sb = reinterpret_cast<const char *>(sc + r0 * GPR + (L / 4) * V * ld_b);
+            const uint4 *wq = qw;
+            const uint16_t *sq = sc;
+            int cb = L * V * ld_b;   // first chunk of the batch within its weight row
+            if constexpr (MODE == VALU_COMBINE) {
+                const int slot = cb / CPRW;
+                const int32_t e = ids_s[slot];
+                const int64_t ee = (e >= 0 && e < E) ? e : 0;
+                wq += ee * N * CPRW;
+                sq += ee * N * GPRW;
+                cb -= slot * CPRW;
+            }
+            const char *wb = reinterpret_cast<const char *>(wq + r0 * CPRW + cb);
+            const char *sb = reinterpret_cast<const char *>(sq + r0 * GPRW + (cb >> 2));
 #pragma unroll
             for (int v = 0; v < V; ++v)
 #pragma unroll
@@ -361,7 +427,7 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     };
 
     ValuBuf<L, V, U> bufA, bufB;
-    if (!MOE)
+    if (MODE == VALU_DENSE)
         load(bufA);     // overlaps the first weights with the activation fetch below
 
     // ---- stage activations: re-pair, transpose to [j][c], and form per-chunk offsets
@@ -382,13 +448,16 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 bs[t * CPR + (w >> 2)] = -kOffset * sum;
         }
     }
-    if (MOE)
-        for (int i = threadIdx.x; i < topk; i += blockDim.x)
+    if (MODE != VALU_DENSE)
+        for (int i = threadIdx.x; i < topk; i += blockDim.x) {
             ids_s[i] = ids[i];
+            if (MODE == VALU_COMBINE)
+                rw_s[i] = (ids[i] >= 0 && ids[i] < E) ? rw[i] : 0.0f;
+        }
     __syncthreads();
     if (!active)
         return;
-    if (MOE)
+    if (MODE != VALU_DENSE)
         load(bufA);
 
     float acc[U][MT];
@@ -399,6 +468,22 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             acc[u][t] = 0.0f;
 
     auto finish = [&](int64_t st) {
+        if constexpr (MODE == VALU_SWIGLU) {
+            float v[1] = {acc[0][0]};
+            fold_rows<L, 1>(v, pr);
+            const float up = __shfl_xor(v[0], 32, 64);   // the up row sits 32 lanes above its gate row
+            if (pr == 0 && rr < HALF) {
+                int64_t slot, p;
+                swiglu_row(st, slot, p);
+                const int32_t e = ids_s[slot];
+                const float g = v[0];
+                const float h = g / (1.0f + expf(-g)) * up;
+                reinterpret_cast<uint16_t *>(Y)[slot * ldy + p] =
+                    (e >= 0 && e < E) ? float_to_bf16_rne(h) : (uint16_t)0;
+            }
+            acc[0][0] = 0.0f;
+            return;
+        }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             float v[U];
@@ -407,10 +492,11 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 v[u] = acc[u][t];
             const int u = fold_rows<L, U>(v, pr);
             if ((pr & (L / U - 1)) == 0) {
-                const int64_t vrow = MOE ? st * ROWS + u * R + rr : st_row0(st) + lrow[u];
+                const int64_t vrow =
+                    MODE == VALU_MOE ? st * ROWS + u * R + rr : st_row0(st) + lrow[u];
                 if (vrow < rows_total) {
                     bool zero = false;
-                    if (MOE) {
+                    if (MODE == VALU_MOE) {
                         const int32_t e = ids_s[vrow / N];
                         zero = e < 0 || e >= E;
                     }
@@ -442,7 +528,9 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const float s = half_bits_to_float(buf.s[v][u]);
+                float s = half_bits_to_float(buf.s[v][u]);
+                if constexpr (MODE == VALU_COMBINE)
+                    s *= rw_s[(L * V * cp_b) / CPRW];
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
                     acc[u][t] = fmaf(s, chunk_dot(buf.w[v][u], xq[t], off[t]), acc[u][t]);
@@ -979,13 +1067,14 @@ unpack_kernel(const uint32_t *__restrict__ qw, int8_t *__restrict__ out, int64_t
 // ------------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------------
-template <int MT, int L, int V, int U, bool MOE>
+template <int MT, int L, int V, int U, int MODE>
 static hipError_t launch_valu_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
-    auto kern = gemv_valu_kernel<MT, L, V, U, MOE>;
+    auto kern = gemv_valu_kernel<MT, L, V, U, MODE>;
     void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X,  (void *)&a.ldx,
                     (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.ids, (void *)&a.topk,
-                    (void *)&a.E,       (void *)&a.N,      (void *)&a.K};
+                    (void *)&a.E,       (void *)&a.N,      (void *)&a.K,   (void *)&a.route_w,
+                    (void *)&a.KR};
     return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(p.threads),
                            args, (size_t)p.lds_bytes, stream);
 }
@@ -1014,9 +1103,18 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
 }
 
 #define W4A16_VALU_CASE(MT_, L_, V_, U_)                                                     \
-    if (p.MT == MT_ && p.L == L_ && p.V == V_ && p.U == U_)                                  \
-        return p.moe ? launch_valu_t<MT_, L_, V_, U_, (MT_ == 1)>(a, p, stream)              \
-                     : launch_valu_t<MT_, L_, V_, U_, false>(a, p, stream);
+    if (p.MT == MT_ && p.L == L_ && p.V == V_ && p.U == U_ && p.mode == PLAN_MODE_DENSE)       \
+        return launch_valu_t<MT_, L_, V_, U_, VALU_DENSE>(a, p, stream);                      \
+    if (MT_ == 1 && p.MT == MT_ && p.L == L_ && p.V == V_ && p.U == U_ &&                    \
+        p.mode == PLAN_MODE_MOE)                                                              \
+        return launch_valu_t<(MT_ == 1 ? 1 : 1), L_, V_, U_, VALU_MOE>(a, p, stream);
+
+#define W4A16_TAIL_CASE(L_, V_)                                                              \
+    if (p.MT == 1 && p.L == L_ && p.V == V_ && p.U == 1 && p.mode == PLAN_MODE_COMBINE)       \
+        return launch_valu_t<1, L_, V_, 1, VALU_COMBINE>(a, p, stream);                       \
+    if (L_ <= 32 && p.MT == 1 && p.L == L_ && p.V == V_ && p.U == 1 &&                        \
+        p.mode == PLAN_MODE_SWIGLU)                                                           \
+        return launch_valu_t<1, (L_ <= 32 ? L_ : 32), V_, 1, VALU_SWIGLU>(a, p, stream);
 
 #define W4A16_SPLITK_CASE(MT_, L_, CL_, U_)                                                  \
     if (p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_ && !p.moe)                       \
@@ -1030,6 +1128,7 @@ hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
     if (p.kind == PLAN_VALU) {
         W4A16_VALU_CONFIGS(W4A16_VALU_CASE)
+        W4A16_TAIL_CONFIGS(W4A16_TAIL_CASE)
     } else if (p.kind == PLAN_SPLITK) {
         W4A16_SPLITK_CONFIGS(W4A16_SPLITK_CASE)
     } else if (p.kind == PLAN_MFMA) {

@@ -19,7 +19,12 @@ int64_t valu_max_k(int MT, int64_t lds_limit)
 bool plan_instantiated(const Plan &p)
 {
 #define W4A16_VALU_MATCH(MT_, L_, V_, U_)                                                     \
-    if (p.kind == PLAN_VALU && p.MT == MT_ && p.L == L_ && p.V == V_ && p.U == U_)             \
+    if (p.kind == PLAN_VALU && p.MT == MT_ && p.L == L_ && p.V == V_ && p.U == U_ &&           \
+        (p.mode == PLAN_MODE_DENSE || (p.mode == PLAN_MODE_MOE && MT_ == 1)))                  \
+        return true;
+#define W4A16_TAIL_MATCH(L_, V_)                                                              \
+    if (p.kind == PLAN_VALU && p.MT == 1 && p.L == L_ && p.V == V_ && p.U == 1 &&              \
+        (p.mode == PLAN_MODE_COMBINE || (p.mode == PLAN_MODE_SWIGLU && L_ <= 32)))             \
         return true;
 #define W4A16_SPLITK_MATCH(MT_, L_, CL_, U_)                                                  \
     if (p.kind == PLAN_SPLITK && p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_)          \
@@ -29,10 +34,12 @@ bool plan_instantiated(const Plan &p)
         p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))                             \
         return true;
     W4A16_VALU_CONFIGS(W4A16_VALU_MATCH)
+    W4A16_TAIL_CONFIGS(W4A16_TAIL_MATCH)
     W4A16_MFMA_CONFIGS(W4A16_MFMA_MATCH)
     W4A16_SPLITK_CONFIGS(W4A16_SPLITK_MATCH)
 #undef W4A16_SPLITK_MATCH
 #undef W4A16_VALU_MATCH
+#undef W4A16_TAIL_MATCH
 #undef W4A16_MFMA_MATCH
     return false;
 }
@@ -55,16 +62,29 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
     if (p->kind == PLAN_VALU) {
         if (p->MT != M || cpr % ((int64_t)p->L * p->V) != 0)
             return false;
+        // The combine form reads batches of L*V chunks that must not straddle two slots.
+        if (p->mode == PLAN_MODE_COMBINE &&
+            (p->kr < 128 || p->kr % 128 != 0 || (p->kr / 32) % ((int64_t)p->L * p->V) != 0 ||
+             K != (int64_t)topk * p->kr))
+            return false;
+        if (p->mode == PLAN_MODE_SWIGLU && (N % 2 != 0 || N < 2))
+            return false;
         if (p->threads == 0)
             p->threads = 256;
         if (p->threads % 64 || p->threads < 64 || p->threads > 256)
             return false;
-        p->lds_bytes = (int64_t)p->MT * (K * 2 + cpr * 4) + (p->moe ? 4LL * topk : 0);
+        p->lds_bytes = (int64_t)p->MT * (K * 2 + cpr * 4) +
+                       (p->mode == PLAN_MODE_DENSE ? 0 : 4LL * topk) +
+                       (p->mode == PLAN_MODE_COMBINE ? 4LL * topk : 0);
         if (p->lds_bytes > lds_limit)
             return false;
-        const int64_t rows = p->moe ? (int64_t)topk * N : N;
+        const int64_t rows = p->mode == PLAN_MODE_MOE ? (int64_t)topk * N : N;
         const int64_t rows_per_wave_step = (int64_t)p->U * (64 / p->L);
-        const int64_t n_super = (rows + rows_per_wave_step - 1) / rows_per_wave_step;
+        int64_t n_super = (rows + rows_per_wave_step - 1) / rows_per_wave_step;
+        if (p->mode == PLAN_MODE_SWIGLU) {
+            const int64_t half = rows_per_wave_step / 2;
+            n_super = (int64_t)topk * ((N / 2 + half - 1) / half);
+        }
         const int wpb = p->threads / 64;
         int64_t blocks = (n_super + wpb - 1) / wpb;
         int per_cu = blocks_per_cu;
@@ -182,6 +202,7 @@ Plan valu(int MT, int L, int V, int U, bool moe)
     c.V = V;
     c.U = U;
     c.moe = moe;
+    c.mode = moe ? PLAN_MODE_MOE : PLAN_MODE_DENSE;
     return c;
 }
 
@@ -286,6 +307,40 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     return false;
 }
 
+// Expert tail. SwiGLU gate+up: the grouped-expert launch shape (8 lanes with 3 chunks per item for
+// rows of 72 chunks, else the widest lanes per row up to 32, one chunk per item). Combine: the
+// widest lanes per row up to 32 that divide the chunks of one weight row, one chunk per item,
+// which keeps the most waves busy on the short down-projection rows.
+bool make_tail_plan(int mode, int64_t N, int64_t K, int64_t KR, int topk, int cus,
+                    int64_t lds_limit, Plan *p)
+{
+    *p = Plan{};
+    if (N < 1 || K < 128 || K % 128 != 0 || topk < 1)
+        return false;
+    if (mode == PLAN_MODE_SWIGLU) {
+        const int64_t cpr = K / 32;
+        const int L = pow2_lanes(cpr) > 32 ? 32 : pow2_lanes(cpr);
+        Plan c = valu(1, 8, 3, 1, true);
+        c.mode = PLAN_MODE_SWIGLU;
+        if (L == 8 && (cpr / 8) % 3 == 0 && try_plan(c, 8, 1, N, K, topk, cus, lds_limit, p))
+            return true;
+        c = valu(1, L, 1, 1, true);
+        c.mode = PLAN_MODE_SWIGLU;
+        return L >= 4 && try_plan(c, 8, 1, N, K, topk, cus, lds_limit, p);
+    }
+    if (mode == PLAN_MODE_COMBINE) {
+        if (KR < 128 || KR % 128 != 0)
+            return false;
+        const int64_t cprw = KR / 32;
+        const int L = pow2_lanes(cprw) > 32 ? 32 : pow2_lanes(cprw);
+        Plan c = valu(1, L, 1, 1, false);
+        c.mode = PLAN_MODE_COMBINE;
+        c.kr = KR;
+        return L >= 4 && try_plan(c, 8, 1, N, K, topk, cus, lds_limit, p);
+    }
+    return false;
+}
+
 int describe_plan(const Plan &p, char *buf, size_t len)
 {
     if (!buf || len == 0)
@@ -295,7 +350,11 @@ int describe_plan(const Plan &p, char *buf, size_t len)
         n = snprintf(buf, len,
                      "valu%s tokens=%d lanes_per_row=%d chunks_per_item=%d row_steps=%d "
                      "threads=%d blocks=%lld lds=%lld",
-                     p.moe ? "_moe" : "", p.MT, p.L, p.V, p.U, p.threads, (long long)p.blocks,
+                     p.mode == PLAN_MODE_MOE       ? "_moe"
+                     : p.mode == PLAN_MODE_SWIGLU  ? "_moe_swiglu"
+                     : p.mode == PLAN_MODE_COMBINE ? "_moe_combine"
+                                                   : "",
+                     p.MT, p.L, p.V, p.U, p.threads, (long long)p.blocks,
                      (long long)p.lds_bytes);
     else if (p.kind == PLAN_SPLITK)
         n = snprintf(buf, len,

@@ -9,6 +9,11 @@ namespace w4a16 {
 
 enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3 };
 
+// What the rows of a staged VALU launch are: one matrix, expert rows, the gate+up experts with
+// the SwiGLU epilogue, or the down experts summed with router weights.
+enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
+                PLAN_MODE_COMBINE = 3 };
+
 // Instantiated kernels. A build may supply its own lists (for launch-shape sweeps) by defining
 // the macros first.
 //
@@ -22,6 +27,12 @@ enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3 };
     X(2, 64, 1, 1) X(2, 32, 1, 1) X(2, 16, 1, 1) X(2, 8, 1, 1) X(2, 4, 1, 1) X(2, 8, 1, 2)    \
     X(3, 64, 1, 1) X(3, 32, 1, 1) X(3, 16, 1, 1) X(3, 8, 1, 1) X(3, 4, 1, 1)                 \
     X(4, 64, 1, 1) X(4, 32, 1, 1) X(4, 16, 1, 1) X(4, 8, 1, 1) X(4, 4, 1, 1)
+#endif
+
+// Expert-tail kernels (staged VALU, one token, one row step): X(lanes per row, chunks per item),
+// each instantiated for the SwiGLU gate+up form (lanes per row <= 32) and the combine form.
+#ifndef W4A16_TAIL_CONFIGS
+#define W4A16_TAIL_CONFIGS(X) X(8, 3) X(32, 1) X(16, 1) X(8, 1) X(4, 1)
 #endif
 
 // Split-K VALU kernels (dense calls): X(tokens, lanes per row, chunks per lane, row steps).
@@ -44,7 +55,9 @@ struct Plan {
     int MT, L, V, U;   // VALU: tokens, lanes per row, chunks per lane per item, row steps per item
     int T, KS;         // MFMA: 16-row tiles per wave, waves splitting K (V: groups per item)
     bool xlds;         // MFMA: activations of all 16 token slots staged in LDS
-    bool moe;
+    bool moe;          // rows through expert ids (grouped and SwiGLU forms)
+    int mode;          // PlanMode (staged VALU)
+    int64_t kr;        // combine form: length of one weight row (K is the activation length)
     int threads;       // work-group size
     int64_t blocks;    // grid size
     int64_t lds_bytes; // dynamic LDS per work-group
@@ -64,6 +77,8 @@ struct GemvArgs {
     int64_t N;
     int32_t K;
     int32_t M;
+    const float *route_w;  // combine form: router weights (device), else null
+    int32_t KR;            // combine form: weight row length I (K = topk * I); else K
 };
 
 // Largest K handled by the VALU kernel for MT tokens (activations staged in LDS).
@@ -75,6 +90,12 @@ bool plan_instantiated(const Plan &p);
 // Fill `p` with the kernel and launch shape for a call (topk = 0 for dense calls).
 // Returns false when no kernel covers the shape.
 bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit, Plan *p);
+
+// Expert tail: mode PLAN_MODE_SWIGLU (N = 2I rows per expert, K) or PLAN_MODE_COMBINE (N = H
+// rows, K = topk * KR activation values, KR the weight row length). Returns false when no kernel
+// covers the shape.
+bool make_tail_plan(int mode, int64_t N, int64_t K, int64_t KR, int topk, int cus,
+                    int64_t lds_limit, Plan *p);
 
 // Launch-shape override for tuning: keeps the caller's kernel choice, fills in grid and LDS.
 bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit,
