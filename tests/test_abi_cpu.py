@@ -126,7 +126,7 @@ def test_down_combine_validation(kw, status):
 @pytest.mark.parametrize("step,rows,K,I,topk,want", [
     (0, 0, 2304, 1024, 8, "valu_moe_swiglu tokens=1 lanes_per_row=8 chunks_per_item=3"),
     (0, 0, 2048, 1408, 8, "valu_moe_swiglu tokens=1 lanes_per_row=32 chunks_per_item=1"),
-    (1, 2304, 0, 1024, 8, "valu_moe_combine tokens=1 lanes_per_row=32 chunks_per_item=1"),
+    (1, 2304, 0, 1024, 8, "splitk_moe_combine tokens=1 lanes_per_row=32 chunks_per_lane=1"),
     (1, 7168, 0, 1408, 8, "valu_moe_combine tokens=1 lanes_per_row=4 chunks_per_item=1"),
     (1, 5, 0, 128, 1, "valu_moe_combine tokens=1 lanes_per_row=4"),
 ])

@@ -572,18 +572,27 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
 // time with one item of prefetch and unconditional loads (rows past the block's end re-read its
 // last row); per-row partial sums of the W slices meet in LDS once, after the last row, and are
 // added in slice order.
+//
+// GATHER (one token): the combine form of the expert tail. The activation is the concatenation
+// of the topk rows h[t] (K = topk*KR), and the L chunks that chunk step j of a wave covers lie in
+// one slot t_j (KR/32 is a multiple of L), read from expert ids[t_j]'s rows with the partial sum
+// scaled by the router weight w[t_j]: the block's rows come out as sum_t w[t] W_{ids[t]}[n] h[t].
+// Slot, expert and weight are the same in every lane, so the row bases stay scalar. An invalid
+// id reads expert 0 with weight 0.
 // ------------------------------------------------------------------------------------------
-template <int MT, int L, int CL, int U>
+template <int MT, int L, int CL, int U, bool GATHER>
 __global__ void __launch_bounds__(512)
 gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                    const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
-                   int64_t N, int32_t K, int32_t rows_per_block)
+                   int64_t N, int32_t K, int32_t rows_per_block, const int32_t *__restrict__ ids,
+                   int32_t E, const float *__restrict__ rw, int32_t KR)
 {
+    static_assert(!GATHER || MT == 1, "the combine form is single-token");
     constexpr int R = 64 / L;
     constexpr int ROWS = U * R;
     extern __shared__ float red[];      // [MT][rows_per_block][W]
-    const int CPR = K >> 5;
-    const int GPR = K >> 7;
+    const int CPR = (GATHER ? KR : K) >> 5;   // 16-byte chunks per weight row
+    const int GPR = (GATHER ? KR : K) >> 7;
     const int W = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -611,8 +620,8 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
         if (!full && r > rcount - 1)
             r = rcount - 1;
         lrow[u] = r;
-        woff[u] = (uint32_t)((r * CPR + cbase) * 16);
-        soff[u] = (uint32_t)((r * GPR + (cbase >> 2)) * 2);
+        woff[u] = (uint32_t)((r * CPR + pr) * 16);
+        soff[u] = (uint32_t)((r * GPR + (pr >> 2)) * 2);
     }
     auto item_row0 = [&](int item) -> int {
         if (!full)
@@ -620,17 +629,39 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
         const int r = item * ROWS;
         return r + ROWS <= rcount ? r : rcount - ROWS;
     };
+    // Per chunk step j: the weight-row base (in chunks and in scale groups) of its slot's expert
+    // and the router weight; dense calls use row 0 of the matrix and weight 1.
+    const uint4 *wq[CL];
+    const uint16_t *sq[CL];
+    float wt[CL];
+#pragma unroll
+    for (int j = 0; j < CL; ++j) {
+        if constexpr (GATHER) {
+            const int c0 = wave * (L * CL) + L * j;   // first chunk of step j, uniform
+            const int slot = c0 / CPR;
+            const int32_t e = __builtin_amdgcn_readfirstlane(ids[slot]);
+            const bool ok = e >= 0 && e < E;
+            const int64_t ee = ok ? e : 0;
+            wq[j] = qw + ee * N * CPR + (c0 - slot * CPR);
+            sq[j] = sc + ee * N * GPR + ((c0 - slot * CPR) >> 2);
+            wt[j] = ok ? rw[slot] : 0.0f;
+        } else {
+            wq[j] = qw + wave * (L * CL) + L * j;
+            sq[j] = sc + ((wave * (L * CL) + L * j) >> 2);
+            wt[j] = 1.0f;
+        }
+    }
     int ld_item = 0;
     auto load = [&](Buf &buf) {
         const int64_t row0 = r0 + item_row0(ld_item);
-        const char *wb = reinterpret_cast<const char *>(qw + row0 * CPR);
-        const char *sb = reinterpret_cast<const char *>(sc + row0 * GPR);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < CL; ++j) {
-                buf.w[j][u] = load_weights(reinterpret_cast<const uint4 *>(wb + woff[u] + 16 * L * j));
-                buf.s[j][u] = *reinterpret_cast<const uint16_t *>(sb + soff[u] + 2 * (L / 4) * j);
+                const char *wb = reinterpret_cast<const char *>(wq[j] + row0 * CPR);
+                const char *sb = reinterpret_cast<const char *>(sq[j] + row0 * GPR);
+                buf.w[j][u] = load_weights(reinterpret_cast<const uint4 *>(wb + woff[u]));
+                buf.s[j][u] = *reinterpret_cast<const uint16_t *>(sb + soff[u]);
             }
         ++ld_item;
     };
@@ -680,7 +711,9 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
         for (int j = 0; j < CL; ++j)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const float s = half_bits_to_float(buf.s[j][u]);
+                float s = half_bits_to_float(buf.s[j][u]);
+                if constexpr (GATHER)
+                    s *= wt[j];
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
                     acc[u][t] = fmaf(s, chunk_dot(buf.w[j][u], xq[t][j], off[t][j]), acc[u][t]);
@@ -1079,14 +1112,15 @@ static hipError_t launch_valu_t(const GemvArgs &a, const Plan &p, hipStream_t st
                            args, (size_t)p.lds_bytes, stream);
 }
 
-template <int MT, int L, int CL, int U>
+template <int MT, int L, int CL, int U, bool GATHER>
 static hipError_t launch_splitk_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
-    auto kern = gemv_splitk_kernel<MT, L, CL, U>;
+    auto kern = gemv_splitk_kernel<MT, L, CL, U, GATHER>;
     int32_t rpb = (int32_t)p.rows_per_block;
-    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X, (void *)&a.ldx,
-                    (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.N, (void *)&a.K,
-                    (void *)&rpb};
+    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X,   (void *)&a.ldx,
+                    (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.N,   (void *)&a.K,
+                    (void *)&rpb,       (void *)&a.ids,    (void *)&a.E,   (void *)&a.route_w,
+                    (void *)&a.KR};
     return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(p.threads),
                            args, (size_t)p.lds_bytes, stream);
 }
@@ -1117,8 +1151,12 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
         return launch_valu_t<1, (L_ <= 32 ? L_ : 32), V_, 1, VALU_SWIGLU>(a, p, stream);
 
 #define W4A16_SPLITK_CASE(MT_, L_, CL_, U_)                                                  \
-    if (p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_ && !p.moe)                       \
-        return launch_splitk_t<MT_, L_, CL_, U_>(a, p, stream);
+    if (p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_ && p.mode == PLAN_MODE_DENSE)      \
+        return launch_splitk_t<MT_, L_, CL_, U_, false>(a, p, stream);
+
+#define W4A16_GATHER_CASE(L_, CL_)                                                           \
+    if (p.MT == 1 && p.L == L_ && p.V == CL_ && p.U == 1 && p.mode == PLAN_MODE_COMBINE)      \
+        return launch_splitk_t<1, L_, CL_, 1, true>(a, p, stream);
 
 #define W4A16_MFMA_CASE(T_, KS_, XL_, GU_, WPB_)                                             \
     if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) && p.V == GU_ && p.threads == 64 * WPB_) \
@@ -1131,6 +1169,7 @@ hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream)
         W4A16_TAIL_CONFIGS(W4A16_TAIL_CASE)
     } else if (p.kind == PLAN_SPLITK) {
         W4A16_SPLITK_CONFIGS(W4A16_SPLITK_CASE)
+        W4A16_GATHER_CONFIGS(W4A16_GATHER_CASE)
     } else if (p.kind == PLAN_MFMA) {
         W4A16_MFMA_CONFIGS(W4A16_MFMA_CASE)
     }

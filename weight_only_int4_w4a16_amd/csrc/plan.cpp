@@ -27,7 +27,12 @@ bool plan_instantiated(const Plan &p)
         (p.mode == PLAN_MODE_COMBINE || (p.mode == PLAN_MODE_SWIGLU && L_ <= 32)))             \
         return true;
 #define W4A16_SPLITK_MATCH(MT_, L_, CL_, U_)                                                  \
-    if (p.kind == PLAN_SPLITK && p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_)          \
+    if (p.kind == PLAN_SPLITK && p.MT == MT_ && p.L == L_ && p.V == CL_ && p.U == U_ &&        \
+        p.mode == PLAN_MODE_DENSE)                                                            \
+        return true;
+#define W4A16_GATHER_MATCH(L_, CL_)                                                           \
+    if (p.kind == PLAN_SPLITK && p.MT == 1 && p.L == L_ && p.V == CL_ && p.U == 1 &&           \
+        p.mode == PLAN_MODE_COMBINE)                                                          \
         return true;
 #define W4A16_MFMA_MATCH(T_, KS_, XL_, GU_, WPB_)                                            \
     if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) &&            \
@@ -37,7 +42,9 @@ bool plan_instantiated(const Plan &p)
     W4A16_TAIL_CONFIGS(W4A16_TAIL_MATCH)
     W4A16_MFMA_CONFIGS(W4A16_MFMA_MATCH)
     W4A16_SPLITK_CONFIGS(W4A16_SPLITK_MATCH)
+    W4A16_GATHER_CONFIGS(W4A16_GATHER_MATCH)
 #undef W4A16_SPLITK_MATCH
+#undef W4A16_GATHER_MATCH
 #undef W4A16_VALU_MATCH
 #undef W4A16_TAIL_MATCH
 #undef W4A16_MFMA_MATCH
@@ -103,6 +110,11 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
         // V holds the chunks per lane; the number of waves follows from K. Dense calls only.
         const int64_t per_wave = (int64_t)p->L * p->V;
         if (p->MT != M || p->moe || cpr % per_wave != 0)
+            return false;
+        // Combine form: every chunk step of a wave lies in one slot.
+        if (p->mode == PLAN_MODE_COMBINE &&
+            (p->kr < 128 || p->kr % 128 != 0 || (p->kr / 32) % p->L != 0 ||
+             K != (int64_t)topk * p->kr))
             return false;
         const int64_t waves = cpr / per_wave;
         if (waves < 1 || waves > 8)
@@ -333,6 +345,16 @@ bool make_tail_plan(int mode, int64_t N, int64_t K, int64_t KR, int topk, int cu
             return false;
         const int64_t cprw = KR / 32;
         const int L = pow2_lanes(cprw) > 32 ? 32 : pow2_lanes(cprw);
+        // Split-K over the slots when the waves fit a work-group, with the fewest chunks per
+        // lane that keep the waves within 8 (2 work-groups per CU); else the staged kernel.
+        static const int cls[] = {1, 2, 4, 8};
+        for (int cl : cls) {
+            Plan c = splitk(1, L, cl, 1, false);
+            c.mode = PLAN_MODE_COMBINE;
+            c.kr = KR;
+            if (try_plan(c, 2, 1, N, K, topk, cus, lds_limit, p))
+                return true;
+        }
         Plan c = valu(1, L, 1, 1, false);
         c.mode = PLAN_MODE_COMBINE;
         c.kr = KR;
@@ -360,7 +382,7 @@ int describe_plan(const Plan &p, char *buf, size_t len)
         n = snprintf(buf, len,
                      "splitk%s tokens=%d lanes_per_row=%d chunks_per_lane=%d row_steps=%d "
                      "threads=%d blocks=%lld rows_per_block=%lld lds=%lld",
-                     p.moe ? "_moe" : "", p.MT, p.L, p.V, p.U, p.threads, (long long)p.blocks,
+                     p.mode == PLAN_MODE_COMBINE ? "_moe_combine" : "", p.MT, p.L, p.V, p.U, p.threads, (long long)p.blocks,
                      (long long)p.rows_per_block, (long long)p.lds_bytes);
     else if (p.kind == PLAN_MFMA)
         n = snprintf(buf, len,

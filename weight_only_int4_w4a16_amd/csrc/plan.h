@@ -35,6 +35,11 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
 #define W4A16_TAIL_CONFIGS(X) X(8, 3) X(32, 1) X(16, 1) X(8, 1) X(4, 1)
 #endif
 
+// Split-K kernels in the combine form of the expert tail: X(lanes per row, chunks per lane).
+#ifndef W4A16_GATHER_CONFIGS
+#define W4A16_GATHER_CONFIGS(X) X(32, 1) X(32, 2) X(16, 2) X(16, 4) X(8, 4) X(8, 8) X(4, 8)
+#endif
+
 // Split-K VALU kernels (dense calls): X(tokens, lanes per row, chunks per lane, row steps).
 #ifndef W4A16_SPLITK_CONFIGS
 #define W4A16_SPLITK_CONFIGS(X)                                                              \
