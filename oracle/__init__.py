@@ -9,7 +9,9 @@ It computes y[n] = sum_k q[n,k] * s[n, k/128] * x[k] exactly as that sum reads (
 plus mag[n] = sum_k |q s x|, the basis of the per-element tolerance
 |err| <= 1e-3 * mag + 1e-5. For the expert tail it also computes the SwiGLU of the grouped
 gate+up product (h = silu(g) * u, rounded to bfloat16) and the router-weighted sum of the
-grouped down projection, out = sum_t w[t] * W_down[ids[t]] h[t]. See w4a16_oracle.c for
+grouped down projection, out = sum_t w[t] * W_down[ids[t]] h[t], and the step before the path:
+symmetric round-to-nearest quantisation of bf16 weights into the packed format (codes and fp16
+scales decided in float32, so they are exact targets). See w4a16_oracle.c for
 the storage format and the passage of the local-kimi README it follows.
 
 Pins (tests/test_oracle_pins.py) tie it to facts other than itself: hand-computed worked
@@ -85,8 +87,12 @@ class Oracle:
                                           P, P, P, P, P, P]
         lib.oracle_moe_down_combine.argtypes = [P, P, P, P, i32, i32, P, i64, i64, i32, P, i64,
                                                 P, P]
+        lib.oracle_float_to_f16_sat.argtypes = [ctypes.c_float]
+        lib.oracle_float_to_f16_sat.restype = ctypes.c_uint16
+        lib.oracle_quantize_pack.argtypes = [P, i64, i64, i64, i32, P, P]
         for f in (lib.oracle_unpack, lib.oracle_gemv, lib.oracle_gemv_batched,
-                  lib.oracle_moe_gemv, lib.oracle_moe_swiglu, lib.oracle_moe_down_combine):
+                  lib.oracle_moe_gemv, lib.oracle_moe_swiglu, lib.oracle_moe_down_combine,
+                  lib.oracle_quantize_pack):
             f.restype = ctypes.c_int
         self.lib = lib
 
@@ -188,6 +194,22 @@ class Oracle:
         return out, mag
 
 
+    def float_to_f16_sat(self, v: float) -> int:
+        return int(self.lib.oracle_float_to_f16_sat(float(v)))
+
+    def quantize_pack(self, w_bf16, K: int, group: int = 128) -> Tuple[np.ndarray, np.ndarray]:
+        """(qweight uint32 [N][K/8], scales uint16 fp16 bits [N][K/G]) of bf16 bits [N][ldw]."""
+        ww = _c(w_bf16, np.uint16)
+        if ww.ndim == 1:
+            ww = ww.reshape(1, -1)
+        N, ldw = ww.shape
+        qw = np.zeros((N, K // 8), np.uint32)
+        sc = np.zeros((N, K // group), np.uint16)
+        if self.lib.oracle_quantize_pack(_ptr(ww), ldw, N, K, group, _ptr(qw), _ptr(sc)):
+            raise ValueError("oracle_quantize_pack: bad arguments")
+        return qw, sc
+
+
 _default: Optional[Oracle] = None
 
 
@@ -239,6 +261,10 @@ def moe_swiglu(*a, **kw):
 
 def moe_down_combine(*a, **kw):
     return default().moe_down_combine(*a, **kw)
+
+
+def quantize_pack(*a, **kw):
+    return default().quantize_pack(*a, **kw)
 
 
 def bound(mag: np.ndarray) -> np.ndarray:

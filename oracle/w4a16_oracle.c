@@ -305,3 +305,93 @@ int oracle_moe_down_combine(const uint32_t *qweight, const uint16_t *scales, con
     }
     return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * The step before the path: turning bf16 weights into the packed format. The pages say only
+ * that the INT4 artifact was built from the bf16 checkpoint ("selective INT4"); the method is
+ * this library's reading, the plainest symmetric round-to-nearest scheme for the format:
+ *   per row n and 128-wide group g:  amax = max |w|,  s = fp16(amax / 7)  (float32 division,
+ *   round to nearest even; a result beyond the largest finite fp16 saturates to 65504),
+ *   q = clamp(rint(w / s), -8, 7) with w / s a float32 division and rint ties-to-even,
+ *   and q = 0 for the whole group when s is zero.
+ * Every decision is taken in float32, as the definition states, so the codes and scales are
+ * exact targets for any implementation of it.
+ * ------------------------------------------------------------------------------------------ */
+
+/* float -> IEEE binary16 bit pattern, round to nearest even; values beyond the largest finite
+ * binary16 saturate to +-65504 (0x7BFF). NaN gives a quiet NaN. */
+uint16_t oracle_float_to_f16_sat(float f)
+{
+    double v = (double)f;      /* exact */
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7E00u);
+    if (a == 0.0)
+        return sign;
+    int ex;
+    frexp(a, &ex);                     /* leading bit 2^(ex-1) */
+    int qexp = ex - 1 - 10;            /* spacing of binary16 values: 2^(e-10), e >= -14 */
+    if (qexp < -24)
+        qexp = -24;                    /* subnormal spacing 2^-24 */
+    double r = rint(ldexp(a, -qexp));  /* nearest, ties to even */
+    double q = ldexp(r, qexp);
+    if (q > 65504.0)
+        return (uint16_t)(sign | 0x7BFFu);
+    /* encode q (exactly representable) */
+    if (q < ldexp(1.0, -14))
+        return (uint16_t)(sign | (uint16_t)rint(ldexp(q, 24)));      /* subnormal or zero */
+    frexp(q, &ex);
+    int e = ex - 1;                                                    /* q = m * 2^e, m in [1,2) */
+    int frac = (int)rint(ldexp(q, 10 - e)) - 1024;
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)frac);
+}
+
+/* The float32 value of a bf16 pattern (exact). */
+static float bf16_to_float(uint16_t b)
+{
+    uint32_t bits = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/*
+ * Quantise and pack w (bf16 bits, N rows of stride ldw elements, K values each) into
+ * qweight uint32[N][K/8] (value k in bits [4(k%8), 4(k%8)+3] of word k/8, two's complement) and
+ * scales fp16 bits [N][K/G]. K % G == 0, G % 8 == 0.
+ */
+int oracle_quantize_pack(const uint16_t *w, int64_t ldw, int64_t N, int64_t K, int32_t G,
+                         uint32_t *qweight, uint16_t *scales)
+{
+    if (!w || !qweight || !scales || N < 1 || K < 1 || G < 8 || G % 8 || K % G || ldw < K)
+        return ORACLE_BAD_ARG;
+    for (int64_t n = 0; n < N; ++n) {
+        const uint16_t *row = w + n * ldw;
+        for (int64_t g = 0; g < K / G; ++g) {
+            float amax = 0.0f;
+            for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+                float a = fabsf(bf16_to_float(row[k]));
+                if (a > amax)
+                    amax = a;
+            }
+            volatile float s32 = amax / 7.0f;            /* one float32 division */
+            uint16_t sbits = oracle_float_to_f16_sat(s32);
+            scales[n * (K / G) + g] = sbits;
+            float s = (float)oracle_f16_to_double(sbits);
+            for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+                int q = 0;
+                if (s != 0.0f) {
+                    volatile float r = bf16_to_float(row[k]) / s;   /* one float32 division */
+                    float qi = rintf(r);
+                    q = qi < -8.0f ? -8 : (qi > 7.0f ? 7 : (int)qi);
+                }
+                uint32_t *word = &qweight[n * (K / 8) + k / 8];
+                uint32_t nib = (uint32_t)q & 0xFu;
+                int shift = 4 * (int)(k % 8);
+                *word = (*word & ~(0xFu << shift)) | (nib << shift);
+            }
+        }
+    }
+    return ORACLE_OK;
+}

@@ -448,9 +448,81 @@ def pin_down_combine(orc):
     assert np.all(mag >= np.abs(out))
 
 
+# ---------------------------------------------------------------- quantise + pack
+def pin_quantize_golden(orc):
+    gold = _golden("w4_quantize_round_to_even.json")
+    row = np.zeros(256, np.uint16)
+    row[:8] = gold["group0"]["bf16"]
+    row[128:132] = gold["group1"]["bf16"]
+    qw, sc = orc.quantize_pack(row[None, :], 256)
+    assert list(sc[0]) == [gold["group0"]["scale"], gold["group1"]["scale"]]
+    assert int(qw[0, 0]) == gold["group0"]["word0"] and int(qw[0, 16]) == gold["group1"]["word16"]
+    assert np.all(qw[0, 1:16] == 0) and np.all(qw[0, 17:] == 0)
+
+
+def numpy_quantize(w_bits: np.ndarray, K: int):
+    """Independent float32 numpy path of the same definition (numpy's own float32 division,
+    float16 conversion and rint), used as a brute-force check."""
+    w = (w_bits.astype(np.uint32) << 16).view(np.float32).reshape(w_bits.shape[0], K // 128, 128)
+    amax = np.abs(w).max(axis=2)
+    with np.errstate(over="ignore"):
+        s16 = (amax / np.float32(7.0)).astype(np.float16)
+    s16 = np.where(np.isinf(s16), np.float16(65504.0), s16)
+    s = s16.astype(np.float32)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s == 0, 0, np.clip(np.rint(w / s), -8, 7)).astype(np.int64)
+    return q.reshape(w_bits.shape[0], K), s16.view(np.uint16)
+
+
+def pin_quantize_brute(orc):
+    """Codes and scales equal the numpy float32 path bit for bit on random rows with a wide
+    magnitude spread, zero groups, huge groups (scale saturation) and tiny ones (subnormal
+    scales); packing round-trips through unpack; |w - q s| <= s / 2 off the clamp."""
+    rng = np.random.default_rng(41)
+    N, K = 12, 512
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    w *= np.exp2(rng.integers(-30, 20, size=(N, K // 128))).repeat(128, axis=1).astype(np.float32)
+    w[3, 128:256] = 0.0                      # zero group
+    w[5, :128] *= np.float32(2.0 ** 100)     # scale saturates at 65504
+    w[7, 256:384] *= np.float32(2.0 ** -110)  # subnormal or zero scales
+    bits = (w.view(np.uint32) >> 16).astype(np.uint16)   # truncated to bf16 (any bf16 will do)
+    qw, sc = orc.quantize_pack(bits, K)
+    q_ref, s_ref = numpy_quantize(bits, K)
+    assert np.array_equal(sc, s_ref)
+    assert np.array_equal(orc.unpack(qw, K).astype(np.int64), q_ref)
+    s = sc.view(np.float16).astype(np.float64).repeat(128, axis=1)
+    wv = bf16_bits_to_f64(bits)
+    q = q_ref.astype(np.float64)
+    inside = (np.abs(q) < 7) & (s > 0)
+    assert np.all(np.abs(wv - q * s)[inside] <= s[inside] / 2 * (1 + 2.0 ** -20))
+    assert np.all(q[3, 128:256] == 0) and np.all(sc[3, 1] == 0)
+    assert np.all(sc[5, 0] == 0x7BFF)
+
+
+def pin_quantize_gemv_roundtrip(orc):
+    """Quantising a matrix that is already exactly representable (integer codes in [-7, 7]
+    times an fp16 scale with amax 7 in every group) returns the same codes and scales, so the
+    GEMV of the quantised matrix equals the product with the original values."""
+    rng = np.random.default_rng(42)
+    N, K = 6, 384
+    q = rng.integers(-7, 8, size=(N, K))
+    q[:, ::128] = 7                          # amax 7 in every group
+    scale_exp = rng.integers(-10, 3, size=(N, K // 128))
+    s = np.exp2(scale_exp).astype(np.float64)
+    w = (q * s.repeat(128, axis=1)).astype(np.float32)
+    bits = (w.view(np.uint32) >> 16).astype(np.uint16)
+    qw, sc = orc.quantize_pack(bits, K)
+    assert np.array_equal(orc.unpack(qw, K).astype(np.int64), q)
+    assert np.array_equal(sc.view(np.float16).astype(np.float64), s)
+    x = (rng.standard_normal(K).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y, _ = orc.gemv(qw, sc, x, K)
+    assert np.allclose(y, w.astype(np.float64) @ bf16_bits_to_f64(x), rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [
     pin_f16_decode, pin_bf16_decode, pin_w1, pin_w2, pin_unpack, pin_unit_probes,
     pin_zero_scale_groups, pin_linearity, pin_negation, pin_constant_rows, pin_brute_force,
     pin_mag_nonnegative, pin_batched, pin_moe, pin_row_subset, pin_bf16_round_brute,
     pin_bf16_round_ties, pin_silu, pin_swiglu_golden, pin_swiglu_brute, pin_down_combine,
+    pin_quantize_golden, pin_quantize_brute, pin_quantize_gemv_roundtrip,
 ]

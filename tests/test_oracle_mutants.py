@@ -44,6 +44,15 @@ MUTANTS = {
     "down_slot_as_expert": ("int64_t row = (int64_t)e * H + n;", "int64_t row = (int64_t)t * H + n;"),
     "down_shared_h_row": ("h + (int64_t)t * I, I, G,", "h, I, G,"),
     "down_signed_mag": ("m += fabs((double)w[t]) * ym;", "m += (double)w[t] * ym;"),
+    "quant_divides_by_8": ("amax / 7.0f", "amax / 8.0f"),
+    "quant_ties_away": ("float qi = rintf(r);", "float qi = roundf(r);"),
+    "quant_truncates": ("float qi = rintf(r);", "float qi = truncf(r);"),
+    "quant_scale_truncated": ("double r = rint(ldexp(a, -qexp));  /* nearest, ties to even */",
+                              "double r = floor(ldexp(a, -qexp));"),
+    "quant_no_saturation": ("return (uint16_t)(sign | 0x7BFFu);", "return (uint16_t)(sign | 0x7C00u);"),
+    "quant_nibble_order": ("int shift = 4 * (int)(k % 8);", "int shift = 4 * (7 - (int)(k % 8));"),
+    "quant_amax_signed": ("float a = fabsf(bf16_to_float(row[k]));", "float a = bf16_to_float(row[k]);"),
+    "quant_f16_subnormal": ("if (qexp < -24)\n        qexp = -24;", "if (qexp < -30)\n        qexp = -30;"),
 }
 
 
