@@ -354,7 +354,30 @@ def per_workload(torch, np, w, synthetic, dev, cus):
     del m, x, y, idsets
     torch.cuda.empty_cache()
     res["c4_expert_tail_top8_of_256"] = expert_tail(torch, np, w, synthetic, dev, cus)
+    res["quantize_pack_28672x4096"] = quantize_rate(torch, np, w, dev)
     return res
+
+
+def quantize_rate(torch, np, w, dev):
+    """bf16 -> packed INT4 for the 28672 x 4096 gate+up matrix: reads 2 bytes and writes
+    0.5 + 1/64 bytes per weight. Four rotated input copies (940 MB) so reads come from HBM."""
+    N, K = 28672, 4096
+    g = torch.Generator(device="cpu").manual_seed(0)
+    src = (torch.randn((N, K), generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    R = 4
+    copies = rotated(torch, src, R)
+    del src
+    qw = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    sc = torch.empty((N, K // 128), dtype=torch.float16, device=dev)
+    fn = lambda i: w.quantize_pack(copies[i % R], out=(qw, sc))  # noqa: E731
+    fn(0)
+    med, p10, p90 = graph_replay_stats(torch, fn, 16, 5)
+    b = 2 * N * K + N * K // 2 + N * (K // 128) * 2
+    del copies
+    torch.cuda.empty_cache()
+    return {"N": N, "K": K, "bytes": b, "us_per_call": round(med, 3), "us_p10": round(p10, 3),
+            "us_p90": round(p90, 3), "GB_s": round(b / med / 1e3, 1),
+            "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1)}
 
 
 def tail_bytes(d):

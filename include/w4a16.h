@@ -134,6 +134,21 @@ w4a16_status_t w4a16_moe_down_combine(const uint32_t *qweight, const uint16_t *s
                                       hipStream_t stream);
 
 /*
+ * The step before the path: quantise a bf16 weight matrix into this library's format. The
+ * local-kimi README, technical-detail section, builds its INT4 artifact from the bf16 weights
+ * without giving the method; this is the plainest symmetric round-to-nearest scheme:
+ *   per row n and 128-wide group g: s = fp16(amax / 7), the float32 quotient rounded to the
+ *   nearest-even binary16 and saturated at 65504; q = clamp(rint(w / s), -8, 7) with a float32
+ *   quotient and ties to even; q = 0 for a group whose s is zero.
+ *   w bf16 bits, N rows of stride ldw elements (ldw >= K, ldw % 8 == 0, w 16-byte aligned);
+ *   qweight uint32[N][K/8] and scales fp16 bits [N][K/128] (outputs, fully overwritten).
+ *   1 <= N <= 2^31 - 1; 128 <= K <= 2^20, K % 128 == 0. Inputs must be finite.
+ */
+w4a16_status_t w4a16_quantize_pack(const uint16_t *w, int64_t ldw, uint32_t *qweight,
+                                   uint16_t *scales, int64_t N, int64_t K, int32_t group_size,
+                                   hipStream_t stream);
+
+/*
  * Test support: q_out int8[N][K] receives the signed value of every packed nibble, so the
  * unpacking can be checked bit for bit. 1 <= N, 8 <= K, K % 8 == 0; qweight 4-byte aligned
  * (one word per thread); otherwise W4A16_ERR_MISALIGNED.

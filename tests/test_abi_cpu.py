@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     for n in ("w4a16_gemv", "w4a16_gemv_batched", "w4a16_moe_gemv", "w4a16_unpack_debug",
               "w4a16_describe_plan", "w4a16_status_string", "w4a16_abi_version",
               "w4a16_stream_read", "w4a16_moe_gemv_swiglu", "w4a16_moe_down_combine",
-              "w4a16_describe_tail_plan"):
+              "w4a16_describe_tail_plan", "w4a16_quantize_pack"):
         assert n in names
 
 
@@ -134,6 +134,20 @@ def test_tail_dispatch(step, rows, K, I, topk, want):
     assert w.describe_tail_plan(step, rows, K, I, topk).startswith(want)
 
 
+def quant(w_=A, ldw=256, qw=A, sc=A, N=64, K=256, G=128):
+    return w.library().w4a16_quantize_pack(w_, ldw, qw, sc, N, K, G, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w_=None), NULLP), (dict(qw=None), NULLP), (dict(sc=None), NULLP), (dict(G=64), GROUP),
+    (dict(N=0), SHAPE), (dict(K=200), SHAPE), (dict(K=0), SHAPE), (dict(ldw=128), SHAPE),
+    (dict(K=(1 << 20) + 128, ldw=(1 << 20) + 128), SHAPE), (dict(w_=A + 8), ALIGN),
+    (dict(ldw=260), ALIGN), (dict(qw=A + 2), ALIGN), (dict(sc=A + 1), ALIGN),
+])
+def test_quantize_validation(kw, status):
+    assert quant(**kw) == status
+
+
 def test_unpack_validation():
     lib = w.library()
     assert lib.w4a16_unpack_debug(None, A, 4, 64, None) == NULLP
@@ -166,6 +180,7 @@ def test_valid_arguments_reach_the_device_check_only():
     assert w.library().w4a16_stream_read(A, 64, A, 1, 4, None) == DEVICE
     assert swiglu() == DEVICE
     assert down() == DEVICE
+    assert quant() == DEVICE
 
 
 @pytest.mark.parametrize("M,N,K,topk,kind", [

@@ -23,7 +23,8 @@ from typing import Optional
 import torch
 
 __all__ = ["gemv", "gemv_batched", "moe_gemv", "moe_gemv_swiglu", "moe_down_combine",
-           "unpack_debug", "describe_plan", "describe_tail_plan", "stream_read", "W4A16Error",
+           "quantize_pack", "unpack_debug", "describe_plan", "describe_tail_plan", "stream_read",
+           "W4A16Error",
            "library", "LIB_PATH", "GROUP_SIZE", "MAX_BATCH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")
@@ -58,13 +59,14 @@ def library() -> ctypes.CDLL:
     lib.w4a16_moe_gemv_swiglu.argtypes = [P, P, P, i32, i32, P, P, i64, i64, i32, P]
     lib.w4a16_moe_down_combine.argtypes = [P, P, P, P, i32, i32, P, P, i64, i64, i32, P]
     lib.w4a16_describe_tail_plan.argtypes = [i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i64]
+    lib.w4a16_quantize_pack.argtypes = [P, i64, P, P, i64, i64, i32, P]
     lib.w4a16_status_string.argtypes = [ctypes.c_int]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_abi_version.argtypes = []
     for f in (lib.w4a16_gemv, lib.w4a16_gemv_batched, lib.w4a16_moe_gemv,
               lib.w4a16_unpack_debug, lib.w4a16_describe_plan, lib.w4a16_stream_read,
               lib.w4a16_moe_gemv_swiglu, lib.w4a16_moe_down_combine,
-              lib.w4a16_describe_tail_plan, lib.w4a16_abi_version):
+              lib.w4a16_describe_tail_plan, lib.w4a16_quantize_pack, lib.w4a16_abi_version):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -222,6 +224,33 @@ def moe_down_combine(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: to
                                          E, h.data_ptr(), out.data_ptr(), H, I, GROUP_SIZE,
                                          _stream(stream)), "w4a16_moe_down_combine")
     return out
+
+
+def quantize_pack(w_bf16: torch.Tensor, out=None, stream=None):
+    """Quantise bf16 weights [N, >=K] (unit stride along K; K = w.shape[1] unless out says
+    otherwise) into (qweight int32 [N, K/8], scales float16 [N, K/128])."""
+    _need(w_bf16, torch.bfloat16, "w", 2)
+    N = w_bf16.shape[0]
+    if w_bf16.stride(1) != 1:
+        raise ValueError("w must have unit stride along K")
+    if out is None:
+        K = w_bf16.shape[1]
+        qweight = torch.empty((N, K // 8), dtype=torch.int32, device=w_bf16.device)
+        scales = torch.empty((N, K // GROUP_SIZE), dtype=torch.float16, device=w_bf16.device)
+    else:
+        qweight, scales = out
+        K = qweight.shape[1] * 8
+    _need(qweight, torch.int32, "qweight", 2)
+    _need(scales, torch.float16, "scales", 2)
+    if (tuple(qweight.shape) != (N, K // 8) or tuple(scales.shape) != (N, K // GROUP_SIZE)
+            or not qweight.is_contiguous() or not scales.is_contiguous()
+            or K > w_bf16.shape[1]):
+        raise ValueError("qweight [N, K/8] and scales [N, K/128] must be contiguous")
+    ldw = w_bf16.stride(0) if N > 1 else max(w_bf16.stride(0), K)
+    _ok(library().w4a16_quantize_pack(w_bf16.data_ptr(), ldw, qweight.data_ptr(),
+                                      scales.data_ptr(), N, K, GROUP_SIZE, _stream(stream)),
+        "w4a16_quantize_pack")
+    return qweight, scales
 
 
 def unpack_debug(qweight: torch.Tensor, stream=None) -> torch.Tensor:

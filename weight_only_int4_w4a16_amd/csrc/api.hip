@@ -15,6 +15,8 @@ hipError_t launch_unpack(const uint32_t *qw, int8_t *out, int64_t words, int cus
                          hipStream_t stream);
 hipError_t launch_stream_read(const void *buf, int64_t n16, uint32_t *out, int blocks,
                               int unroll, hipStream_t stream);
+hipError_t launch_quantize(const uint16_t *W, int64_t ldw, uint32_t *qw, uint16_t *sc, int64_t N,
+                           int32_t K, int cus, hipStream_t stream);
 
 namespace {
 
@@ -189,6 +191,27 @@ w4a16_status_t w4a16_moe_down_combine(const uint32_t *qweight, const uint16_t *s
     GemvArgs a{qweight, scales, h, K, out, H, expert_ids, topk, num_experts, H, (int32_t)K, 1,
                route_weights, (int32_t)I};
     return launch(a, plan, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+w4a16_status_t w4a16_quantize_pack(const uint16_t *w, int64_t ldw, uint32_t *qweight,
+                                   uint16_t *scales, int64_t N, int64_t K, int32_t group_size,
+                                   hipStream_t stream)
+{
+    if (!w || !qweight || !scales)
+        return W4A16_ERR_NULL_POINTER;
+    if (group_size != W4A16_GROUP_SIZE)
+        return W4A16_ERR_BAD_GROUP;
+    if (N < 1 || N > kMaxN || K < W4A16_GROUP_SIZE || K % W4A16_GROUP_SIZE != 0 ||
+        K > kMaxKBatched || ldw < K)
+        return W4A16_ERR_BAD_SHAPE;
+    if (!aligned(w, 16) || ldw % 8 != 0 || !aligned(qweight, 4) || !aligned(scales, 2))
+        return W4A16_ERR_MISALIGNED;
+    const DeviceInfo *dev = current_device();
+    if (!dev)
+        return W4A16_ERR_UNSUPPORTED_DEVICE;
+    return launch_quantize(w, ldw, qweight, scales, N, (int32_t)K, dev->cus, stream) == hipSuccess
+               ? W4A16_OK
+               : W4A16_ERR_LAUNCH;
 }
 
 w4a16_status_t w4a16_unpack_debug(const uint32_t *qweight, int8_t *q_out, int64_t N, int64_t K,
