@@ -90,9 +90,11 @@ class Oracle:
         lib.oracle_float_to_f16_sat.argtypes = [ctypes.c_float]
         lib.oracle_float_to_f16_sat.restype = ctypes.c_uint16
         lib.oracle_quantize_pack.argtypes = [P, i64, i64, i64, i32, P, P]
+        lib.oracle_moe_gemv_batched.argtypes = [P, P, P, i32, i32, i32, P, i64, i64, i64, i32,
+                                                P, i64, P, P]
         for f in (lib.oracle_unpack, lib.oracle_gemv, lib.oracle_gemv_batched,
                   lib.oracle_moe_gemv, lib.oracle_moe_swiglu, lib.oracle_moe_down_combine,
-                  lib.oracle_quantize_pack):
+                  lib.oracle_quantize_pack, lib.oracle_moe_gemv_batched):
             f.restype = ctypes.c_int
         self.lib = lib
 
@@ -194,6 +196,24 @@ class Oracle:
         return out, mag
 
 
+    def moe_gemv_batched(self, qweight, scales, ids, X, K: int, group: int = 128,
+                         rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """(Y, mag) float64 [M][topk][rows]: token m times expert ids[m][t], qweight [E][N][K/8]."""
+        qw, sc = _c(qweight, np.uint32), _c(scales, np.uint16)
+        ii, XX = _c(ids, np.int32), _c(X, np.uint16)
+        if XX.ndim == 1:
+            XX = XX.reshape(1, -1)
+        M, ldx = XX.shape
+        ii = ii.reshape(M, -1)
+        topk = ii.shape[1]
+        E, N = qw.shape[0], qw.shape[1]
+        r, nr = _rows(rows, N)
+        Y, mag = np.empty((M, topk, nr)), np.empty((M, topk, nr))
+        if self.lib.oracle_moe_gemv_batched(_ptr(qw), _ptr(sc), _ptr(ii), M, topk, E, _ptr(XX),
+                                            ldx, N, K, group, _ptr(r), nr, _ptr(Y), _ptr(mag)):
+            raise ValueError("oracle_moe_gemv_batched: bad arguments")
+        return Y, mag
+
     def float_to_f16_sat(self, v: float) -> int:
         return int(self.lib.oracle_float_to_f16_sat(float(v)))
 
@@ -261,6 +281,10 @@ def moe_swiglu(*a, **kw):
 
 def moe_down_combine(*a, **kw):
     return default().moe_down_combine(*a, **kw)
+
+
+def moe_gemv_batched(*a, **kw):
+    return default().moe_gemv_batched(*a, **kw)
 
 
 def quantize_pack(*a, **kw):

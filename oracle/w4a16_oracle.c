@@ -395,3 +395,38 @@ int oracle_quantize_pack(const uint16_t *w, int64_t ldw, int64_t N, int64_t K, i
     }
     return ORACLE_OK;
 }
+
+/*
+ * Grouped-expert form for M tokens at once, each with its own topk experts:
+ *   Y[m][t][r] = sum_k q_e[n,k] s_e[n, k/G] X[m][k],  e = ids[m * topk + t], n = rows[r],
+ * qweight uint32[E][N][K/8], scales fp16 bits [E][N][K/G], ids int32[M][topk], X bf16 bits
+ * [M][ldx]; Y and mag are [M][topk][n_rows]. An id outside [0, E) gives zeros. (How a kernel
+ * shares one expert's weights between the tokens that chose it does not change the result.)
+ */
+int oracle_moe_gemv_batched(const uint32_t *qweight, const uint16_t *scales, const int32_t *ids,
+                            int32_t M, int32_t topk, int32_t E, const uint16_t *X, int64_t ldx,
+                            int64_t N, int64_t K, int32_t G, const int64_t *rows, int64_t n_rows,
+                            double *Y, double *mag)
+{
+    if (check_dense(qweight, scales, X, N, K, G, rows, n_rows, Y, mag))
+        return ORACLE_BAD_ARG;
+    if (!ids || M < 1 || topk < 1 || E < 1 || ldx < K || (!rows && n_rows != N))
+        return ORACLE_BAD_ARG;
+    for (int32_t m = 0; m < M; ++m)
+        for (int32_t t = 0; t < topk; ++t) {
+            int32_t e = ids[(int64_t)m * topk + t];
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t n = rows ? rows[r] : r;
+                int64_t o = ((int64_t)m * topk + t) * n_rows + r;
+                if (e < 0 || e >= E) {
+                    Y[o] = 0.0;
+                    mag[o] = 0.0;
+                    continue;
+                }
+                int64_t row = (int64_t)e * N + n;
+                dot_row(qweight + row * (K / 8), scales + row * (K / G), X + m * ldx, K, G,
+                        &Y[o], &mag[o]);
+            }
+        }
+    return ORACLE_OK;
+}

@@ -519,10 +519,38 @@ def pin_quantize_gemv_roundtrip(orc):
     assert np.allclose(y, w.astype(np.float64) @ bf16_bits_to_f64(x), rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------- batched grouped experts
+def pin_moe_batched(orc):
+    """Token m, slot t is the product of expert ids[m][t] with X[m]: against the independent
+    numpy dequantise + BLAS path, with repeated experts across tokens, a repeated expert within
+    a token, invalid ids (zeros), a padded X stride and a row subset."""
+    E, N, K, M, T = 7, 5, 256, 3, 4
+    rng = np.random.default_rng(51)
+    q = rng.integers(-8, 8, size=(E, N, K))
+    words = np.stack([pack_nibbles(q[e]) for e in range(E)])
+    scales = rng.uniform(0.001, 0.01, size=(E, N, K // 128)).astype(np.float16).view(np.uint16)
+    X = (rng.standard_normal((M, K + 8)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ids = np.array([[1, 4, 6, 1], [4, 0, -2, 6], [7, 3, 1, 2]], np.int32)
+    Y, mag = orc.moe_gemv_batched(words, scales, ids, X, K)
+    xs = bf16_bits_to_f64(X[:, :K])
+    for m in range(M):
+        for t in range(T):
+            e = ids[m, t]
+            if not 0 <= e < E:
+                assert np.all(Y[m, t] == 0) and np.all(mag[m, t] == 0)
+                continue
+            W = numpy_dense_weights(words[e], scales[e], K)
+            assert np.allclose(Y[m, t], W @ xs[m], rtol=1e-12, atol=1e-14)
+            assert np.allclose(mag[m, t], np.abs(W * xs[m]).sum(1), rtol=1e-12)
+    assert np.array_equal(Y[0, 0], Y[0, 3]) and not np.array_equal(Y[0, 1], Y[1, 0])
+    Ys, ms = orc.moe_gemv_batched(words, scales, ids, X, K, rows=[4, 0])
+    assert np.array_equal(Ys, Y[:, :, [4, 0]]) and np.array_equal(ms, mag[:, :, [4, 0]])
+
+
 ALL_PINS = [
     pin_f16_decode, pin_bf16_decode, pin_w1, pin_w2, pin_unpack, pin_unit_probes,
     pin_zero_scale_groups, pin_linearity, pin_negation, pin_constant_rows, pin_brute_force,
     pin_mag_nonnegative, pin_batched, pin_moe, pin_row_subset, pin_bf16_round_brute,
     pin_bf16_round_ties, pin_silu, pin_swiglu_golden, pin_swiglu_brute, pin_down_combine,
-    pin_quantize_golden, pin_quantize_brute, pin_quantize_gemv_roundtrip,
+    pin_quantize_golden, pin_quantize_brute, pin_quantize_gemv_roundtrip, pin_moe_batched,
 ]

@@ -52,6 +52,9 @@ MUTANTS = {
     "quant_no_saturation": ("return (uint16_t)(sign | 0x7BFFu);", "return (uint16_t)(sign | 0x7C00u);"),
     "quant_nibble_order": ("int shift = 4 * (int)(k % 8);", "int shift = 4 * (7 - (int)(k % 8));"),
     "quant_amax_signed": ("float a = fabsf(bf16_to_float(row[k]));", "float a = bf16_to_float(row[k]);"),
+    "moe_batched_token_row": ("X + m * ldx, K, G,\n                        &Y[o], &mag[o]);",
+                              "X, K, G,\n                        &Y[o], &mag[o]);"),
+    "moe_batched_id_index": ("ids[(int64_t)m * topk + t]", "ids[(int64_t)t * M + m]"),
     "quant_f16_subnormal": ("if (qexp < -24)\n        qexp = -24;", "if (qexp < -30)\n        qexp = -30;"),
 }
 
