@@ -355,7 +355,45 @@ def per_workload(torch, np, w, synthetic, dev, cus):
     torch.cuda.empty_cache()
     res["c4_expert_tail_top8_of_256"] = expert_tail(torch, np, w, synthetic, dev, cus)
     res["quantize_pack_28672x4096"] = quantize_rate(torch, np, w, dev)
+    res.update(moe_batched(torch, np, w, synthetic, dev, cus))
     return res
+
+
+def moe_batched(torch, np, w, synthetic, dev, cus):
+    """The c4 experts (256 of 2048 x 2304) for M tokens decoded together, each with its own
+    top-8: every selected expert is read once. Bytes count each selected expert once (the mean
+    over the 64 id sets used) plus the M activation rows."""
+    m = synthetic.config("c4", 0)
+    qw = torch.from_numpy(m.qweight.view(np.int32)).to(dev)
+    sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
+    cp = list(zip(rotated(torch, qw, 2), rotated(torch, sc, 2)))
+    del qw, sc
+    per_expert = m.N * m.K // 2 + m.N * (m.K // 128) * 2
+    out = {}
+    for M in (2, 4, 8, 16):
+        rng = np.random.default_rng([4, 2, M])
+        sets = [np.stack([rng.choice(m.E, m.topk, replace=False) for _ in range(M)])
+                .astype(np.int32) for _ in range(64)]
+        uniq = float(np.mean([len(np.unique(s_)) for s_ in sets]))
+        idsets = [torch.from_numpy(s_).to(dev) for s_ in sets]
+        X = torch.from_numpy(synthetic.draw_acts(rng, (M, m.K)).view(np.int16)).to(dev)
+        X = X.view(torch.bfloat16)
+        Y = torch.empty((M, m.topk, m.N), dtype=torch.float32, device=dev)
+
+        def fn(i, idsets=idsets, X=X, Y=Y):
+            w.moe_gemv_batched(cp[i % 2][0], cp[i % 2][1], idsets[i % 64], X, out=Y)
+        fn(0)
+        med, p10, p90 = graph_replay_stats(torch, fn, 128, 10)
+        b = uniq * per_expert + M * m.K * 2
+        out[f"c4_moe_batched_M{M}"] = {
+            "experts": m.E, "topk": m.topk, "N": m.N, "K": m.K, "M": M,
+            "mean_unique_experts": round(uniq, 2),
+            "plan": w.describe_moe_batched_plan(M, m.N, m.K, m.topk, cus),
+            "us_per_call": round(med, 3), "us_p10": round(p10, 3), "us_p90": round(p90, 3),
+            "GB_s": round(b / med / 1e3, 1), "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1)}
+    del cp
+    torch.cuda.empty_cache()
+    return out
 
 
 def quantize_rate(torch, np, w, dev):
@@ -446,12 +484,25 @@ def profile_workload(torch, np, w, synthetic, dev, name, M, steps):
         sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
         cp = list(zip(rotated(torch, qw, 2), rotated(torch, sc, 2)))
         del qw, sc
-        x = torch.from_numpy(m.x.view(np.int16)).to(dev).view(torch.bfloat16)
-        ids = torch.from_numpy(m.ids).to(dev)
-        y = torch.empty((m.topk, m.N), dtype=torch.float32, device=dev)
-        for i in range(steps):
-            w.moe_gemv(cp[i % 2][0], cp[i % 2][1], ids, x, out=y)
-        plan = w.describe_plan(1, m.N, m.K, m.topk)
+        if M == 1:
+            x = torch.from_numpy(m.x.view(np.int16)).to(dev).view(torch.bfloat16)
+            ids = torch.from_numpy(m.ids).to(dev)
+            y = torch.empty((m.topk, m.N), dtype=torch.float32, device=dev)
+            for i in range(steps):
+                w.moe_gemv(cp[i % 2][0], cp[i % 2][1], ids, x, out=y)
+            plan = w.describe_plan(1, m.N, m.K, m.topk)
+        else:
+            # M tokens with their own top-8 (one id set, the same as the bench's first)
+            rng = np.random.default_rng([4, 2, M])
+            idn = np.stack([rng.choice(m.E, m.topk, replace=False) for _ in range(M)])
+            ids = torch.from_numpy(idn.astype(np.int32)).to(dev)
+            X = torch.from_numpy(synthetic.draw_acts(rng, (M, m.K)).view(np.int16)).to(dev)
+            X = X.view(torch.bfloat16)
+            Y = torch.empty((M, m.topk, m.N), dtype=torch.float32, device=dev)
+            for i in range(steps):
+                w.moe_gemv_batched(cp[i % 2][0], cp[i % 2][1], ids, X, out=Y)
+            plan = (w.describe_moe_batched_plan(M, m.N, m.K, m.topk) +
+                    f" unique_experts={len(np.unique(idn))}")
     else:
         d = synthetic.config(name, 0, M=M)
         qw, sc, x = to_dev(d, dev, torch, np)

@@ -99,6 +99,24 @@ w4a16_status_t w4a16_moe_gemv(const uint32_t *qweight, const uint16_t *scales,
                               int32_t group_size, hipStream_t stream);
 
 /*
+ * Grouped-expert GEMV for M tokens decoded together, each with its own topk experts:
+ *   Y[m][t] = W_e X[m],  e = expert_ids[m * topk + t]
+ *   qweight uint32[E][N][K/8], scales fp16 bits [E][N][K/128]; expert_ids int32[M][topk] in
+ *   DEVICE memory; X bf16 bits, M rows of stride ldx (ldx >= K, ldx % 8 == 0); Y float
+ *   [M][topk][N], fully overwritten. Every expert that any token selected is read once per call
+ *   and applied to all the tokens that chose it (the grouped-expert form of the local-kimi
+ *   README, technical-detail section, extended to a batch). An id outside [0, E) gives a row of
+ *   +0.0; repeated ids are allowed.
+ *   1 <= M <= 16; 1 <= topk, M * topk <= 256; N, K as for w4a16_gemv, and the M activation rows
+ *   must fit in LDS (about M * K * 2.1 bytes <= 150 KiB), else W4A16_ERR_BAD_SHAPE.
+ */
+w4a16_status_t w4a16_moe_gemv_batched(const uint32_t *qweight, const uint16_t *scales,
+                                      const int32_t *expert_ids, int32_t M, int32_t topk,
+                                      int32_t num_experts, const uint16_t *X, int64_t ldx,
+                                      float *Y, int64_t N, int64_t K, int32_t group_size,
+                                      hipStream_t stream);
+
+/*
  * Expert tail, step 1: the grouped gate+up product of one token with the SwiGLU epilogue. The
  * local-kimi README, technical-detail section, lists a SwiGLU variant of the grouped W4A16 kernel
  * beside the plain one; the split of an expert's rows and the rounding of h are this library's
@@ -182,6 +200,10 @@ w4a16_status_t w4a16_describe_plan(int32_t M, int64_t N, int64_t K, int32_t topk
  */
 w4a16_status_t w4a16_describe_tail_plan(int32_t step, int64_t rows, int64_t K, int64_t I,
                                         int32_t topk, int32_t cus, char *buf, int64_t len);
+
+/* Host-only introspection of w4a16_moe_gemv_batched's launch (same conventions). */
+w4a16_status_t w4a16_describe_moe_batched_plan(int32_t M, int64_t N, int64_t K, int32_t topk,
+                                               int32_t cus, char *buf, int64_t len);
 
 /* Static, never-NULL description of a status code. */
 const char *w4a16_status_string(w4a16_status_t status);

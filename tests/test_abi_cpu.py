@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     for n in ("w4a16_gemv", "w4a16_gemv_batched", "w4a16_moe_gemv", "w4a16_unpack_debug",
               "w4a16_describe_plan", "w4a16_status_string", "w4a16_abi_version",
               "w4a16_stream_read", "w4a16_moe_gemv_swiglu", "w4a16_moe_down_combine",
-              "w4a16_describe_tail_plan", "w4a16_quantize_pack"):
+              "w4a16_describe_tail_plan", "w4a16_quantize_pack", "w4a16_moe_gemv_batched",
+              "w4a16_describe_moe_batched_plan"):
         assert n in names
 
 
@@ -148,6 +149,28 @@ def test_quantize_validation(kw, status):
     assert quant(**kw) == status
 
 
+def moeb(qw=A, sc=A, ids=A, M=4, topk=8, E=16, X=A, ldx=256, Y=A, N=64, K=256, G=128):
+    return w.library().w4a16_moe_gemv_batched(qw, sc, ids, M, topk, E, X, ldx, Y, N, K, G, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qw=None), NULLP), (dict(ids=None), NULLP), (dict(X=None), NULLP), (dict(Y=None), NULLP),
+    (dict(G=64), GROUP), (dict(M=0), SHAPE), (dict(M=17), SHAPE), (dict(topk=0), SHAPE),
+    (dict(M=16, topk=17), SHAPE), (dict(E=0), SHAPE), (dict(ldx=128), SHAPE), (dict(K=200), SHAPE),
+    (dict(ldx=260), ALIGN), (dict(ids=A + 2), ALIGN), (dict(X=A + 8), ALIGN),
+])
+def test_moe_batched_validation(kw, status):
+    assert moeb(**kw) == status
+
+
+def test_moe_batched_plans():
+    assert w.describe_moe_batched_plan(16, 2048, 2304, 8).startswith(
+        "moe_batched tokens_per_pass=1 lanes_per_row=8 chunks_per_item=3 threads=512")
+    assert w.describe_moe_batched_plan(1, 5, 128, 256).startswith("moe_batched")
+    with pytest.raises(w.W4A16Error):
+        w.describe_moe_batched_plan(16, 100, 8192, 8)    # activations do not fit in LDS
+
+
 def test_unpack_validation():
     lib = w.library()
     assert lib.w4a16_unpack_debug(None, A, 4, 64, None) == NULLP
@@ -181,6 +204,7 @@ def test_valid_arguments_reach_the_device_check_only():
     assert swiglu() == DEVICE
     assert down() == DEVICE
     assert quant() == DEVICE
+    assert moeb() == DEVICE
 
 
 @pytest.mark.parametrize("M,N,K,topk,kind", [

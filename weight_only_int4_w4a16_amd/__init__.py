@@ -22,7 +22,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["gemv", "gemv_batched", "moe_gemv", "moe_gemv_swiglu", "moe_down_combine",
+__all__ = ["gemv", "gemv_batched", "moe_gemv", "moe_gemv_batched", "moe_gemv_swiglu",
+           "moe_down_combine", "describe_moe_batched_plan",
            "quantize_pack", "unpack_debug", "describe_plan", "describe_tail_plan", "stream_read",
            "W4A16Error",
            "library", "LIB_PATH", "GROUP_SIZE", "MAX_BATCH"]
@@ -60,13 +61,17 @@ def library() -> ctypes.CDLL:
     lib.w4a16_moe_down_combine.argtypes = [P, P, P, P, i32, i32, P, P, i64, i64, i32, P]
     lib.w4a16_describe_tail_plan.argtypes = [i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i64]
     lib.w4a16_quantize_pack.argtypes = [P, i64, P, P, i64, i64, i32, P]
+    lib.w4a16_moe_gemv_batched.argtypes = [P, P, P, i32, i32, i32, P, i64, P, i64, i64, i32, P]
+    lib.w4a16_describe_moe_batched_plan.argtypes = [i32, i64, i64, i32, i32, ctypes.c_char_p,
+                                                    i64]
     lib.w4a16_status_string.argtypes = [ctypes.c_int]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_abi_version.argtypes = []
     for f in (lib.w4a16_gemv, lib.w4a16_gemv_batched, lib.w4a16_moe_gemv,
               lib.w4a16_unpack_debug, lib.w4a16_describe_plan, lib.w4a16_stream_read,
               lib.w4a16_moe_gemv_swiglu, lib.w4a16_moe_down_combine,
-              lib.w4a16_describe_tail_plan, lib.w4a16_quantize_pack, lib.w4a16_abi_version):
+              lib.w4a16_describe_tail_plan, lib.w4a16_quantize_pack, lib.w4a16_moe_gemv_batched,
+              lib.w4a16_describe_moe_batched_plan, lib.w4a16_abi_version):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -168,6 +173,35 @@ def moe_gemv(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tens
     return out
 
 
+def moe_gemv_batched(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tensor,
+                     X: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Y[m, t] = W_{expert_ids[m, t]} X[m] for M <= 16 tokens with their own experts; every
+    selected expert is read once. expert_ids int32 [M, topk]; returns float32 [M, topk, N]."""
+    _need(qweight, torch.int32, "qweight", 3)
+    _need(scales, torch.float16, "scales", 3)
+    _need(expert_ids, torch.int32, "expert_ids", 2)
+    _need(X, torch.bfloat16, "X", 2)
+    E, N, K = qweight.shape[0], qweight.shape[1], qweight.shape[2] * 8
+    M, topk = expert_ids.shape
+    if not all(t.is_contiguous() for t in (qweight, scales, expert_ids)):
+        raise ValueError("qweight, scales and expert_ids must be contiguous")
+    if (tuple(scales.shape) != (E, N, K // GROUP_SIZE) or X.shape[0] != M or X.shape[1] < K
+            or X.stride(1) != 1):
+        raise ValueError("shape mismatch between qweight, scales, expert_ids and X")
+    if out is None:
+        out = torch.empty((M, topk, N), dtype=torch.float32, device=qweight.device)
+    _need(out, torch.float32, "out", 3)
+    if tuple(out.shape) != (M, topk, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [M, topk, N] tensor")
+    ldx = X.stride(0) if M > 1 else max(X.stride(0), K)
+    _ok(library().w4a16_moe_gemv_batched(qweight.data_ptr(), scales.data_ptr(),
+                                         expert_ids.data_ptr(), M, topk, E, X.data_ptr(), ldx,
+                                         out.data_ptr(), N, K, GROUP_SIZE, _stream(stream)),
+        "w4a16_moe_gemv_batched")
+    return out
+
+
 def moe_gemv_swiglu(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tensor,
                     x: torch.Tensor, out: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:
@@ -263,6 +297,14 @@ def unpack_debug(qweight: torch.Tensor, stream=None) -> torch.Tensor:
     _ok(library().w4a16_unpack_debug(qweight.data_ptr(), out.data_ptr(), N, K, _stream(stream)),
         "w4a16_unpack_debug")
     return out
+
+
+def describe_moe_batched_plan(M: int, N: int, K: int, topk: int, cus: int = 256) -> str:
+    """Launch shape of w4a16_moe_gemv_batched (host-only)."""
+    buf = ctypes.create_string_buffer(256)
+    _ok(library().w4a16_describe_moe_batched_plan(M, N, K, topk, cus, buf, len(buf)),
+        "w4a16_describe_moe_batched_plan")
+    return buf.value.decode()
 
 
 def describe_tail_plan(step: int, rows: int, K: int, I: int, topk: int, cus: int = 256) -> str:

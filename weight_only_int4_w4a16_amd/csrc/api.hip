@@ -138,6 +138,33 @@ w4a16_status_t w4a16_moe_gemv(const uint32_t *qweight, const uint16_t *scales,
     return run(a, 1, topk, stream);
 }
 
+w4a16_status_t w4a16_moe_gemv_batched(const uint32_t *qweight, const uint16_t *scales,
+                                      const int32_t *expert_ids, int32_t M, int32_t topk,
+                                      int32_t num_experts, const uint16_t *X, int64_t ldx,
+                                      float *Y, int64_t N, int64_t K, int32_t group_size,
+                                      hipStream_t stream)
+{
+    w4a16_status_t st = check_common(qweight, scales, X, Y, N, K, group_size, kMaxKDense);
+    if (st != W4A16_OK)
+        return st;
+    if (!expert_ids)
+        return W4A16_ERR_NULL_POINTER;
+    if (M < 1 || M > W4A16_MAX_BATCH || topk < 1 || M * topk > 256 || num_experts < 1 ||
+        ldx < K || (int64_t)M * topk * N > kMaxN)
+        return W4A16_ERR_BAD_SHAPE;
+    if (ldx % 8 != 0 || !aligned(expert_ids, 4))
+        return W4A16_ERR_MISALIGNED;
+    const DeviceInfo *dev = current_device();
+    if (!dev)
+        return W4A16_ERR_UNSUPPORTED_DEVICE;
+    Plan plan;
+    if (!make_moe_batched_plan(M, N, K, topk, dev->cus, dev->lds_limit, &plan))
+        return W4A16_ERR_BAD_SHAPE;
+    GemvArgs a{qweight, scales, X, ldx, Y, N, expert_ids, topk, num_experts, N, (int32_t)K, M,
+               nullptr, (int32_t)K};
+    return launch(a, plan, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
 w4a16_status_t w4a16_moe_gemv_swiglu(const uint32_t *qweight, const uint16_t *scales,
                                      const int32_t *expert_ids, int32_t topk, int32_t num_experts,
                                      const uint16_t *x, uint16_t *h, int64_t I, int64_t K,
@@ -257,6 +284,19 @@ w4a16_status_t w4a16_describe_plan(int32_t M, int64_t N, int64_t K, int32_t topk
     Plan plan;
     // 160 KiB of LDS per work-group, as on gfx950.
     if (cus < 1 || !make_plan(M, N, K, topk, cus, 160 * 1024, &plan))
+        return W4A16_ERR_BAD_SHAPE;
+    describe_plan(plan, buf, (size_t)len);
+    return W4A16_OK;
+}
+
+w4a16_status_t w4a16_describe_moe_batched_plan(int32_t M, int64_t N, int64_t K, int32_t topk,
+                                               int32_t cus, char *buf, int64_t len)
+{
+    if (!buf || len < 1)
+        return W4A16_ERR_NULL_POINTER;
+    buf[0] = '\0';
+    Plan plan;
+    if (cus < 1 || !make_moe_batched_plan(M, N, K, topk, cus, 160 * 1024, &plan))
         return W4A16_ERR_BAD_SHAPE;
     describe_plan(plan, buf, (size_t)len);
     return W4A16_OK;

@@ -760,6 +760,228 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
 }
 
 // ------------------------------------------------------------------------------------------
+// Grouped-expert GEMV for M tokens with their own topk experts each: every expert selected by
+// any token is streamed once per call and multiplied with all the tokens that chose it.
+//
+// Set-up (every work-group, identically, in LDS): the P = M*topk entries (token m, slot t) are
+// grouped by expert id, in order of first appearance; ids outside [0, E) form one group of their
+// own whose outputs are zero. A group of c entries becomes ceil(c / MT) virtual entries of up to
+// MT (token, slot) pairs. Work items are (block of rows, virtual entry), block-major, so the
+// virtual entries of one expert read the same rows in consecutive waves of a work-group and a
+// second token of an expert finds those rows in the L2 cache; within an item the wave streams R
+// rows of the entry's expert like the staged kernel (activations of all M tokens staged in LDS,
+// re-paired, with their chunk offsets) and accumulates one product per pair. Empty pair slots are
+// skipped by wave-uniform branches around the arithmetic only (the loads stay straight-line).
+// One pair per virtual entry (MT = 1) measured fastest on MI355X: larger MT costs registers, and
+// so waves, on every expert for the few that more than one token chose.
+// ------------------------------------------------------------------------------------------
+template <int L, int V, int MT>
+__global__ void __launch_bounds__(512)
+gemv_moe_batched_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
+                        const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y,
+                        const int32_t *__restrict__ ids, int32_t M, int32_t topk, int32_t E,
+                        int64_t N, int32_t K)
+{
+    constexpr int R = 64 / L;
+    extern __shared__ uint4 smem[];
+    const int KW = K >> 3;
+    const int CPR = K >> 5;
+    const int GPR = K >> 7;
+    const int P = M * topk;
+    // Region A holds the grouping scratch first and the staged activations afterwards.
+    const int a16 = (M * KW > (5 * P + 3) / 4) ? M * KW : (5 * P + 3) / 4;   // 16-byte units
+    uint4 *xs = smem;                                              // [M][4][CPR]
+    int32_t *key_s = reinterpret_cast<int32_t *>(smem);           // [P] expert id or -1
+    int32_t *first_s = key_s + P;                                   // [P] first entry of the group
+    int32_t *rank_s = first_s + P;                                  // [P] position in the group
+    int32_t *cnt_s = rank_s + P;                                    // [P] virtual entries (firsts)
+    int32_t *vbase_s = cnt_s + P;                                   // [P] first virtual entry
+    float *bs = reinterpret_cast<float *>(smem + a16);            // [M][CPR]
+    int32_t *ve_e = reinterpret_cast<int32_t *>(bs + M * CPR);    // [P] virtual entry's expert
+    int32_t *ve_tok = ve_e + P;                                     // [P][MT] entries or -1
+    int32_t *nve_s = ve_tok + P * MT;                               // [1]
+
+    // ---- group the entries by expert
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        const int32_t e = ids[i];
+        key_s[i] = (e >= 0 && e < E) ? e : -1;
+        ve_e[i] = -1;
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+            ve_tok[i * MT + j] = -1;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        const int32_t k = key_s[i];
+        int f = i, r = 0;
+        for (int j = i - 1; j >= 0; --j)
+            if (key_s[j] == k) {
+                f = j;
+                ++r;
+            }
+        first_s[i] = f;
+        rank_s[i] = r;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        int c = 0;
+        if (first_s[i] == i)
+            for (int q = i; q < P; ++q)
+                c += key_s[q] == key_s[i];
+        cnt_s[i] = (c + MT - 1) / MT;      // virtual entries of the group (0 unless first)
+    }
+    __syncthreads();
+    // Virtual entries of the groups whose first entry precedes i, summed in entry order.
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        int base = 0;
+        for (int j = 0; j < i; ++j)
+            base += cnt_s[j];
+        vbase_s[i] = base;
+        if (i == P - 1)
+            nve_s[0] = base + cnt_s[i];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        const int v = vbase_s[first_s[i]] + rank_s[i] / MT;
+        ve_tok[v * MT + rank_s[i] % MT] = i;
+        if (rank_s[i] % MT == 0)
+            ve_e[v] = key_s[i];
+    }
+    __syncthreads();   // the grouping scratch is overwritten by the activations below
+
+    // ---- stage the activations of every token
+    for (int t = 0; t < M; ++t) {
+        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
+        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
+            const uint4 v = xg[w];
+            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
+            float sum = 0.0f;
+            sum = dot2(v.x, 0x3F803F80u, sum);
+            sum = dot2(v.y, 0x3F803F80u, sum);
+            sum = dot2(v.z, 0x3F803F80u, sum);
+            sum = dot2(v.w, 0x3F803F80u, sum);
+            sum += dpp_partner(sum, 0);
+            sum += dpp_partner(sum, 1);
+            if ((w & 3) == 0)
+                bs[t * CPR + (w >> 2)] = -kOffset * sum;
+        }
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int pr = lane & (L - 1);
+    const int rr = lane / L;
+    const int wpb = blockDim.x >> 6;
+    const int64_t gw = (int64_t)blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t GW = (int64_t)gridDim.x * wpb;
+    const int nve = nve_s[0];
+    // P * N < 2^31 (checked by the host), so block counts and item indices fit in 32 bits.
+    const uint32_t n_blocks = (uint32_t)((N + R - 1) / R);
+    const uint32_t n_super = (uint32_t)nve * n_blocks;
+    const int nb = CPR / (L * V);
+    if (gw >= (int64_t)n_super)
+        return;
+    const int64_t n_items = ((n_super - 1 - gw) / GW + 1) * nb;
+
+    // Rows of block b of an expert: the last block is pulled back to end at row N - 1 (rows
+    // computed twice give identical bits); with fewer than R rows the lane rows are clamped.
+    auto lane_row = [&](uint32_t b) -> int64_t {
+        if (N < R)
+            return rr < N ? rr : N - 1;
+        const int64_t r0 = (int64_t)b * R + R <= N ? (int64_t)b * R : N - R;
+        return r0 + rr;
+    };
+    struct Buf {
+        uint4 w[V];
+        uint16_t s[V];
+    };
+    uint32_t ld_st = (uint32_t)gw;
+    int ld_b = 0;
+    auto load = [&](Buf &buf) {
+        const uint32_t b = ld_st / (uint32_t)nve;
+        const uint32_t v = ld_st - b * (uint32_t)nve;
+        const int32_t e = ve_e[v];
+        const int64_t row = (int64_t)(e >= 0 ? e : 0) * N + lane_row(b);
+        const uint4 *wr = pick(e >= 0, qw + row * CPR, reinterpret_cast<const uint4 *>(X));
+        const uint16_t *sr = pick(e >= 0, sc + row * GPR, X);
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+            const int c = pr + L * (q + V * ld_b);
+            buf.w[q] = load_weights(wr + c);
+            buf.s[q] = sr[c >> 2];
+        }
+        const bool wrap = ld_b + 1 == nb;
+        ld_b = wrap ? 0 : ld_b + 1;
+        ld_st += wrap ? (uint32_t)GW : 0u;
+    };
+
+    float acc[MT];
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+        acc[j] = 0.0f;
+    uint32_t cp_st = (uint32_t)gw;
+    int cp_b = 0;
+    auto compute = [&](const Buf &buf) {
+        const uint32_t bb = cp_st / (uint32_t)nve;
+        const uint32_t v = cp_st - bb * (uint32_t)nve;
+        int tok[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+            tok[j] = ve_tok[v * MT + j];
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+            const int c = pr + L * (q + V * cp_b);
+            const float s = half_bits_to_float(buf.s[q]);
+#pragma unroll
+            for (int j = 0; j < MT; ++j) {
+                if (j > 0 && tok[j] < 0)
+                    break;
+                const int m = tok[j] >= 0 ? tok[j] / topk : 0;
+                uint4 xq[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    xq[h] = xs[m * KW + h * CPR + c];
+                acc[j] = fmaf(s, chunk_dot(buf.w[q], xq, bs[m * CPR + c]), acc[j]);
+            }
+        }
+        if (cp_b == nb - 1) {
+            const int32_t e = ve_e[v];
+            const int64_t row = lane_row(bb);
+#pragma unroll
+            for (int j = 0; j < MT; ++j) {
+                if (j > 0 && tok[j] < 0)
+                    break;
+                float r[1] = {acc[j]};
+                fold_rows<L, 1>(r, pr);
+                if (pr == 0 && tok[j] >= 0)
+                    Y[(int64_t)tok[j] * N + row] = e >= 0 ? r[0] : 0.0f;
+                acc[j] = 0.0f;
+            }
+        }
+        const bool wrap = cp_b + 1 == nb;
+        cp_b = wrap ? 0 : cp_b + 1;
+        cp_st += wrap ? (uint32_t)GW : 0u;
+    };
+
+    Buf bufA, bufB;
+    load(bufA);
+    int64_t i = 0;
+    for (; i + 2 < n_items; i += 2) {
+        load(bufB);
+        compute(bufA);
+        load(bufA);
+        compute(bufB);
+    }
+    if (i + 1 < n_items) {
+        load(bufB);
+        compute(bufA);
+        compute(bufB);
+    } else {
+        compute(bufA);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // MFMA GEMV for 2..16 tokens (v_mfma_f32_16x16x32_bf16), computed as D = X * W^T so that each
 // lane's four outputs belong to one weight row: lane (i = l%16, g = l/16) supplies, for word j of
 // chunk 4s+g of a group s, the 8 activations of token i (A operand, re-paired) and the 8 decoded
@@ -1125,6 +1347,21 @@ static hipError_t launch_splitk_t(const GemvArgs &a, const Plan &p, hipStream_t 
                            args, (size_t)p.lds_bytes, stream);
 }
 
+#ifndef W4A16_MOE_BATCHED_MT
+#define W4A16_MOE_BATCHED_MT 1   // tokens accumulated per pass over an expert's rows
+#endif
+
+template <int L, int V>
+static hipError_t launch_moe_batched_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
+{
+    auto kern = gemv_moe_batched_kernel<L, V, W4A16_MOE_BATCHED_MT>;
+    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X,    (void *)&a.ldx,
+                    (void *)&a.Y,       (void *)&a.ids,    (void *)&a.M,    (void *)&a.topk,
+                    (void *)&a.E,       (void *)&a.N,      (void *)&a.K};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(p.threads),
+                           args, (size_t)p.lds_bytes, stream);
+}
+
 template <int T, int KS, bool XLDS, int GU, int WPB>
 static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
@@ -1162,8 +1399,16 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
     if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) && p.V == GU_ && p.threads == 64 * WPB_) \
         return launch_mfma_t<T_, KS_, (XL_ != 0), GU_, WPB_>(a, p, stream);
 
+#define W4A16_MOE_BATCHED_CASE(L_, V_)                                                       \
+    if (p.L == L_ && p.V == V_)                                                              \
+        return launch_moe_batched_t<L_, V_>(a, p, stream);
+
 hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
+    if (p.kind == PLAN_MOE_BATCHED) {
+        W4A16_MOE_BATCHED_CONFIGS(W4A16_MOE_BATCHED_CASE)
+        return hipErrorInvalidConfiguration;
+    }
     if (p.kind == PLAN_VALU) {
         W4A16_VALU_CONFIGS(W4A16_VALU_CASE)
         W4A16_TAIL_CONFIGS(W4A16_TAIL_CASE)

@@ -363,6 +363,55 @@ bool make_tail_plan(int mode, int64_t N, int64_t K, int64_t KR, int topk, int cu
     return false;
 }
 
+#ifndef W4A16_MOE_BATCHED_MT
+#define W4A16_MOE_BATCHED_MT 1
+#endif
+
+// Grouped experts for M tokens: the grouped-expert launch shape of the one-token form (8 lanes
+// with 3 chunks per item for rows of 72 chunks, else the widest lanes per row), persistent
+// work-groups of 8 waves, two per CU (one if LDS holds only one): 16 waves per CU is what the
+// kernel's registers allow, and fewer, longer-lived work-groups amortise the grouping set-up
+// (measured on MI355X over 2-16 tokens).
+bool make_moe_batched_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit,
+                           Plan *p)
+{
+    *p = Plan{};
+    if (M < 1 || M > 16 || topk < 1 || M * topk > 256 || N < 1 || K < 128 || K % 128 != 0 ||
+        cus < 1)
+        return false;
+    const int64_t cpr = K / 32;
+    int L = pow2_lanes(cpr), V = 1;
+    if (L == 8 && (cpr / 8) % 3 == 0)
+        V = 3;
+    if (L < 4)
+        return false;
+    const int64_t P = (int64_t)M * topk;
+    p->kind = PLAN_MOE_BATCHED;
+    p->MT = W4A16_MOE_BATCHED_MT;
+    p->L = L;
+    p->V = V;
+    p->U = 1;
+    p->moe = true;
+    p->threads = 512;
+    // Region A (activations, or the grouping scratch before them) + chunk offsets + the
+    // virtual entries (expert and MT pairs each) + their count.
+    const int64_t xs_bytes = (int64_t)M * K * 2;
+    const int64_t scratch = ((20 * P + 15) / 16) * 16;
+    p->lds_bytes = (xs_bytes > scratch ? xs_bytes : scratch) + (int64_t)M * cpr * 4 +
+                   4 * (P + P * W4A16_MOE_BATCHED_MT + 1);
+    if (p->lds_bytes > lds_limit)
+        return false;
+    int64_t per_cu = lds_limit / p->lds_bytes;
+    if (per_cu > 2)
+        per_cu = 2;
+    const int64_t R = 64 / L;
+    const int64_t most = (P * ((N + R - 1) / R) + 7) / 8;   // work-groups that could have work
+    p->blocks = (int64_t)cus * per_cu;
+    if (p->blocks > most)
+        p->blocks = most;
+    return p->blocks >= 1 && p->blocks < (1LL << 31);
+}
+
 int describe_plan(const Plan &p, char *buf, size_t len)
 {
     if (!buf || len == 0)
@@ -384,6 +433,11 @@ int describe_plan(const Plan &p, char *buf, size_t len)
                      "threads=%d blocks=%lld rows_per_block=%lld lds=%lld",
                      p.mode == PLAN_MODE_COMBINE ? "_moe_combine" : "", p.MT, p.L, p.V, p.U, p.threads, (long long)p.blocks,
                      (long long)p.rows_per_block, (long long)p.lds_bytes);
+    else if (p.kind == PLAN_MOE_BATCHED)
+        n = snprintf(buf, len,
+                     "moe_batched tokens_per_pass=%d lanes_per_row=%d chunks_per_item=%d "
+                     "threads=%d blocks=%lld lds=%lld",
+                     p.MT, p.L, p.V, p.threads, (long long)p.blocks, (long long)p.lds_bytes);
     else if (p.kind == PLAN_MFMA)
         n = snprintf(buf, len,
                      "mfma16x16x32%s tiles_per_wave=%d k_split=%d groups_per_item=%d threads=%d "

@@ -7,7 +7,8 @@
 
 namespace w4a16 {
 
-enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3 };
+enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3,
+                PLAN_MOE_BATCHED = 4 };
 
 // What the rows of a staged VALU launch are: one matrix, expert rows, the gate+up experts with
 // the SwiGLU epilogue, or the down experts summed with router weights.
@@ -33,6 +34,11 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
 // each instantiated for the SwiGLU gate+up form (lanes per row <= 32) and the combine form.
 #ifndef W4A16_TAIL_CONFIGS
 #define W4A16_TAIL_CONFIGS(X) X(8, 3) X(32, 1) X(16, 1) X(8, 1) X(4, 1)
+#endif
+
+// Grouped-expert kernels for M tokens with their own experts: X(lanes per row, chunks per item).
+#ifndef W4A16_MOE_BATCHED_CONFIGS
+#define W4A16_MOE_BATCHED_CONFIGS(X) X(8, 3) X(64, 1) X(32, 1) X(16, 1) X(8, 1) X(4, 1)
 #endif
 
 // Split-K kernels in the combine form of the expert tail: X(lanes per row, chunks per lane).
@@ -101,6 +107,11 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
 // covers the shape.
 bool make_tail_plan(int mode, int64_t N, int64_t K, int64_t KR, int topk, int cus,
                     int64_t lds_limit, Plan *p);
+
+// Grouped-expert GEMV of M tokens, each with topk experts (M * topk <= 256). Returns false when
+// the activations of the M tokens do not fit in LDS.
+bool make_moe_batched_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit,
+                           Plan *p);
 
 // Launch-shape override for tuning: keeps the caller's kernel choice, fills in grid and LDS.
 bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit,
