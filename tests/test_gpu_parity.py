@@ -147,6 +147,18 @@ def test_batched_every_m_ragged(M):
     within(Y[:, :N], ref, mag, f"batched M={M} {N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 300, 4096), (9, 2049, 1024), (16, 129, 1536), (5, 7, 256),
+                                   (12, 1000, 2304), (16, 4096, 2048), (6, 100, 384)])
+def test_batched_mfma_plans(M, N, K):
+    """Every MFMA form: whole-line loads with 2, 4 and 6 groups per item, rows below and above
+    one row block, and the operand-order forms."""
+    d = synthetic.dense(N=N, K=K, seed=M + N, M=M, config_id=803)
+    print(f"batched M={M} {N}x{K} plan={w.describe_plan(M, N, K)}", flush=True)
+    Y = host(w.gemv_batched(words(d.qweight), f16(d.scales), bf16(d.x)))
+    ref, mag = oracle.gemv_batched(d.qweight, d.scales, d.x, K)
+    within(Y, ref, mag, f"batched M={M} {N}x{K}")
+
+
 def test_batched_rows_match_single_token():
     N, K, M = 500, 8192, 16
     d = synthetic.dense(N=N, K=K, seed=9, M=M, config_id=802)

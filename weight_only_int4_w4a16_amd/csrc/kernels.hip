@@ -997,6 +997,13 @@ gemv_moe_batched_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict
 // partial sums are added through LDS in a fixed order.
 // Token slots past M read token M-1 (their outputs are never stored); rows past N re-read row
 // N-1 (never stored). Every load is unconditional.
+//
+// LINES (XLDS, one tile per wave, an even number of groups per item): a lane of the B operand
+// reads 16 bytes of one row, so an operand-order load covers 64 bytes of each of 16 rows (half
+// lines, the second half served by L2, with L1 tag conflicts). Instead each pair of groups --
+// one 128-byte line of every row -- is loaded by two whole-line instructions (lane l: row
+// 8h + l/8, chunk l%8 of the line), passed through a per-wave LDS slot, and read back in
+// operand order (lane (i, g) takes chunk g, then 4 + g, of row i).
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
@@ -1032,12 +1039,15 @@ __device__ __forceinline__ void load_scales(const char *p, uint16_t (&out)[GU])
     }
 }
 
-template <int T, int KS, bool XLDS, int GU, int WPB>
+template <int T, int KS, int XMODE, int GU, int WPB>
 __global__ void __launch_bounds__(64 * WPB)
 gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                  const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
                  int32_t M, int64_t N, int32_t K)
 {
+    constexpr bool XLDS = XMODE != 0;          // activations staged in LDS
+    constexpr bool LINES = XMODE == 2;         // whole-line weight loads permuted through LDS
+    static_assert(!LINES || (T == 1 && GU % 2 == 0), "line loads pair the groups of one tile");
     static_assert(WPB % KS == 0, "waves per block must be a multiple of the K split");
     constexpr int RG = WPB / KS;               // row groups (waves with distinct rows) per block
     constexpr int TROWS = 16 * T;              // rows per wave item
@@ -1078,6 +1088,15 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         const int64_t r0 = rb * RGT;
         return r0 + RGT <= N ? r0 : N - RGT;
     };
+    // Whole-line loads: instruction h of a line pair reads rows 8h + lane/8 of the wave's tile.
+    uint32_t loff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int r = rg * TROWS + 8 * h + (lane >> 3);
+        if (!full && r > N - 1)
+            r = (int)N - 1;
+        loff[h] = (uint32_t)((r * CPR + (lane & 7)) * 16);
+    }
     auto mma_group = [&](const uint4 (&wv)[T], const uint16_t (&sv)[T], const bf16x8_t xb[4],
                          f32x4_t off, f32x4_t (&acc)[T]) {
 #pragma unroll
@@ -1119,6 +1138,7 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         static_assert(KS == 1, "staged activations serve whole rows");
         uint4 *xl = lds;                                             // [GPR][4][64]
         float *offl = reinterpret_cast<float *>(lds + GPR * 256);   // [GPR][16]
+        uint4 *stage = lds + GPR * 260 + wave * GU * 64;             // LINES: [GU/2][2][64]
         // A flat sequence of (row block, run of GU groups) items for this work-group.
         const int cpr_items = GPR / GU;
         const bool active = blockIdx.x < n_rb;
@@ -1133,8 +1153,11 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
 #pragma unroll
             for (int t = 0; t < T; ++t) {
 #pragma unroll
-                for (int u = 0; u < GU; ++u)
-                    buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + woff[t] + 64 * u));
+                for (int u = 0; u < GU; ++u) {
+                    // LINES: buf.w[2p + h] holds instruction h of line pair p (whole lines)
+                    const uint32_t o = LINES ? loff[u & 1] + 128 * (u >> 1) : woff[t] + 64 * u;
+                    buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + o));
+                }
                 uint16_t sv[GU];
                 load_scales<GU>(sb + soff[t], sv);
 #pragma unroll
@@ -1181,6 +1204,27 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         int64_t cp_rb = rb_first;
         int cp_s = 0;
         auto compute = [&](const Buf &buf) {
+            uint4 wl[GU][T];
+            if constexpr (LINES) {
+                // Whole lines in, operand order out: lane (i, g) takes chunk g (even group) and
+                // 4 + g (odd group) of row i, held by lane 8 (i % 8) + ... of instruction i / 8.
+#pragma unroll
+                for (int u = 0; u < GU; ++u)
+                    stage[u * 64 + lane] = buf.w[u][0];
+                const int src = 8 * (i & 7) + g;
+                const int hh = i >> 3;
+#pragma unroll
+                for (int p2 = 0; p2 < GU / 2; ++p2) {
+                    wl[2 * p2][0] = stage[(2 * p2 + hh) * 64 + src];
+                    wl[2 * p2 + 1][0] = stage[(2 * p2 + hh) * 64 + src + 4];
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < GU; ++u)
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        wl[u][t] = buf.w[u][t];
+            }
 #pragma unroll
             for (int u = 0; u < GU; ++u) {
                 const int s = cp_s + u;
@@ -1190,7 +1234,7 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                     xb[j] = as_bf16x8(xl[(s * 4 + j) * 64 + lane]);
                 const float4 o4 = *reinterpret_cast<const float4 *>(offl + s * 16 + 4 * g);
                 const f32x4_t off = {o4.x, o4.y, o4.z, o4.w};
-                mma_group(buf.w[u], buf.s[u], xb, off, acc);
+                mma_group(wl[u], buf.s[u], xb, off, acc);
             }
             if (cp_s + GU == GPR) {
                 store(cp_rb, acc);
@@ -1362,10 +1406,10 @@ static hipError_t launch_moe_batched_t(const GemvArgs &a, const Plan &p, hipStre
                            args, (size_t)p.lds_bytes, stream);
 }
 
-template <int T, int KS, bool XLDS, int GU, int WPB>
+template <int T, int KS, int XMODE, int GU, int WPB>
 static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
-    auto kern = gemv_mfma_kernel<T, KS, XLDS, GU, WPB>;
+    auto kern = gemv_mfma_kernel<T, KS, XMODE, GU, WPB>;
     void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X, (void *)&a.ldx,
                     (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.M, (void *)&a.N,
                     (void *)&a.K};
@@ -1396,8 +1440,9 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
         return launch_splitk_t<1, L_, CL_, 1, true>(a, p, stream);
 
 #define W4A16_MFMA_CASE(T_, KS_, XL_, GU_, WPB_)                                             \
-    if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) && p.V == GU_ && p.threads == 64 * WPB_) \
-        return launch_mfma_t<T_, KS_, (XL_ != 0), GU_, WPB_>(a, p, stream);
+    if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) && p.lines == (XL_ == 2) &&         \
+        p.V == GU_ && p.threads == 64 * WPB_)                                                 \
+        return launch_mfma_t<T_, KS_, XL_, GU_, WPB_>(a, p, stream);
 
 #define W4A16_MOE_BATCHED_CASE(L_, V_)                                                       \
     if (p.L == L_ && p.V == V_)                                                              \

@@ -36,7 +36,7 @@ bool plan_instantiated(const Plan &p)
         return true;
 #define W4A16_MFMA_MATCH(T_, KS_, XL_, GU_, WPB_)                                            \
     if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) &&            \
-        p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))                             \
+        p.lines == (XL_ == 2) && p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))    \
         return true;
     W4A16_VALU_CONFIGS(W4A16_VALU_MATCH)
     W4A16_TAIL_CONFIGS(W4A16_TAIL_MATCH)
@@ -149,12 +149,15 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
             return false;
         if (p->V < 1 || gpr % p->KS != 0 || (gpr / p->KS) % p->V != 0 || (p->xlds && p->KS != 1))
             return false;
+        if (p->lines && (!p->xlds || p->T != 1 || p->V % 2 != 0))
+            return false;
         const int64_t rows_per_block = 16LL * p->T * (wpb / p->KS);
         const int64_t row_blocks = (N + rows_per_block - 1) / rows_per_block;
         if (p->xlds) {
             // 16 token slots of activation fragments (16 bytes per lane, word and group) plus
-            // one fp32 offset per (group, token).
-            p->lds_bytes = gpr * 4096 + gpr * 64;
+            // one fp32 offset per (group, token); with line loads, one 1 KiB staging slot per
+            // group of an item and wave.
+            p->lds_bytes = gpr * 4096 + gpr * 64 + (p->lines ? (int64_t)wpb * p->V * 1024 : 0);
             if (p->lds_bytes > lds_limit)
                 return false;
             int per_cu = blocks_per_cu;
@@ -284,6 +287,24 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     // come from global memory: two tiles per wave, K split over 4 (or 2, or 1) waves while that
     // keeps at least 2 work-groups per CU.
     const int64_t gpr = K / 128;
+    // Staged activations with whole-line weight loads (6, 4 or 2 groups per item, whichever
+    // divides the groups of a row and leaves the staging slots room in LDS), else staged
+    // activations with operand-order loads.
+    {
+        static const int gus[] = {6, 4, 2};
+        for (int gu : gus) {
+            Plan c{};
+            c.kind = PLAN_MFMA;
+            c.T = 1;
+            c.KS = 1;
+            c.V = gu;
+            c.xlds = true;
+            c.lines = true;
+            c.threads = 512;
+            if (gpr % gu == 0 && try_plan(c, 2, M, N, K, topk, cus, lds_limit, p))
+                return true;
+        }
+    }
     if (gpr * 4160 <= lds_limit / 2) {
         static const int gus[] = {6, 4, 2, 1};
         for (int gu : gus) {
@@ -442,8 +463,8 @@ int describe_plan(const Plan &p, char *buf, size_t len)
         n = snprintf(buf, len,
                      "mfma16x16x32%s tiles_per_wave=%d k_split=%d groups_per_item=%d threads=%d "
                      "blocks=%lld lds=%lld",
-                     p.xlds ? "_lds" : "", p.T, p.KS, p.V, p.threads, (long long)p.blocks,
-                     (long long)p.lds_bytes);
+                     p.lines ? "_lds_lines" : p.xlds ? "_lds" : "", p.T, p.KS, p.V, p.threads,
+                     (long long)p.blocks, (long long)p.lds_bytes);
     else
         n = snprintf(buf, len, "none");
     return n;

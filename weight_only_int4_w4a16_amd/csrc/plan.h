@@ -53,11 +53,12 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
     X(2, 64, 1, 4) X(3, 64, 1, 4) X(4, 64, 1, 4)
 #endif
 
-// MFMA kernels: X(16-row tiles per wave, waves splitting K, activations staged in LDS,
-// groups per item, waves per work-group).
+// MFMA kernels: X(16-row tiles per wave, waves splitting K, activations staged in LDS (1) and
+// weights loaded as whole lines (2), groups per item, waves per work-group).
 #ifndef W4A16_MFMA_CONFIGS
 #define W4A16_MFMA_CONFIGS(X)                                                                \
     X(1, 1, 1, 6, 8) X(1, 1, 1, 4, 8) X(1, 1, 1, 2, 8) X(1, 1, 1, 1, 8)                       \
+    X(1, 1, 2, 6, 8) X(1, 1, 2, 4, 8) X(1, 1, 2, 2, 8)                                        \
     X(2, 4, 0, 2, 4) X(2, 2, 0, 2, 4) X(2, 1, 0, 2, 4) X(1, 1, 0, 2, 4) X(1, 1, 0, 1, 4)
 #endif
 
@@ -66,6 +67,7 @@ struct Plan {
     int MT, L, V, U;   // VALU: tokens, lanes per row, chunks per lane per item, row steps per item
     int T, KS;         // MFMA: 16-row tiles per wave, waves splitting K (V: groups per item)
     bool xlds;         // MFMA: activations of all 16 token slots staged in LDS
+    bool lines;        // MFMA (staged activations): whole-line weight loads permuted via LDS
     bool moe;          // rows through expert ids (grouped and SwiGLU forms)
     int mode;          // PlanMode (staged VALU)
     int64_t kr;        // combine form: length of one weight row (K is the activation length)
