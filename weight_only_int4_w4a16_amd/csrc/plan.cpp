@@ -230,6 +230,84 @@ Plan splitk(int MT, int L, int CL, int U, bool moe)
 
 }  // namespace
 
+// MFMA forms for 2..16 tokens, in order of preference (launch-shape sweeps on MI355X):
+//  1. activations staged in LDS with whole-line weight loads, 8 waves of 16 rows per
+//     work-group, when there are enough row blocks to fill the chip (N/128 >= 0.8 * CUs) and the
+//     staging fits in LDS: tall matrices (163840 x 2304, 28672 x 4096);
+//  2. activations from global memory, two 16-row tiles per wave, K split over 4 waves, when that
+//     gives at least one work-group per CU (8192 x 8192, 14336 x 2048);
+//  3. activations from global memory, one tile per wave, K split over 8 waves, for short
+//     matrices with long rows (4096 x 14336, 2048 x 4096);
+//  4. staged activations with whole-line loads in 4-wave work-groups (4096 x 2304, small N);
+//  5. the remaining forms, which cover every K that is a multiple of 128.
+// Groups per item: even so that line pairs (or both 64-byte halves of a line) go together.
+static bool mfma_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, Plan *p)
+{
+    const int64_t gpr = K / 128;
+    auto lines = [&](int wpb, Plan *out) {
+        static const int gus[] = {6, 4, 2};
+        for (int gu : gus) {
+            Plan c{};
+            c.kind = PLAN_MFMA;
+            c.T = 1;
+            c.KS = 1;
+            c.V = gu;
+            c.xlds = true;
+            c.lines = true;
+            c.threads = 64 * wpb;
+            if (gpr % gu == 0 && try_plan(c, 2, M, N, K, 0, cus, lds_limit, out))
+                return true;
+        }
+        return false;
+    };
+    auto global = [&](int T, int KS, int GU, int wpb, Plan *out) {
+        Plan c{};
+        c.kind = PLAN_MFMA;
+        c.T = T;
+        c.KS = KS;
+        c.V = GU;
+        c.threads = 64 * wpb;
+        return gpr % (KS * GU) == 0 && try_plan(c, 1, M, N, K, 0, cus, lds_limit, out);
+    };
+    if (N / 128 >= (int64_t)cus * 4 / 5 && lines(8, p))
+        return true;
+    if (N / 32 >= cus && global(2, 4, 2, 4, p))
+        return true;
+    if (gpr % 16 == 0 && global(1, 8, 2, 8, p))
+        return true;
+    if (lines(4, p))
+        return true;
+    if (gpr * 4160 <= lds_limit / 2) {
+        static const int gus[] = {6, 4, 2, 1};
+        for (int gu : gus) {
+            Plan c{};
+            c.kind = PLAN_MFMA;
+            c.T = 1;
+            c.KS = 1;
+            c.V = gu;
+            c.xlds = true;
+            c.threads = 512;
+            if (gpr % gu == 0 && try_plan(c, 1, M, N, K, 0, cus, lds_limit, p))
+                return true;
+        }
+    }
+    static const int mf[][3] = {{2, 4, 2}, {2, 2, 2}, {2, 1, 2}, {1, 1, 2}, {1, 1, 1}};
+    for (int i = 0; i < (int)(sizeof(mf) / sizeof(mf[0])); ++i)
+        if (global(mf[i][0], mf[i][1], mf[i][2], 4, p))
+            return true;
+    return false;
+}
+
+// Whether 3 or 4 tokens are better served by the MFMA kernel than by the VALU ones: tall
+// matrices whose rows are not a multiple of 2048 values (the split-K VALU kernel's shapes) and
+// hold an even number of groups (whole-line loads), where decoding each weight once for all tokens on the matrix cores beats 3-4 dot products
+// per weight on the VALU (163840 x 2304 at 3-4 tokens: 38 us against 49-57 us).
+static bool mfma_for_few_tokens(int M, int64_t N, int64_t K, int cus)
+{
+    return M >= 3 && M <= 4 && K % 2048 != 0 && (K / 128) % 2 == 0 &&
+           N / 128 >= (int64_t)cus * 4 / 5;
+}
+
 bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit, Plan *p)
 {
     *p = Plan{};
@@ -274,70 +352,15 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
             return true;
         return try_plan(valu(1, L, 1, 1, moe), 6, M, N, K, topk, cus, lds_limit, p);
     }
+    if (!moe && mfma_for_few_tokens(M, N, K, cus) && mfma_plan(M, N, K, cus, lds_limit, p))
+        return true;
     if (M <= 4) {
         if (M == 2 && L == 8 && try_plan(valu(2, 8, 1, 2, false), 4, M, N, K, topk, cus, lds_limit, p))
             return true;
         if (try_plan(valu(M, L, 1, 1, false), M == 2 ? 4 : 8, M, N, K, topk, cus, lds_limit, p))
             return true;
     }
-    // MFMA. A lane's 16-byte weight load covers half of a 128-byte line of its row, so an item always
-    // spans an even number of groups when it can: both halves of every line are requested back to
-    // back. Activations staged in LDS when 16 token slots of K fit in half the LDS (persistent
-    // 8-wave work-groups, one 16-row tile per wave, 6/4/2 groups per item); otherwise activations
-    // come from global memory: two tiles per wave, K split over 4 (or 2, or 1) waves while that
-    // keeps at least 2 work-groups per CU.
-    const int64_t gpr = K / 128;
-    // Staged activations with whole-line weight loads (6, 4 or 2 groups per item, whichever
-    // divides the groups of a row and leaves the staging slots room in LDS), else staged
-    // activations with operand-order loads.
-    {
-        static const int gus[] = {6, 4, 2};
-        for (int gu : gus) {
-            Plan c{};
-            c.kind = PLAN_MFMA;
-            c.T = 1;
-            c.KS = 1;
-            c.V = gu;
-            c.xlds = true;
-            c.lines = true;
-            c.threads = 512;
-            if (gpr % gu == 0 && try_plan(c, 2, M, N, K, topk, cus, lds_limit, p))
-                return true;
-        }
-    }
-    if (gpr * 4160 <= lds_limit / 2) {
-        static const int gus[] = {6, 4, 2, 1};
-        for (int gu : gus) {
-            Plan c{};
-            c.kind = PLAN_MFMA;
-            c.T = 1;
-            c.KS = 1;
-            c.V = gu;
-            c.xlds = true;
-            c.threads = 512;
-            if (gpr % gu == 0 && try_plan(c, 1, M, N, K, topk, cus, lds_limit, p))
-                return true;
-        }
-    }
-    static const int mf[][3] = {{2, 4, 2}, {2, 2, 2}, {2, 1, 2}, {1, 1, 2}, {1, 1, 1}};
-    for (int i = 0; i < (int)(sizeof(mf) / sizeof(mf[0])); ++i) {
-        Plan c{};
-        c.kind = PLAN_MFMA;
-        c.T = mf[i][0];
-        c.KS = mf[i][1];
-        c.V = mf[i][2];
-        c.threads = 256;
-        if (gpr % c.KS != 0 || (gpr / c.KS) % c.V != 0)
-            continue;
-        const int64_t rows_per_block = 16LL * c.T * (4 / c.KS);
-        const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
-        const bool last = i == (int)(sizeof(mf) / sizeof(mf[0])) - 1;
-        if (blocks < 2LL * cus && c.KS == 1 && !last)
-            continue;
-        if (try_plan(c, 1, M, N, K, topk, cus, lds_limit, p))
-            return true;
-    }
-    return false;
+    return mfma_plan(M, N, K, cus, lds_limit, p);
 }
 
 // Expert tail. SwiGLU gate+up: the grouped-expert launch shape (8 lanes with 3 chunks per item for
