@@ -88,7 +88,8 @@ def graph_avg_us(torch, fn, n):
     with torch.cuda.graph(g):
         for i in range(n):
             fn(i)
-    g.replay()
+    for _ in range(3):          # untimed replays: graph upload and steady clocks
+        g.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -213,9 +213,11 @@ def test_valid_arguments_reach_the_device_check_only():
     (1, 2048, 2304, 8, "valu_moe"), (1, 5, 128, 0, "valu "), (1, 64, 65536, 0, "splitk "),
     (2, 8192, 8192, 0, "splitk "), (4, 163840, 2304, 0, "mfma16x16x32_lds_lines"),
     (2, 163840, 2304, 0, "valu "), (3, 100, 384, 0, "valu "), (4, 28672, 4096, 0, "splitk "),
-    (16, 8192, 8192, 0, "mfma16x16x32 tiles_per_wave=2 k_split=4"),
+    (16, 8192, 8192, 0, "mfma16x16x32_lines tiles_per_wave=2 k_split=4"),
+    (16, 14336, 2048, 0, "mfma16x16x32_lines tiles_per_wave=4 k_split=4"),
+    (16, 300, 2688, 0, "mfma16x16x32 tiles_per_wave=1 k_split=1 groups_per_item=1"),
     (16, 163840, 2304, 0, "mfma16x16x32_lds_lines"), (8, 8192, 8192, 0, "mfma"),
-    (16, 2048, 4096, 0, "mfma16x16x32 tiles_per_wave=1 k_split=8"),
+    (16, 2048, 4096, 0, "mfma16x16x32_lines tiles_per_wave=1 k_split=8"),
     (16, 4096, 2304, 0, "mfma16x16x32_lds_lines tiles_per_wave=1 k_split=1 groups_per_item=6 threads=256"),
 ])
 def test_default_dispatch(M, N, K, topk, kind):

@@ -1004,6 +1004,12 @@ gemv_moe_batched_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict
 // one 128-byte line of every row -- is loaded by two whole-line instructions (lane l: row
 // 8h + l/8, chunk l%8 of the line), passed through a per-wave LDS slot, and read back in
 // operand order (lane (i, g) takes chunk g, then 4 + g, of row i).
+//
+// GLINES (activations from global memory, an even number of groups per item): the same
+// whole-line weight loads for every tile, and the activation fragments loaded contiguously
+// (instruction j' of a group: lane (i, g) reads the 16 bytes 4j' + g of token i's 256-byte
+// group, so the four lanes of a token cover 64 contiguous bytes) and exchanged through LDS into
+// operand order (lane (i, g), word j comes from lane (i, j) of instruction g).
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
@@ -1045,9 +1051,11 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                  const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
                  int32_t M, int64_t N, int32_t K)
 {
-    constexpr bool XLDS = XMODE != 0;          // activations staged in LDS
+    constexpr bool XLDS = XMODE == 1 || XMODE == 2;   // activations staged in LDS
     constexpr bool LINES = XMODE == 2;         // whole-line weight loads permuted through LDS
+    constexpr bool GLINES = XMODE == 3;        // global activations, whole-line loads via LDS
     static_assert(!LINES || (T == 1 && GU % 2 == 0), "line loads pair the groups of one tile");
+    static_assert(!GLINES || GU % 2 == 0, "line loads pair the groups of an item");
     static_assert(WPB % KS == 0, "waves per block must be a multiple of the K split");
     constexpr int RG = WPB / KS;               // row groups (waves with distinct rows) per block
     constexpr int TROWS = 16 * T;              // rows per wave item
@@ -1088,15 +1096,17 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         const int64_t r0 = rb * RGT;
         return r0 + RGT <= N ? r0 : N - RGT;
     };
-    // Whole-line loads: instruction h of a line pair reads rows 8h + lane/8 of the wave's tile.
-    uint32_t loff[2];
+    // Whole-line loads: instruction h of a line pair reads rows 8h + lane/8 of tile t.
+    uint32_t loff[T][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int r = rg * TROWS + 8 * h + (lane >> 3);
-        if (!full && r > N - 1)
-            r = (int)N - 1;
-        loff[h] = (uint32_t)((r * CPR + (lane & 7)) * 16);
-    }
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int r = rg * TROWS + 16 * t + 8 * h + (lane >> 3);
+            if (!full && r > N - 1)
+                r = (int)N - 1;
+            loff[t][h] = (uint32_t)((r * CPR + (lane & 7)) * 16);
+        }
     auto mma_group = [&](const uint4 (&wv)[T], const uint16_t (&sv)[T], const bf16x8_t xb[4],
                          f32x4_t off, f32x4_t (&acc)[T]) {
 #pragma unroll
@@ -1155,7 +1165,7 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
 #pragma unroll
                 for (int u = 0; u < GU; ++u) {
                     // LINES: buf.w[2p + h] holds instruction h of line pair p (whole lines)
-                    const uint32_t o = LINES ? loff[u & 1] + 128 * (u >> 1) : woff[t] + 64 * u;
+                    const uint32_t o = LINES ? loff[0][u & 1] + 128 * (u >> 1) : woff[t] + 64 * u;
                     buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + o));
                 }
                 uint16_t sv[GU];
@@ -1263,10 +1273,14 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     } else {
         // One row block per work-group; KS waves split the groups of K into runs of GU.
         f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);           // [WPB][T][64]
+        // GLINES staging per wave after the reduction slots: weights [T][GU][64], then
+        // activation fragments [GU][4][64] (16 bytes each).
+        uint4 *stage_w = lds + (KS > 1 ? WPB * T * 64 : 0) + wave * (T + 4) * GU * 64;
+        uint4 *stage_x = stage_w + T * GU * 64;
         const int64_t rb = blockIdx.x;
         const int gpk = GPR / KS;
         const int n_items = gpk / GU;
-        const uint4 *xp = reinterpret_cast<const uint4 *>(X + (int64_t)tok * ldx) + 4 * g;
+        const uint4 *xp = reinterpret_cast<const uint4 *>(X + (int64_t)tok * ldx) + (GLINES ? g : 4 * g);
         int ld_s = ks * gpk;
         auto load = [&](Buf &buf) {
             const char *wb = wbase(rb, ld_s);
@@ -1275,12 +1289,14 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             for (int u = 0; u < GU; ++u)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    buf.x[u][j] = xp[16 * (ld_s + u) + j];
+                    buf.x[u][j] = xp[16 * (ld_s + u) + (GLINES ? 4 * j : j)];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
 #pragma unroll
-                for (int u = 0; u < GU; ++u)
-                    buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + woff[t] + 64 * u));
+                for (int u = 0; u < GU; ++u) {
+                    const uint32_t o = GLINES ? loff[t][u & 1] + 128 * (u >> 1) : woff[t] + 64 * u;
+                    buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + o));
+                }
                 uint16_t sv[GU];
                 load_scales<GU>(sb + soff[t], sv);
 #pragma unroll
@@ -1294,16 +1310,54 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         for (int t = 0; t < T; ++t)
             acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         auto compute = [&](const Buf &buf) {
+            uint4 wl[GU][T];
+            uint4 xr[GU][4];
+            if constexpr (GLINES) {
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+#pragma unroll
+                    for (int u = 0; u < GU; ++u)
+                        stage_w[(t * GU + u) * 64 + lane] = buf.w[u][t];
+#pragma unroll
+                for (int u = 0; u < GU; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        stage_x[(u * 4 + j) * 64 + lane] = buf.x[u][j];
+                const int src = 8 * (i & 7) + g;
+                const int hh = i >> 3;
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+#pragma unroll
+                    for (int p2 = 0; p2 < GU / 2; ++p2) {
+                        wl[2 * p2][t] = stage_w[(t * GU + 2 * p2 + hh) * 64 + src];
+                        wl[2 * p2 + 1][t] = stage_w[(t * GU + 2 * p2 + hh) * 64 + src + 4];
+                    }
+#pragma unroll
+                for (int u = 0; u < GU; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        xr[u][j] = stage_x[(u * 4 + g) * 64 + i + 16 * j];
+            } else {
+#pragma unroll
+                for (int u = 0; u < GU; ++u) {
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        wl[u][t] = buf.w[u][t];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        xr[u][j] = buf.x[u][j];
+                }
+            }
 #pragma unroll
             for (int u = 0; u < GU; ++u) {
                 bf16x8_t xb[4];
                 f32x4_t off = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    xb[j] = as_bf16x8(pair_activations(buf.x[u][j]));
+                    xb[j] = as_bf16x8(pair_activations(xr[u][j]));
                     off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], c136, off, 0, 0, 0);
                 }
-                mma_group(buf.w[u], buf.s[u], xb, -off, acc);
+                mma_group(wl[u], buf.s[u], xb, -off, acc);
             }
         };
         Buf bufA, bufB;
@@ -1440,8 +1494,8 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
         return launch_splitk_t<1, L_, CL_, 1, true>(a, p, stream);
 
 #define W4A16_MFMA_CASE(T_, KS_, XL_, GU_, WPB_)                                             \
-    if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) && p.lines == (XL_ == 2) &&         \
-        p.V == GU_ && p.threads == 64 * WPB_)                                                 \
+    if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ == 1 || XL_ == 2) &&                      \
+        p.lines == (XL_ >= 2) && p.V == GU_ && p.threads == 64 * WPB_)                        \
         return launch_mfma_t<T_, KS_, XL_, GU_, WPB_>(a, p, stream);
 
 #define W4A16_MOE_BATCHED_CASE(L_, V_)                                                       \

@@ -35,8 +35,8 @@ bool plan_instantiated(const Plan &p)
         p.mode == PLAN_MODE_COMBINE)                                                          \
         return true;
 #define W4A16_MFMA_MATCH(T_, KS_, XL_, GU_, WPB_)                                            \
-    if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ && p.xlds == (XL_ != 0) &&            \
-        p.lines == (XL_ == 2) && p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))    \
+    if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ && p.xlds == (XL_ == 1 || XL_ == 2) && \
+        p.lines == (XL_ >= 2) && p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))    \
         return true;
     W4A16_VALU_CONFIGS(W4A16_VALU_MATCH)
     W4A16_TAIL_CONFIGS(W4A16_TAIL_MATCH)
@@ -149,7 +149,7 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
             return false;
         if (p->V < 1 || gpr % p->KS != 0 || (gpr / p->KS) % p->V != 0 || (p->xlds && p->KS != 1))
             return false;
-        if (p->lines && (!p->xlds || p->T != 1 || p->V % 2 != 0))
+        if (p->lines && (p->V % 2 != 0 || (p->xlds && p->T != 1)))
             return false;
         const int64_t rows_per_block = 16LL * p->T * (wpb / p->KS);
         const int64_t row_blocks = (N + rows_per_block - 1) / rows_per_block;
@@ -169,7 +169,12 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
             const int64_t cap = (int64_t)cus * per_cu;
             p->blocks = row_blocks < cap ? row_blocks : cap;
         } else {
-            p->lds_bytes = p->KS > 1 ? (int64_t)wpb * p->T * 64 * 16 : 0;
+            // K-split partial sums, and with line loads a staging slot per wave for the
+            // weights (T x groups per item) and activation fragments (4 x groups per item).
+            p->lds_bytes = (p->KS > 1 ? (int64_t)wpb * p->T * 64 * 16 : 0) +
+                           (p->lines ? (int64_t)wpb * (p->T + 4) * p->V * 1024 : 0);
+            if (p->lds_bytes > lds_limit)
+                return false;
             p->blocks = row_blocks;
         }
         return p->blocks >= 1 && p->blocks < (1LL << 31);
@@ -234,10 +239,11 @@ Plan splitk(int MT, int L, int CL, int U, bool moe)
 //  1. activations staged in LDS with whole-line weight loads, 8 waves of 16 rows per
 //     work-group, when there are enough row blocks to fill the chip (N/128 >= 0.8 * CUs) and the
 //     staging fits in LDS: tall matrices (163840 x 2304, 28672 x 4096);
-//  2. activations from global memory, two 16-row tiles per wave, K split over 4 waves, when that
-//     gives at least one work-group per CU (8192 x 8192, 14336 x 2048);
-//  3. activations from global memory, one tile per wave, K split over 8 waves, for short
-//     matrices with long rows (4096 x 14336, 2048 x 4096);
+//  2. activations from global memory with whole-line weight and activation loads, K split over
+//     4 waves, four 16-row tiles per wave when that still fills the chip (14336 x 2048), else
+//     two (8192 x 8192);
+//  3. the same with one tile per wave and K split over 8 waves, for short matrices with long
+//     rows (4096 x 14336, 2048 x 4096);
 //  4. staged activations with whole-line loads in 4-wave work-groups (4096 x 2304, small N);
 //  5. the remaining forms, which cover every K that is a multiple of 128.
 // Groups per item: even so that line pairs (or both 64-byte halves of a line) go together.
@@ -260,20 +266,23 @@ static bool mfma_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, P
         }
         return false;
     };
-    auto global = [&](int T, int KS, int GU, int wpb, Plan *out) {
+    auto global = [&](int T, int KS, int GU, int wpb, bool whole_lines, Plan *out) {
         Plan c{};
         c.kind = PLAN_MFMA;
         c.T = T;
         c.KS = KS;
         c.V = GU;
+        c.lines = whole_lines;
         c.threads = 64 * wpb;
         return gpr % (KS * GU) == 0 && try_plan(c, 1, M, N, K, 0, cus, lds_limit, out);
     };
     if (N / 128 >= (int64_t)cus * 4 / 5 && lines(8, p))
         return true;
-    if (N / 32 >= cus && global(2, 4, 2, 4, p))
+    if (N / 64 >= (int64_t)cus * 4 / 5 && global(4, 4, 2, 4, true, p))
         return true;
-    if (gpr % 16 == 0 && global(1, 8, 2, 8, p))
+    if (N / 32 >= cus && global(2, 4, 2, 4, true, p))
+        return true;
+    if (gpr % 16 == 0 && global(1, 8, 2, 8, true, p))
         return true;
     if (lines(4, p))
         return true;
@@ -293,7 +302,7 @@ static bool mfma_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, P
     }
     static const int mf[][3] = {{2, 4, 2}, {2, 2, 2}, {2, 1, 2}, {1, 1, 2}, {1, 1, 1}};
     for (int i = 0; i < (int)(sizeof(mf) / sizeof(mf[0])); ++i)
-        if (global(mf[i][0], mf[i][1], mf[i][2], 4, p))
+        if (global(mf[i][0], mf[i][1], mf[i][2], 4, false, p))
             return true;
     return false;
 }
@@ -486,7 +495,8 @@ int describe_plan(const Plan &p, char *buf, size_t len)
         n = snprintf(buf, len,
                      "mfma16x16x32%s tiles_per_wave=%d k_split=%d groups_per_item=%d threads=%d "
                      "blocks=%lld lds=%lld",
-                     p.lines ? "_lds_lines" : p.xlds ? "_lds" : "", p.T, p.KS, p.V, p.threads,
+                     p.lines ? (p.xlds ? "_lds_lines" : "_lines") : p.xlds ? "_lds" : "", p.T,
+                     p.KS, p.V, p.threads,
                      (long long)p.blocks, (long long)p.lds_bytes);
     else
         n = snprintf(buf, len, "none");

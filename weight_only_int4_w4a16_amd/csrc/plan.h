@@ -53,13 +53,14 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
     X(2, 64, 1, 4) X(3, 64, 1, 4) X(4, 64, 1, 4)
 #endif
 
-// MFMA kernels: X(16-row tiles per wave, waves splitting K, activations staged in LDS (1) and
-// weights loaded as whole lines (2), groups per item, waves per work-group).
+// MFMA kernels: X(16-row tiles per wave, waves splitting K, activation mode, groups per item,
+// waves per work-group). Activation mode: 0 from global memory, 1 staged in LDS, 2 staged with
+// whole-line weight loads, 3 from global memory with whole-line weight and activation loads.
 #ifndef W4A16_MFMA_CONFIGS
 #define W4A16_MFMA_CONFIGS(X)                                                                \
     X(1, 1, 1, 6, 8) X(1, 1, 1, 4, 8) X(1, 1, 1, 2, 8) X(1, 1, 1, 1, 8)                       \
     X(1, 1, 2, 6, 8) X(1, 1, 2, 4, 8) X(1, 1, 2, 2, 8) X(1, 1, 2, 6, 4) X(1, 1, 2, 4, 4)      \
-    X(1, 1, 2, 2, 4) X(1, 8, 0, 2, 8)                                                        \
+    X(1, 1, 2, 2, 4) X(2, 4, 3, 2, 4) X(1, 8, 3, 2, 8) X(4, 4, 3, 2, 4)                      \
     X(2, 4, 0, 2, 4) X(2, 2, 0, 2, 4) X(2, 1, 0, 2, 4) X(1, 1, 0, 2, 4) X(1, 1, 0, 1, 4)
 #endif
 
