@@ -160,7 +160,8 @@ w4a16_status_t w4a16_moe_down_combine(const uint32_t *qweight, const uint16_t *s
  *   quotient and ties to even; q = 0 for a group whose s is zero.
  *   w bf16 bits, N rows of stride ldw elements (ldw >= K, ldw % 8 == 0, w 16-byte aligned);
  *   qweight uint32[N][K/8] and scales fp16 bits [N][K/128] (outputs, fully overwritten).
- *   1 <= N <= 2^31 - 1; 128 <= K <= 2^20, K % 128 == 0. Inputs must be finite.
+ *   1 <= N <= 2^31 - 1; 128 <= K <= 2^20, K % 128 == 0; N * K / 128 < 2^32. Inputs must be
+ *   finite.
  */
 w4a16_status_t w4a16_quantize_pack(const uint16_t *w, int64_t ldw, uint32_t *qweight,
                                    uint16_t *scales, int64_t N, int64_t K, int32_t group_size,

@@ -71,6 +71,26 @@ def test_quantize_special_groups():
     assert list(codes) == [7, -7, 0, 2, 2, 4, 4, 6, 6, 0, -2, -2, -4, -4, -6, -6]
 
 
+def test_quantize_near_ties_bit_exact():
+    """Values at and next to w / s = k + 1/2 for scales that are not powers of two: the kernel's
+    reciprocal estimate must defer to the exact quotient wherever rounding is close."""
+    rng = np.random.default_rng(21)
+    K = 128 * 64
+    rows = []
+    for s16 in rng.integers(0x2800, 0x5000, size=24, dtype=np.uint16):
+        s = float(np.array([s16], np.uint16).view(np.float16)[0])
+        k = rng.integers(-8, 8, size=K).astype(np.float64)
+        jitter = rng.choice([-2, -1, 0, 1, 2], size=K) * 2.0 ** -7
+        vals = ((k + 0.5 + jitter * np.abs(k + 0.5) * 2.0 ** -1) * s).astype(np.float32)
+        vals.reshape(-1, 128)[:, 0] = np.float32(7.0 * s)         # amax 7 s in every group
+        rows.append(vals)
+    a = np.stack(rows)
+    bits = (a.view(np.uint32) >> 16).astype(np.uint16)
+    qw, sc = run(bits, K)
+    rq, rs = oracle.quantize_pack(bits, K)
+    assert np.array_equal(sc, rs) and np.array_equal(qw, rq)
+
+
 def test_quantize_then_gemv_matches_oracle():
     """The quantised matrix feeds the GEMV: GPU quantise + GPU GEMV against the oracle's
     quantisation and GEMV (identical operands, so the GEMV tolerance applies)."""

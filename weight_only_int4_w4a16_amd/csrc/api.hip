@@ -229,7 +229,7 @@ w4a16_status_t w4a16_quantize_pack(const uint16_t *w, int64_t ldw, uint32_t *qwe
     if (group_size != W4A16_GROUP_SIZE)
         return W4A16_ERR_BAD_GROUP;
     if (N < 1 || N > kMaxN || K < W4A16_GROUP_SIZE || K % W4A16_GROUP_SIZE != 0 ||
-        K > kMaxKBatched || ldw < K)
+        K > kMaxKBatched || ldw < K || N * (K / W4A16_GROUP_SIZE) > (int64_t)0xFFFFFFFFLL)
         return W4A16_ERR_BAD_SHAPE;
     if (!aligned(w, 16) || ldw % 8 != 0 || !aligned(qweight, 4) || !aligned(scales, 2))
         return W4A16_ERR_MISALIGNED;
