@@ -144,6 +144,7 @@ def quant(w_=A, ldw=256, qw=A, sc=A, N=64, K=256, G=128):
     (dict(N=0), SHAPE), (dict(K=200), SHAPE), (dict(K=0), SHAPE), (dict(ldw=128), SHAPE),
     (dict(K=(1 << 20) + 128, ldw=(1 << 20) + 128), SHAPE), (dict(w_=A + 8), ALIGN),
     (dict(ldw=260), ALIGN), (dict(qw=A + 2), ALIGN), (dict(sc=A + 1), ALIGN),
+    (dict(N=1 << 24, K=1 << 20, ldw=1 << 20), SHAPE),
 ])
 def test_quantize_validation(kw, status):
     assert quant(**kw) == status
