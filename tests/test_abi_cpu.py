@@ -241,3 +241,20 @@ def test_describe_rejects_bad_shapes():
     for args in ((0, 10, 128), (17, 10, 128), (1, 0, 128), (1, 10, 100), (2, 10, 128, 4)):
         with pytest.raises(w.W4A16Error):
             w.describe_plan(*args)
+
+
+def test_binding_refuses_host_tensors_and_wrong_dtypes():
+    """The Python layer checks dtypes, devices and ranks before calling the library."""
+    import torch
+    q = torch.zeros((4, 16), dtype=torch.int32)
+    s = torch.zeros((4, 1), dtype=torch.float16)
+    x = torch.zeros(128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        w.gemv(q, s, x)                       # host tensors
+    with pytest.raises(TypeError, match="qweight"):
+        w.gemv(q.float(), s, x)
+    for args in ((q, s.float(), x), (q, s, x.half()), (q.reshape(-1), s, x)):
+        with pytest.raises((TypeError, ValueError)):
+            w.gemv(*args)
+    with pytest.raises(TypeError, match="qweight"):
+        w.moe_gemv(q.reshape(1, 4, 16).float(), s.reshape(1, 4, 1), torch.zeros(2), x)
