@@ -226,7 +226,8 @@ def main():
 
     if not args.no_configs:
         out["per_workload"] = per_workload(torch, np, w, synthetic, dev,
-                                           props.multi_processor_count)
+                                           props.multi_processor_count,
+                                           with_oracle=not args.no_cpu_baseline)
         ref = out["per_workload"]["c3a_M1"]
         if "stream_read_us" in ref:
             # the plain streaming read of the same bytes, the practical ceiling of this kernel
@@ -281,7 +282,22 @@ def stream_ceiling_us(torch, w, dev, nbytes, R, cus):
     return best
 
 
-def per_workload(torch, np, w, synthetic, dev, cus):
+def single_call_us(torch, call, reps=21):
+    """Median µs of one eager call between two events, synchronising after each (latency
+    context: includes the launch, unlike the graph-timed numbers)."""
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    return sorted(times)[reps // 2]
+
+
+def per_workload(torch, np, w, synthetic, dev, cus, with_oracle=False):
     """µs per call and GB/s for every workload shape (graph-timed, rotated copies), with the
     same call on one cache-resident copy and the plain streaming-read ceiling over the same
     number of bytes, rotated the same way."""
@@ -322,6 +338,7 @@ def per_workload(torch, np, w, synthetic, dev, cus):
             n = max(2 * R, 64)
             stats = graph_replay_stats(torch, fn, n, 10)
             warm, _, _ = graph_replay_stats(torch, lambda i: fn(0), 64, 5)
+            single = single_call_us(torch, lambda: fn(0))
             b = synthetic.algorithmic_bytes(d.N, d.K, M)
             del cp
             torch.cuda.empty_cache()
@@ -329,6 +346,11 @@ def per_workload(torch, np, w, synthetic, dev, cus):
                 ceilings[b] = stream_ceiling_us(torch, w, dev, b, rot(b), cus)
             record(f"{name}_M{M}", d.N, d.K, M, b, stats, warm, ceilings[b],
                    w.describe_plan(M, d.N, d.K, 0, cus))
+            res[f"{name}_M{M}"]["us_single_call_not_graphed"] = round(single, 3)
+            if with_oracle:
+                ous = oracle_us(d, M, rows=512)
+                res[f"{name}_M{M}"]["oracle_us_1_core"] = round(ous, 1)
+                res[f"{name}_M{M}"]["oracle_GB_s"] = round(b / ous / 1e3, 4)
     m = synthetic.config("c4", 0)
     qw = torch.from_numpy(m.qweight.view(np.int32)).to(dev)
     sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
@@ -536,7 +558,40 @@ def cpu_baseline(da, db, bytes_per_step, target_s):
             "cores": 1, "kind": "oracle",
             "sample": f"{steps} whole steps (28672x4096 + 4096x14336 GEMV, every row), "
                       f"{el:.1f} s, single-threaded C oracle in float64",
-            "ms_per_step": round(el / steps * 1e3, 1)}
+            "ms_per_step": round(el / steps * 1e3, 1),
+            "host": host_description()}
+
+
+def host_description():
+    """CPU model and the number of cores the process may use (the oracle uses one)."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count()
+    return {"cpu": model, "cores_available": avail}
+
+
+def oracle_us(d, M, rows):
+    """µs of the CPU oracle for one call of workload d, timed on a row sample and scaled."""
+    import numpy as np
+    import oracle
+    orc = oracle.default()
+    sample = np.arange(0, d.N, max(1, d.N // rows))
+    t0 = time.perf_counter()
+    if M == 1:
+        orc.gemv(d.qweight, d.scales, d.x[0], d.K, rows=sample)
+    else:
+        orc.gemv_batched(d.qweight, d.scales, d.x, d.K, rows=sample)
+    return (time.perf_counter() - t0) * 1e6 * d.N / sample.size
 
 
 if __name__ == "__main__":
