@@ -32,17 +32,19 @@ METRIC = "W4A16 GEMV achieved HBM GB/s (% of MI355X peak) and µs/call at M=1"
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_28672x4096.json")
-# The sources that define the GEMV kernels and their launch shapes (not the validation layer):
-# a recorded traffic measurement stays valid while these are unchanged.
+# The sources that define the GEMV kernels and their template instances (not the validation or
+# dispatch layers). A recorded traffic measurement stays valid while these and the launch plan
+# of the measured kernel (its describe_plan text) are unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "weight_only_int4_w4a16_amd", "csrc", f)
-                  for f in ("kernels.hip", "plan.cpp", "plan.h")]
+                  for f in ("kernels.hip", "plan.h")]
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(plan_text: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(f, "rb") as fh:
             h.update(fh.read())
+    h.update(plan_text.encode())
     return h.hexdigest()[:16]
 
 
@@ -178,7 +180,8 @@ def main():
     down_us, _ = graph_avg_us(torch, lambda i: w.gemv(copies[i % R][2], copies[i % R][3], xb1,
                                                        out=yb), args.steps)
     achieved = bytes_a / (gate_us * 1e-6) / 1e9
-    digest = kernel_source_digest()
+    plan_a = w.describe_plan(1, da.N, da.K, 0, props.multi_processor_count)
+    digest = kernel_source_digest(plan_a)
     traffic = traffic_for(digest, bytes_a)
 
     out = {
@@ -205,7 +208,7 @@ def main():
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "us_per_call": {"gate_up_28672x4096": round(gate_us, 3),
                             "down_4096x14336": round(down_us, 3)},
-            "plans": {"gate_up": w.describe_plan(1, da.N, da.K, 0, props.multi_processor_count),
+            "plans": {"gate_up": plan_a,
                       "down": w.describe_plan(1, db.N, db.K, 0, props.multi_processor_count)},
             "device": f"{props.name} {getattr(props, 'gcnArchName', '')} "
                       f"{props.multi_processor_count} CUs",

@@ -122,6 +122,7 @@ def test_deterministic_across_calls_and_streams():
 @pytest.mark.parametrize("N,K", [
     (1, 128), (3, 256), (17, 384), (64, 1152), (129, 2048), (1000, 2304), (257, 4096),
     (70, 8192), (33, 14336), (5, 65536), (2049, 1024), (4096, 2048), (9000, 2048),
+    (300, 3072), (1000, 7168), (9000, 5120), (5000, 1536),
 ])
 def test_gemv_small_shapes(N, K):
     d = synthetic.dense(N=N, K=K, seed=N + K, config_id=800)

@@ -353,7 +353,17 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
             try_plan(splitk(1, 64, 4, 2, false), 1, M, N, K, topk, cus, lds_limit, p))
             return true;
     }
+    // One token, rows of 32k chunks that are not a multiple of 64 (K = 3072, 5120, 7168): split
+    // K over 32 lanes, 2 chunks in flight per lane (4096 x 7168: 5.2 us against 6.6 us staged;
+    // 16384 x 3072: 6.7 against 7.4).
+    if (!moe && M == 1 && !k2048 && cpr % 32 == 0 && cpr >= 96 &&
+        try_plan(splitk(1, 32, 1, 2, false), rows < 8192 ? 2 : 4, M, N, K, topk, cus, lds_limit, p))
+        return true;
     if (M == 1) {
+        // rows of 48 chunks (K = 1536): 8 lanes with 3 chunks per item, like rows of 72 chunks
+        if (!moe && L == 16 && (cpr / 8) % 3 == 0 &&
+            try_plan(valu(1, 8, 3, 1, false), 4, M, N, K, topk, cus, lds_limit, p))
+            return true;
         if (L == 8 && (cpr / 8) % 3 == 0 &&
             try_plan(valu(1, 8, 3, 1, moe), moe ? 8 : 2, M, N, K, topk, cus, lds_limit, p))
             return true;
