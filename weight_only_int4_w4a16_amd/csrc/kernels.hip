@@ -1025,29 +1025,45 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return as_bf16x8(v.x, v.y, v.z, v.w); }
 
+// Scale words of an item: with GU even, dword k holds the fp16 scales of groups 2k (low half) and
+// 2k + 1 (high half); with GU odd, word k holds group k's scale in its low half.
+template <int GU>
+constexpr int mfma_scale_words() { return GU % 2 == 0 ? GU / 2 : GU; }
+
 template <int T, int GU, bool XLDS>
 struct MfmaBuf {
     uint4 w[GU][T];
-    uint16_t s[GU][T];
+    uint32_t s[mfma_scale_words<GU>()][T];   // raw scale words, split only where they are used
     uint4 x[XLDS ? 1 : GU][4];     // activation fragments (global-memory mode only)
 };
 
 // The GU scales of one row for groups s..s+GU-1. With GU even (and so the group count of a row
-// even, and s even) they are 4-byte aligned and come in GU/2 dword loads.
+// even, and s even) they are 4-byte aligned and come in GU/2 dword loads. The words are kept
+// whole: splitting a half off right after the load would make that point wait for the load.
 template <int GU>
-__device__ __forceinline__ void load_scales(const char *p, uint16_t (&out)[GU])
+__device__ __forceinline__ void load_scales(const char *p, uint32_t (&out)[mfma_scale_words<GU>()])
 {
     if constexpr (GU % 2 == 0) {
 #pragma unroll
-        for (int k = 0; k < GU / 2; ++k) {
-            const uint32_t v = reinterpret_cast<const uint32_t *>(p)[k];
-            out[2 * k] = (uint16_t)(v & 0xFFFFu);
-            out[2 * k + 1] = (uint16_t)(v >> 16);
-        }
+        for (int k = 0; k < GU / 2; ++k)
+            out[k] = reinterpret_cast<const uint32_t *>(p)[k];
     } else {
 #pragma unroll
         for (int k = 0; k < GU; ++k)
             out[k] = reinterpret_cast<const uint16_t *>(p)[k];
+    }
+}
+
+// Scale of group u of an item from its raw words.
+template <int GU>
+__device__ __forceinline__ float mfma_scale(const uint32_t *words, int u)
+{
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    if constexpr (GU % 2 == 0) {
+        const h2_t h = __builtin_bit_cast(h2_t, words[u >> 1]);
+        return (float)((u & 1) ? h.y : h.x);
+    } else {
+        return (float)__builtin_bit_cast(h2_t, words[u]).x;
     }
 }
 
@@ -1113,7 +1129,7 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 r = (int)N - 1;
             loff[t][h] = (uint32_t)((r * CPR + (lane & 7)) * 16);
         }
-    auto mma_group = [&](const uint4 (&wv)[T], const uint16_t (&sv)[T], const bf16x8_t xb[4],
+    auto mma_group = [&](const uint4 (&wv)[T], const float (&scv)[T], const bf16x8_t xb[4],
                          f32x4_t off, f32x4_t (&acc)[T]) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
@@ -1124,10 +1140,9 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             for (int j = 0; j < 4; ++j)
                 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     xb[j], as_bf16x8(p[j][0], p[j][1], p[j][2], p[j][3]), d, 0, 0, 0);
-            const float scv = half_bits_to_float(sv[t]);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                acc[t][r] = fmaf(scv, d[r], acc[t][r]);
+                acc[t][r] = fmaf(scv[t], d[r], acc[t][r]);
         }
     };
     auto store = [&](int64_t rb, const f32x4_t (&acc)[T]) {
@@ -1174,11 +1189,11 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                     const uint32_t o = LINES ? loff[0][u & 1] + 128 * (u >> 1) : woff[t] + 64 * u;
                     buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + o));
                 }
-                uint16_t sv[GU];
+                uint32_t sv[mfma_scale_words<GU>()];
                 load_scales<GU>(sb + soff[t], sv);
 #pragma unroll
-                for (int u = 0; u < GU; ++u)
-                    buf.s[u][t] = sv[u];
+                for (int k = 0; k < mfma_scale_words<GU>(); ++k)
+                    buf.s[k][t] = sv[k];
             }
             const bool wrap = ld_s + GU == GPR;
             ld_s = wrap ? 0 : ld_s + GU;
@@ -1250,7 +1265,16 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                     xb[j] = as_bf16x8(xl[(s * 4 + j) * 64 + lane]);
                 const float4 o4 = *reinterpret_cast<const float4 *>(offl + s * 16 + 4 * g);
                 const f32x4_t off = {o4.x, o4.y, o4.z, o4.w};
-                mma_group(wl[u], buf.s[u], xb, off, acc);
+                float scv[T];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    uint32_t sw[mfma_scale_words<GU>()];
+#pragma unroll
+                    for (int k = 0; k < mfma_scale_words<GU>(); ++k)
+                        sw[k] = buf.s[k][t];
+                    scv[t] = mfma_scale<GU>(sw, u);
+                }
+                mma_group(wl[u], scv, xb, off, acc);
             }
             if (cp_s + GU == GPR) {
                 store(cp_rb, acc);
@@ -1288,14 +1312,16 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         const int n_items = gpk / GU;
         const uint4 *xp = reinterpret_cast<const uint4 *>(X + (int64_t)tok * ldx) + (GLINES ? g : 4 * g);
         int ld_s = ks * gpk;
+        const int s_last = ks * gpk + (n_items - 1) * GU;   // loads past the slice re-read its last item
         auto load = [&](Buf &buf) {
-            const char *wb = wbase(rb, ld_s);
-            const char *sb = sbase(rb, ld_s);
+            const int s_ = ld_s < s_last ? ld_s : s_last;
+            const char *wb = wbase(rb, s_);
+            const char *sb = sbase(rb, s_);
 #pragma unroll
             for (int u = 0; u < GU; ++u)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    buf.x[u][j] = xp[16 * (ld_s + u) + (GLINES ? 4 * j : j)];
+                    buf.x[u][j] = xp[16 * (s_ + u) + (GLINES ? 4 * j : j)];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
 #pragma unroll
@@ -1303,11 +1329,11 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                     const uint32_t o = GLINES ? loff[t][u & 1] + 128 * (u >> 1) : woff[t] + 64 * u;
                     buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + o));
                 }
-                uint16_t sv[GU];
+                uint32_t sv[mfma_scale_words<GU>()];
                 load_scales<GU>(sb + soff[t], sv);
 #pragma unroll
-                for (int u = 0; u < GU; ++u)
-                    buf.s[u][t] = sv[u];
+                for (int k = 0; k < mfma_scale_words<GU>(); ++k)
+                    buf.s[k][t] = sv[k];
             }
             ld_s += GU;
         };
@@ -1363,25 +1389,39 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                     xb[j] = as_bf16x8(pair_activations(xr[u][j]));
                     off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], c136, off, 0, 0, 0);
                 }
-                mma_group(wl[u], buf.s[u], xb, -off, acc);
+                float scv[T];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    uint32_t sw[mfma_scale_words<GU>()];
+#pragma unroll
+                    for (int k = 0; k < mfma_scale_words<GU>(); ++k)
+                        sw[k] = buf.s[k][t];
+                    scv[t] = mfma_scale<GU>(sw, u);
+                }
+                mma_group(wl[u], scv, xb, -off, acc);
             }
         };
-        Buf bufA, bufB;
-        load(bufA);
+        // A ring of RING item buffers: the loads of item it + RING - 1 are issued before item it is
+        // computed. The loop is unrolled by RING so every buffer index is a constant. Two buffers:
+        // these forms hold 16 token slots of activation fragments per item in registers, and a
+        // third buffer makes the compiler spill them (measured slower on every shape).
+        constexpr int RING = 2;
+        Buf ring[RING];
+#pragma unroll
+        for (int r = 0; r < RING - 1; ++r)
+            load(ring[r]);
         int it = 0;
-        for (; it + 2 < n_items; it += 2) {
-            load(bufB);
-            compute(bufA);
-            load(bufA);
-            compute(bufB);
+        for (; it + RING <= n_items; it += RING) {
+#pragma unroll
+            for (int r = 0; r < RING; ++r) {
+                load(ring[(r + RING - 1) % RING]);
+                compute(ring[r]);
+            }
         }
-        if (it + 1 < n_items) {
-            load(bufB);
-            compute(bufA);
-            compute(bufB);
-        } else {
-            compute(bufA);
-        }
+#pragma unroll
+        for (int r = 0; r < RING - 1; ++r)
+            if (it + r < n_items)
+                compute(ring[r]);
         if (KS > 1) {
             if (ks != 0) {
 #pragma unroll
