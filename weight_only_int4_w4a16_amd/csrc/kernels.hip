@@ -322,14 +322,16 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     // back to end at the last row (rows computed twice get identical bits); with fewer rows than
     // one block the lane rows are clamped instead.
     const bool full = rows_total >= ROWS;
+    // Lane row of row step u (u may be a run-time value: it is recomputed, not indexed, so no
+    // per-lane array has to live in scratch memory).
+    auto lane_row = [&](int u) -> int {
+        const int r = u * R + rr;
+        return (!full && r > rows_total - 1) ? (int)rows_total - 1 : r;
+    };
     uint32_t woff[U], soff[U];
-    int lrow[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        int r = u * R + rr;
-        if (!full && r > rows_total - 1)
-            r = (int)rows_total - 1;
-        lrow[u] = r;
+        const int r = lane_row(u);
         woff[u] = (uint32_t)((r * CPRW + pr) * 16);
         soff[u] = (uint32_t)((r * GPRW + (pr >> 2)) * 2);
     }
@@ -493,7 +495,7 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             const int u = fold_rows<L, U>(v, pr);
             if ((pr & (L / U - 1)) == 0) {
                 const int64_t vrow =
-                    MODE == VALU_MOE ? st * ROWS + u * R + rr : st_row0(st) + lrow[u];
+                    MODE == VALU_MOE ? st * ROWS + u * R + rr : st_row0(st) + lane_row(u);
                 if (vrow < rows_total) {
                     bool zero = false;
                     if (MODE == VALU_MOE) {
@@ -612,14 +614,15 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
     // back to end at its last row (rows computed twice get identical bits), and a block with fewer
     // rows than one item clamps the lane rows instead.
     const bool full = rcount >= ROWS;
+    // Lane row of row step u (recomputed for a run-time u rather than indexed).
+    auto lane_row = [&](int u) -> int {
+        const int r = u * R + rr;
+        return (!full && r > rcount - 1) ? rcount - 1 : r;
+    };
     uint32_t woff[U], soff[U];
-    int lrow[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        int r = u * R + rr;
-        if (!full && r > rcount - 1)
-            r = rcount - 1;
-        lrow[u] = r;
+        const int r = lane_row(u);
         woff[u] = (uint32_t)((r * CPR + pr) * 16);
         soff[u] = (uint32_t)((r * GPR + (pr >> 2)) * 2);
     }
@@ -726,7 +729,7 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
                 v[u] = acc[u][t];
             const int u = fold_rows<L, U>(v, pr);
             if ((pr & (L / U - 1)) == 0) {
-                const int lr = item_row0(cp_item) + lrow[u];
+                const int lr = item_row0(cp_item) + lane_row(u);
                 red[((int64_t)t * rows_per_block + lr) * W + wave] = v[0];
             }
         }

@@ -364,8 +364,10 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
         if (!moe && L == 16 && (cpr / 8) % 3 == 0 &&
             try_plan(valu(1, 8, 3, 1, false), 4, M, N, K, topk, cus, lds_limit, p))
             return true;
+        // 8 lanes x 3 chunks per item (rows of 72 chunks, K = 2304). Dense: 6 work-groups per
+        // CU (163840 x 2304: 31.1 us against 32.1 us with 2, same box).
         if (L == 8 && (cpr / 8) % 3 == 0 &&
-            try_plan(valu(1, 8, 3, 1, moe), moe ? 8 : 2, M, N, K, topk, cus, lds_limit, p))
+            try_plan(valu(1, 8, 3, 1, moe), moe ? 8 : 6, M, N, K, topk, cus, lds_limit, p))
             return true;
         if (L == 8 && try_plan(valu(1, 8, 1, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
             return true;
