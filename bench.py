@@ -84,15 +84,33 @@ def rotated(torch, t, R):
     return [big[r] for r in range(R)]
 
 
+WARM_MS = 50.0
+
+
+def warm_graph(torch, g, min_ms=WARM_MS):
+    """Untimed replays of g until at least min_ms of GPU time has passed (at least 3). On
+    MI355X the first ~25 ms of work on freshly set-up buffers run 2-10 % slower than the steady
+    state (interleaved repeats of the same graph agree to 0.1-0.3 % after that), so every timed
+    replay follows such a warm-up."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(max(2, int(min_ms / one) + 1)):
+        g.replay()
+    torch.cuda.synchronize()
+
+
 def graph_avg_us(torch, fn, n):
     """Average µs per fn() call over a HIP graph of n back-to-back calls (events on its stream)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(n):
             fn(i)
-    for _ in range(3):          # untimed replays: graph upload and steady clocks
-        g.replay()
-    torch.cuda.synchronize()
+    warm_graph(torch, g)        # untimed replays: graph upload and steady clocks
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -249,8 +267,7 @@ def graph_replay_stats(torch, fn, n, reps):
     with torch.cuda.graph(g):
         for i in range(n):
             fn(i)
-    g.replay()
-    torch.cuda.synchronize()
+    warm_graph(torch, g)
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev[0].record(stream)

@@ -215,8 +215,17 @@ def test_valid_arguments_reach_the_device_check_only():
     (1, 14336, 2048, 0, "valu tokens=1 lanes_per_row=32 chunks_per_item=2"),
     (1, 4096, 14336, 0, "splitk "), (1, 8192, 8192, 0, "splitk "), (1, 163840, 2304, 0, "valu "),
     (1, 2048, 2304, 8, "valu_moe"), (1, 5, 128, 0, "valu "), (1, 64, 65536, 0, "splitk "),
-    (2, 8192, 8192, 0, "splitk "), (4, 163840, 2304, 0, "mfma16x16x32_lds_lines"),
-    (2, 163840, 2304, 0, "valu "), (3, 100, 384, 0, "valu "), (4, 28672, 4096, 0, "splitk "),
+    (2, 8192, 8192, 0, "splitk "),
+    (4, 163840, 2304, 0, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=3 row_steps=1 "
+                         "blocks_per_row=8"),
+    (2, 163840, 2304, 0, "mfma4x4x4_splitk token_groups=1"),
+    (8, 163840, 2304, 0, "mfma16x16x32_lds_lines"), (3, 100, 384, 0, "valu "),
+    (4, 28672, 4096, 0, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=2 row_steps=2 "
+                        "blocks_per_row=16"),
+    (3, 8192, 8192, 0, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=2"),
+    (8, 4096, 14336, 0, "mfma4x4x4_splitk token_groups=2 chunks_per_lane=4"),
+    (5, 7, 256, 0, "mfma4x4x4_splitk token_groups=2 chunks_per_lane=1 row_steps=2 blocks_per_row=8"),
+    (8, 14336, 2048, 0, "mfma16x16x32_lines"), (2, 28672, 4096, 0, "splitk "),
     (16, 8192, 8192, 0, "mfma16x16x32_lines tiles_per_wave=2 k_split=4"),
     (16, 14336, 2048, 0, "mfma16x16x32_lines tiles_per_wave=4 k_split=4"),
     (16, 300, 2688, 0, "mfma16x16x32 tiles_per_wave=1 k_split=1 groups_per_item=1"),

@@ -163,6 +163,23 @@ def test_batched_mfma_plans(M, N, K):
     within(Y, ref, mag, f"batched M={M} {N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 5000, 2304), (3, 333, 4096), (4, 20001, 4096), (4, 33, 14336),
+                                   (3, 1000, 2048), (4, 999, 1024), (5, 77, 2304), (6, 4096, 14336),
+                                   (8, 1500, 8192), (7, 3, 4096), (8, 8192, 512), (2, 17, 256),
+                                   (3, 16384, 2304), (6, 1, 2304)])
+def test_batched_mfma4_plans(M, N, K):
+    """The 4x4x4-MFMA split-K kernel: 16 and 8 blocks per row group, one and two token groups
+    (partial groups included), 1-4 chunks per lane, one and two row steps per item, fewer rows
+    than one row step, ragged row blocks and the tall launch shapes."""
+    plan = w.describe_plan(M, N, K)
+    assert plan.startswith("mfma4x4x4_splitk"), plan
+    d = synthetic.dense(N=N, K=K, seed=M * 7 + N, M=M, config_id=804)
+    print(f"batched M={M} {N}x{K} plan={plan}", flush=True)
+    Y = host(w.gemv_batched(words(d.qweight), f16(d.scales), bf16(d.x)))
+    ref, mag = oracle.gemv_batched(d.qweight, d.scales, d.x, K)
+    within(Y, ref, mag, f"batched M={M} {N}x{K}")
+
+
 def test_batched_rows_match_single_token():
     N, K, M = 500, 8192, 16
     d = synthetic.dense(N=N, K=K, seed=9, M=M, config_id=802)

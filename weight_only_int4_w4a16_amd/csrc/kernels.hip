@@ -763,6 +763,231 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
 }
 
 // ------------------------------------------------------------------------------------------
+// Split-K GEMV on the 4x4x4 matrix cores for 2..16 tokens. v_mfma_f32_4x4x4_16b_bf16 computes 16
+// independent 4x4x4 blocks per wave: block b lives in lanes 4b..4b+3, lane 4b+q supplies row q of
+// A and column q of B (four consecutive k values each) and receives D[r][q], r = 0..3, in its
+// four result registers. Here A holds weights and B activations (4 tokens per token group, TG
+// groups). The 16 blocks form 16 / BR row groups of BR blocks, and the BR blocks of a row group
+// take BR consecutive 16-byte chunks of K: lane 4b+q, b = BR h + c, reads chunk c of row 4h + q
+// (per row, one instruction covers BR * 16 contiguous bytes, as a BR-lane row of the split-K VALU
+// kernel does) and keeps chunk c of token 4g+q in registers for the whole kernel -- four times
+// fewer activation registers than padding the tokens to 16 columns. A row step is 64 / BR rows;
+// BR = 8 serves rows whose chunk count is a multiple of 8 but not of 16 (K = 2304). Each
+// decoded weight word feeds two MFMAs per token group (k order 0,4,1,5 and 2,6,3,7, the order of
+// the re-paired activations); a chunk's block sum starts at -136 * (the token's sum over the
+// chunk) and is scaled by its row's fp16 scale, broadcast from lane 4b+r by DPP. After an item
+// the BR blocks' partials of a row group are added by DPP row rotations and permlane swaps
+// (all 16 lanes with the same lane % 4 and row group), and the waves of a
+// work-group, which split K as in the split-K kernel, meet in LDS after the last item.
+// ------------------------------------------------------------------------------------------
+typedef short bf16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+
+__device__ __forceinline__ bf16x4_t as_bf16x4(uint32_t a, uint32_t b)
+{
+    const uint2 v = {a, b};
+    return __builtin_bit_cast(bf16x4_t, v);
+}
+
+// Sum of v over the BR lanes 4b + (lane % 4) of a row group, b = BR h .. BR h + BR - 1 (one value
+// per block of a 4x4x4 MFMA): rotations by 4 and 8 lanes within a DPP row add its 4 blocks, the
+// permlane swaps add the rows 16 and 32 lanes away.
+template <int BR>
+__device__ __forceinline__ float sum_over_blocks(float v)
+{
+    int x = __builtin_bit_cast(int, v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false));
+    x = __builtin_bit_cast(int, v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));
+    v = swap_fold(v, v, 4);
+    return BR == 16 ? swap_fold(v, v, 5) : v;
+}
+
+// Up to 16 waves when a lane holds one chunk per step (rows of 72 chunks need 9), else 8.
+template <int TG, int CL, int U, int BR>
+__global__ void __launch_bounds__(CL == 1 ? 1024 : 512)
+gemv_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
+                  const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
+                  int32_t M, int64_t N, int32_t K, int32_t rows_per_block)
+{
+    static_assert(BR == 8 || BR == 16, "a row group is 8 or 16 blocks");
+    constexpr int R = 4 * (16 / BR);     // rows per row step: 4 rows per row group
+    constexpr int ROWS = U * R;
+    extern __shared__ float red[];      // [M][rows_per_block][W]
+    const int CPR = K >> 5;
+    const int GPR = K >> 7;
+    const int W = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 3;              // row of A and token column of B within the block
+    const int b = lane >> 2;             // block
+    const int h = b / BR;                // row group: rows 4h .. 4h + 3 of a row step
+    const int bc = b % BR;               // chunk of each run of BR chunks
+    const int cw = wave * (BR * CL) + bc;   // this lane's first chunk; chunk step j adds BR j
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+    const int64_t left = N - r0;
+    const int rcount = (int)(left < rows_per_block ? left : rows_per_block);   // >= 1
+    const int n_items = (rcount + ROWS - 1) / ROWS;
+    // Rows of an item: a uniform first row plus row r of step u; the last item is pulled back to
+    // end at the block's last row (rows computed twice get identical bits), and a block with fewer
+    // rows than one item clamps the rows instead.
+    const bool full = rcount >= ROWS;
+    auto step_row = [&](int u, int r) -> int {
+        const int x = u * R + r;
+        return (!full && x > rcount - 1) ? rcount - 1 : x;
+    };
+    auto item_row0 = [&](int item) -> int {
+        if (!full)
+            return 0;
+        const int r = item * ROWS;
+        return r + ROWS <= rcount ? r : rcount - ROWS;
+    };
+    struct Buf {
+        uint4 w[CL][U];
+        uint16_t s[CL][U];
+    };
+    uint32_t woff[U], soff[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int r = step_row(u, 4 * h + q);
+        woff[u] = (uint32_t)((r * CPR + cw) * 16);
+        soff[u] = (uint32_t)((r * GPR + (cw >> 2)) * 2);
+    }
+    int ld_item = 0;
+    auto load = [&](Buf &buf) {
+        const int64_t row0 = r0 + item_row0(ld_item);
+        const char *wb = reinterpret_cast<const char *>(qw + row0 * CPR);
+        const char *sb = reinterpret_cast<const char *>(sc + row0 * GPR);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < CL; ++j) {
+                // chunk step j: BR chunks further along the row, BR / 4 scale groups
+                buf.w[j][u] =
+                    load_weights(reinterpret_cast<const uint4 *>(wb + woff[u] + 16 * BR * j));
+                buf.s[j][u] = *reinterpret_cast<const uint16_t *>(sb + soff[u] + (BR / 2) * j);
+            }
+        ++ld_item;
+    };
+
+    // Activations first (load completions are counted in issue order): chunk cw + 16 j of token
+    // 4g + q; token slots past M read token M-1 and their outputs are never stored.
+    uint4 xq[TG][CL][4];
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+        const int t = 4 * g + q < M ? 4 * g + q : M - 1;
+        const uint4 *xg = reinterpret_cast<const uint4 *>(X + (int64_t)t * ldx);
+#pragma unroll
+        for (int j = 0; j < CL; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                xq[g][j][w] = xg[4 * (cw + BR * j) + w];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the activation loads ahead of the weight loads
+    Buf bufA, bufB;
+    load(bufA);
+    float off[TG][CL];
+#pragma unroll
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+        for (int j = 0; j < CL; ++j) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint4 v = xq[g][j][w];
+                sum = dot2(v.x, 0x3F803F80u, sum);
+                sum = dot2(v.y, 0x3F803F80u, sum);
+                sum = dot2(v.z, 0x3F803F80u, sum);
+                sum = dot2(v.w, 0x3F803F80u, sum);
+                xq[g][j][w] = pair_activations(v);
+            }
+            off[g][j] = -kOffset * sum;
+        }
+
+    int cp_item = 0;
+    auto compute = [&](const Buf &buf) {
+        f32x4_t acc[U][TG];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int g = 0; g < TG; ++g)
+                acc[u][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < CL; ++j)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                uint32_t p[4][4];
+                unpack_chunk(buf.w[j][u], p);
+                // scales of the block's rows 0..3 (lane 4b + r holds row r's)
+                const int sv = buf.s[j][u];
+                const float s4[4] = {
+                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0x00, 0xF, 0xF, false)),
+                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0x55, 0xF, 0xF, false)),
+                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xAA, 0xF, 0xF, false)),
+                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xFF, 0xF, 0xF, false))};
+#pragma unroll
+                for (int g = 0; g < TG; ++g) {
+                    const float o = off[g][j];
+                    f32x4_t d = {o, o, o, o};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint4 xv = xq[g][j][w];
+                        d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                            as_bf16x4(p[w][0], p[w][1]), as_bf16x4(xv.x, xv.y), d, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                            as_bf16x4(p[w][2], p[w][3]), as_bf16x4(xv.z, xv.w), d, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[u][g][r] = fmaf(s4[r], d[r], acc[u][g][r]);
+                }
+            }
+        // The BR blocks' partials of each (row, token), then lane 4b + q with bc = r < 4 parks
+        // row 4h + r's value for token 4g + q in LDS.
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int g = 0; g < TG; ++g) {
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] = sum_over_blocks<BR>(acc[u][g][r]);
+                const int t = 4 * g + q;
+                if (bc < 4 && t < M) {
+                    const float val = bc == 0 ? v[0] : bc == 1 ? v[1] : bc == 2 ? v[2] : v[3];
+                    const int lr = item_row0(cp_item) + step_row(u, 4 * h + bc);
+                    red[((int64_t)t * rows_per_block + lr) * W + wave] = val;
+                }
+            }
+        ++cp_item;
+    };
+
+    int i = 0;
+    for (; i + 2 < n_items; i += 2) {
+        load(bufB);
+        compute(bufA);
+        load(bufA);
+        compute(bufB);
+    }
+    if (i + 1 < n_items) {
+        load(bufB);
+        compute(bufA);
+        compute(bufB);
+    } else {
+        compute(bufA);
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < M * rcount; k += blockDim.x) {
+        const int t = k / rcount;
+        const int lr = k - t * rcount;
+        const float *pp = red + ((int64_t)t * rows_per_block + lr) * W;
+        float v = 0.0f;
+        for (int w = 0; w < W; ++w)
+            v += pp[w];
+        Y[t * ldy + r0 + lr] = v;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Grouped-expert GEMV for M tokens with their own topk experts each: every expert selected by
 // any token is streamed once per call and multiplied with all the tokens that chose it.
 //
@@ -1494,6 +1719,18 @@ static hipError_t launch_splitk_t(const GemvArgs &a, const Plan &p, hipStream_t 
                            args, (size_t)p.lds_bytes, stream);
 }
 
+template <int TG, int CL, int U, int BR>
+static hipError_t launch_mfma4_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
+{
+    auto kern = gemv_mfma4_kernel<TG, CL, U, BR>;
+    int32_t rpb = (int32_t)p.rows_per_block;
+    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X, (void *)&a.ldx,
+                    (void *)&a.Y,       (void *)&a.ldy,    (void *)&a.M, (void *)&a.N,
+                    (void *)&a.K,       (void *)&rpb};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(p.threads),
+                           args, (size_t)p.lds_bytes, stream);
+}
+
 #ifndef W4A16_MOE_BATCHED_MT
 #define W4A16_MOE_BATCHED_MT 1   // tokens accumulated per pass over an expert's rows
 #endif
@@ -1547,6 +1784,10 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
         p.lines == (XL_ >= 2) && p.V == GU_ && p.threads == 64 * WPB_)                        \
         return launch_mfma_t<T_, KS_, XL_, GU_, WPB_>(a, p, stream);
 
+#define W4A16_MFMA4_CASE(TG_, CL_, U_, BR_)                                                  \
+    if (p.MT == TG_ && p.V == CL_ && p.U == U_ && p.L == BR_)                                \
+        return launch_mfma4_t<TG_, CL_, U_, BR_>(a, p, stream);
+
 #define W4A16_MOE_BATCHED_CASE(L_, V_)                                                       \
     if (p.L == L_ && p.V == V_)                                                              \
         return launch_moe_batched_t<L_, V_>(a, p, stream);
@@ -1565,6 +1806,8 @@ hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream)
         W4A16_GATHER_CONFIGS(W4A16_GATHER_CASE)
     } else if (p.kind == PLAN_MFMA) {
         W4A16_MFMA_CONFIGS(W4A16_MFMA_CASE)
+    } else if (p.kind == PLAN_MFMA4) {
+        W4A16_MFMA4_CONFIGS(W4A16_MFMA4_CASE)
     }
     return hipErrorInvalidConfiguration;
 }

@@ -38,9 +38,13 @@ bool plan_instantiated(const Plan &p)
     if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ && p.xlds == (XL_ == 1 || XL_ == 2) && \
         p.lines == (XL_ >= 2) && p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))    \
         return true;
+#define W4A16_MFMA4_MATCH(TG_, CL_, U_, BR_)                                                  \
+    if (p.kind == PLAN_MFMA4 && p.MT == TG_ && p.V == CL_ && p.U == U_ && p.L == BR_)           \
+        return true;
     W4A16_VALU_CONFIGS(W4A16_VALU_MATCH)
     W4A16_TAIL_CONFIGS(W4A16_TAIL_MATCH)
     W4A16_MFMA_CONFIGS(W4A16_MFMA_MATCH)
+    W4A16_MFMA4_CONFIGS(W4A16_MFMA4_MATCH)
     W4A16_SPLITK_CONFIGS(W4A16_SPLITK_MATCH)
     W4A16_GATHER_CONFIGS(W4A16_GATHER_MATCH)
 #undef W4A16_SPLITK_MATCH
@@ -48,6 +52,7 @@ bool plan_instantiated(const Plan &p)
 #undef W4A16_VALU_MATCH
 #undef W4A16_TAIL_MATCH
 #undef W4A16_MFMA_MATCH
+#undef W4A16_MFMA4_MATCH
     return false;
 }
 
@@ -105,6 +110,38 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
         const int64_t cap = (int64_t)cus * per_cu;
         p->blocks = blocks < cap ? blocks : cap;
         return p->blocks >= 1;
+    }
+    if (p->kind == PLAN_MFMA4) {
+        // MT holds the token groups of 4, V the chunks per lane and L the blocks per row group
+        // (8 or 16): a wave covers L * V chunks of K and the number of waves follows from K (up
+        // to 16 with one chunk per lane, else 8). Dense calls only.
+        const int64_t per_wave = (int64_t)p->L * p->V;
+        if (p->MT != (M + 3) / 4 || M < 2 || p->moe || (p->L != 8 && p->L != 16) ||
+            cpr % per_wave != 0)
+            return false;
+        const int64_t waves = cpr / per_wave;
+        if (waves < 1 || waves > (p->V == 1 ? 16 : 8))
+            return false;
+        p->threads = (int)(64 * waves);
+        int per_cu = blocks_per_cu;
+        if (per_cu * waves > kMaxWavesPerCu)
+            per_cu = (int)(kMaxWavesPerCu / waves);
+        if (per_cu < 1)
+            per_cu = 1;
+        int64_t blocks = (int64_t)cus * per_cu;
+        const int64_t step = 4LL * (16 / p->L) * p->U;     // rows per item
+        int64_t rpb = (N + blocks - 1) / blocks;
+        rpb = (rpb + step - 1) / step * step;
+        const int64_t max_rpb = lds_limit / (4 * waves * M);
+        if (rpb > max_rpb)
+            rpb = max_rpb / step * step;
+        if (rpb < step)
+            return false;
+        blocks = (N + rpb - 1) / rpb;
+        p->rows_per_block = rpb;
+        p->blocks = blocks;
+        p->lds_bytes = 4 * waves * M * rpb;
+        return blocks >= 1 && blocks < (1LL << 31);
     }
     if (p->kind == PLAN_SPLITK) {
         // V holds the chunks per lane; the number of waves follows from K. Dense calls only.
@@ -307,6 +344,47 @@ static bool mfma_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, P
     return false;
 }
 
+// 4x4x4-MFMA split-K for 2..8 tokens (one or two token groups), from launch-shape sweeps on
+// MI355X with rotated weights:
+// (times are medians of interleaved rounds of the same graph-timed calls):
+//  - rows of a multiple of 16 chunks of at least 128 chunks (K >= 4096): 16 blocks per row
+//    group, 2 chunks per lane (4 with two token groups or for K = 14336); two row steps per item
+//    and 2 work-groups per CU on tall matrices (28672 x 4096 at 4 tokens: 13.6 us against 29.2
+//    us for split-K VALU), else one and one (8192 x 8192 at 4 tokens: 10.5 against 12.3 us; at
+//    8 tokens with 4 chunks per lane: 13.5 against 14.0 us for the 16x16x32 kernel);
+//  - shorter rows of a multiple of 8 chunks (K <= 2048) and rows of 72 chunks (K = 2304): 8
+//    blocks per row group; one chunk per lane and two row steps (14336 x 2048 at 4 tokens: 6.6
+//    against 9.0 us with 16 blocks, 11.0 for VALU), or 3 chunks per lane for 72 chunks with 4
+//    work-groups per CU on tall matrices (163840 x 2304 at 2 tokens: 34.4 against 37.1 us)
+//    and 1 otherwise (4096 x 2304 at 4 tokens: 4.3 against 8.7 us).
+static bool mfma4_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, Plan *p)
+{
+    const int64_t cpr = K / 32;
+    Plan c{};
+    c.kind = PLAN_MFMA4;
+    c.MT = (M + 3) / 4;
+    const bool tall = N >= 16384;
+    int bpc = 1;
+    if (cpr % 16 == 0 && cpr >= 128) {
+        c.L = 16;
+        c.V = (c.MT == 2 && cpr >= 256) || cpr / 32 > 8 ? 4 : 2;
+        c.U = c.MT == 1 && tall ? 2 : 1;
+        bpc = tall ? 2 : 1;
+    } else if (cpr % 8 == 0 && cpr <= 64) {
+        c.L = 8;
+        c.V = 1;
+        c.U = 2;
+    } else if (cpr % 8 == 0) {
+        c.L = 8;
+        c.V = (cpr / 8) % 3 == 0 ? 3 : 1;
+        c.U = 1;
+        bpc = tall ? 4 : 1;
+    } else {
+        return false;
+    }
+    return try_plan(c, bpc, M, N, K, 0, cus, lds_limit, p);
+}
+
 // Whether 3 or 4 tokens are better served by the MFMA kernel than by the VALU ones: tall
 // matrices whose rows are not a multiple of 2048 values (the split-K VALU kernel's shapes) and
 // hold an even number of groups (whole-line loads), where decoding each weight once for all tokens on the matrix cores beats 3-4 dot products
@@ -332,14 +410,19 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     const bool k2048 = cpr % 64 == 0;
 
     const int split_bpc = (int)(c64 >= 8 ? 1 : 8 / (c64 > 0 ? c64 : 1));
+    // K = 4096, one token, tall: 32 lanes x 2 chunks per item, 3 work-groups per CU (28672 x
+    // 4096: 12.0 us against 12.2 with 8).
     if (!moe && M == 1 && K == 4096 && rows >= 16384 &&
-        try_plan(valu(1, 32, 2, 1, false), 8, M, N, K, topk, cus, lds_limit, p))
+        try_plan(valu(1, 32, 2, 1, false), 3, M, N, K, topk, cus, lds_limit, p))
         return true;
     // K = 2048, one token: tall matrices take the staged kernel with 32 lanes and 2 chunks per
     // item (14336 x 2048: 4.9 us against 6.9 us for 64 lanes), the others split K like the
     // longer rows below.
     if (!moe && M == 1 && K == 2048 && rows >= 8192 &&
         try_plan(valu(1, 32, 2, 1, false), 4, M, N, K, topk, cus, lds_limit, p))
+        return true;
+    // 3-4 tokens: the 4x4x4-MFMA split-K kernel wherever its lane layout fits the row.
+    if (!moe && M >= 3 && M <= 4 && mfma4_plan(M, N, K, cus, lds_limit, p))
         return true;
     if (!moe && k2048 && (c64 >= 2 || M == 1) && c64 <= 8 && M <= 4) {
         if (M == 1 && rows <= 16LL * cus &&
@@ -379,6 +462,13 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
             return true;
         return try_plan(valu(1, L, 1, 1, moe), 6, M, N, K, topk, cus, lds_limit, p);
     }
+    // 2 tokens where split-K VALU does not apply (8192 x 8192 at 2 tokens: split-K VALU 9.2 us,
+    // 4x4x4 MFMA 9.5), and 5-8 tokens on matrices of up to 8192 rows (8192 x 8192 at 5-6 tokens:
+    // 12.4-12.7 against 13.1-14.0 us; 4096 x 2304 at 8: 5.7 against 10.8). Taller matrices at
+    // 5-8 tokens keep the 16x16x32 kernels (163840 x 2304 at 8: 39 against 52 us).
+    if (!moe && (M == 2 || (M >= 5 && M <= 8 && N <= 8192)) &&
+        mfma4_plan(M, N, K, cus, lds_limit, p))
+        return true;
     if (!moe && mfma_for_few_tokens(M, N, K, cus) && mfma_plan(M, N, K, cus, lds_limit, p))
         return true;
     if (M <= 4) {
@@ -504,6 +594,12 @@ int describe_plan(const Plan &p, char *buf, size_t len)
                      "threads=%d blocks=%lld rows_per_block=%lld lds=%lld",
                      p.mode == PLAN_MODE_COMBINE ? "_moe_combine" : "", p.MT, p.L, p.V, p.U, p.threads, (long long)p.blocks,
                      (long long)p.rows_per_block, (long long)p.lds_bytes);
+    else if (p.kind == PLAN_MFMA4)
+        n = snprintf(buf, len,
+                     "mfma4x4x4_splitk token_groups=%d chunks_per_lane=%d row_steps=%d "
+                     "blocks_per_row=%d threads=%d blocks=%lld rows_per_block=%lld lds=%lld",
+                     p.MT, p.V, p.U, p.L, p.threads, (long long)p.blocks, (long long)p.rows_per_block,
+                     (long long)p.lds_bytes);
     else if (p.kind == PLAN_MOE_BATCHED)
         n = snprintf(buf, len,
                      "moe_batched tokens_per_pass=%d lanes_per_row=%d chunks_per_item=%d "

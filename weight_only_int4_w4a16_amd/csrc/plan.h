@@ -8,7 +8,7 @@
 namespace w4a16 {
 
 enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3,
-                PLAN_MOE_BATCHED = 4 };
+                PLAN_MOE_BATCHED = 4, PLAN_MFMA4 = 5 };
 
 // What the rows of a staged VALU launch are: one matrix, expert rows, the gate+up experts with
 // the SwiGLU epilogue, or the down experts summed with router weights.
@@ -62,6 +62,16 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
     X(1, 1, 2, 6, 8) X(1, 1, 2, 4, 8) X(1, 1, 2, 2, 8) X(1, 1, 2, 6, 4) X(1, 1, 2, 4, 4)      \
     X(1, 1, 2, 2, 4) X(2, 4, 3, 2, 4) X(1, 8, 3, 2, 8) X(4, 4, 3, 2, 4)                      \
     X(2, 4, 0, 2, 4) X(2, 2, 0, 2, 4) X(2, 1, 0, 2, 4) X(1, 1, 0, 2, 4) X(1, 1, 0, 1, 4)
+#endif
+
+// 4x4x4-MFMA split-K kernels for 2..8 tokens: X(token groups of 4, chunks per lane, row steps per
+// item, blocks per row group). Three and four token groups measured slower than the 16x16x32
+// kernels at 12-16 tokens and need more registers than 1024-thread groups allow.
+#ifndef W4A16_MFMA4_CONFIGS
+#define W4A16_MFMA4_CONFIGS(X)                                                               \
+    X(1, 1, 1, 16) X(1, 2, 1, 16) X(1, 4, 1, 16) X(1, 1, 2, 16) X(1, 2, 2, 16) X(1, 4, 2, 16)  \
+    X(2, 1, 1, 16) X(2, 2, 1, 16) X(2, 4, 1, 16) X(2, 1, 2, 16) X(2, 2, 2, 16)               \
+    X(1, 1, 1, 8) X(1, 1, 2, 8) X(1, 3, 1, 8) X(2, 1, 1, 8) X(2, 1, 2, 8) X(2, 3, 1, 8)
 #endif
 
 struct Plan {
