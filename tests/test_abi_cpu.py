@@ -165,9 +165,14 @@ def test_moe_batched_validation(kw, status):
 
 
 def test_moe_batched_plans():
+    # rows of 8k chunks take the 4x4x4-MFMA form (tokens of an expert share each decode) ...
     assert w.describe_moe_batched_plan(16, 2048, 2304, 8).startswith(
-        "moe_batched tokens_per_pass=1 lanes_per_row=8 chunks_per_item=3 threads=512")
-    assert w.describe_moe_batched_plan(1, 5, 128, 256).startswith("moe_batched")
+        "moe_batched_mfma4x4x4 slots=4 blocks_per_row=8 chunks_per_lane=3 threads=512")
+    assert w.describe_moe_batched_plan(8, 300, 4096, 8).startswith(
+        "moe_batched_mfma4x4x4 slots=4 blocks_per_row=16 chunks_per_lane=2")
+    # ... the others the VALU form
+    assert w.describe_moe_batched_plan(1, 5, 128, 256).startswith("moe_batched tokens_per_pass=1")
+    assert w.describe_moe_batched_plan(3, 64, 384, 4).startswith("moe_batched tokens_per_pass=1")
     with pytest.raises(w.W4A16Error):
         w.describe_moe_batched_plan(16, 100, 8192, 8)    # activations do not fit in LDS
 

@@ -61,7 +61,7 @@ def check(got, ref, mag, what):
 # expert (groups larger than the 4 tokens of one pass); M * topk = 256.
 SHAPES = [(20, 64, 384, 3, 4, True), (6, 5, 128, 2, 3, True), (50, 300, 4096, 8, 8, True),
           (9, 100, 2304, 16, 16, False), (3, 77, 1024, 1, 2, True), (40, 33, 2304, 16, 8, True),
-          (5, 128, 256, 8, 32, False)]
+          (5, 128, 256, 8, 32, False), (7, 5, 2304, 5, 3, True), (12, 40, 1536, 6, 4, False)]
 
 
 @pytest.mark.parametrize("E,N,K,M,topk,distinct", SHAPES)

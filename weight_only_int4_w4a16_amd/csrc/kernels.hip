@@ -988,6 +988,93 @@ gemv_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
 }
 
 // ------------------------------------------------------------------------------------------
+// Set-up shared by the grouped-expert GEMVs for several tokens (every work-group does it, in
+// LDS). moe_group_entries groups the P = M*topk entries (token m, slot t) by expert id, in order
+// of first appearance; ids outside [0, E) form one group of their own (key -1). A group of c
+// entries becomes ceil(c / MT) virtual entries of up to MT entries: ve_e[v] is the expert (or
+// -1), ve_tok[v*MT + j] the j-th entry or -1, and *nve_s the number of virtual entries.
+// Scratch arrays key_s .. vbase_s hold P ints each. Ends without a barrier.
+// ------------------------------------------------------------------------------------------
+template <int MT>
+__device__ void moe_group_entries(const int32_t *__restrict__ ids, int P, int32_t E,
+                                  int32_t *key_s, int32_t *first_s, int32_t *rank_s,
+                                  int32_t *cnt_s, int32_t *vbase_s, int32_t *ve_e,
+                                  int32_t *ve_tok, int32_t *nve_s)
+{
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        const int32_t e = ids[i];
+        key_s[i] = (e >= 0 && e < E) ? e : -1;
+        ve_e[i] = -1;
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+            ve_tok[i * MT + j] = -1;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        const int32_t k = key_s[i];
+        int f = i, r = 0;
+        for (int j = i - 1; j >= 0; --j)
+            if (key_s[j] == k) {
+                f = j;
+                ++r;
+            }
+        first_s[i] = f;
+        rank_s[i] = r;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        int c = 0;
+        if (first_s[i] == i)
+            for (int q = i; q < P; ++q)
+                c += key_s[q] == key_s[i];
+        cnt_s[i] = (c + MT - 1) / MT;      // virtual entries of the group (0 unless first)
+    }
+    __syncthreads();
+    // Virtual entries of the groups whose first entry precedes i, summed in entry order.
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        int base = 0;
+        for (int j = 0; j < i; ++j)
+            base += cnt_s[j];
+        vbase_s[i] = base;
+        if (i == P - 1)
+            nve_s[0] = base + cnt_s[i];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        const int v = vbase_s[first_s[i]] + rank_s[i] / MT;
+        ve_tok[v * MT + rank_s[i] % MT] = i;
+        if (rank_s[i] % MT == 0)
+            ve_e[v] = key_s[i];
+    }
+}
+
+// Activations of every token staged re-paired as [token][word j][chunk] (16 bytes each), with
+// the per-chunk offsets -136 * sum(x) in bs[token][chunk]. Ends without a barrier.
+__device__ void moe_stage_activations(const uint16_t *__restrict__ X, int64_t ldx, int M, int K,
+                                      uint4 *xs, float *bs)
+{
+    const int KW = K >> 3;
+    const int CPR = K >> 5;
+    for (int t = 0; t < M; ++t) {
+        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
+        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
+            const uint4 v = xg[w];
+            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
+            float sum = 0.0f;
+            sum = dot2(v.x, 0x3F803F80u, sum);
+            sum = dot2(v.y, 0x3F803F80u, sum);
+            sum = dot2(v.z, 0x3F803F80u, sum);
+            sum = dot2(v.w, 0x3F803F80u, sum);
+            // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
+            sum += dpp_partner(sum, 0);
+            sum += dpp_partner(sum, 1);
+            if ((w & 3) == 0)
+                bs[t * CPR + (w >> 2)] = -kOffset * sum;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Grouped-expert GEMV for M tokens with their own topk experts each: every expert selected by
 // any token is streamed once per call and multiplied with all the tokens that chose it.
 //
@@ -1035,71 +1122,10 @@ gemv_moe_batched_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict
     int32_t *ve_tok = ve_e + P;                                     // [P][MT] entries or -1
     int32_t *nve_s = ve_tok + P * MT;                               // [1]
 
-    // ---- group the entries by expert
-    for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        const int32_t e = ids[i];
-        key_s[i] = (e >= 0 && e < E) ? e : -1;
-        ve_e[i] = -1;
-#pragma unroll
-        for (int j = 0; j < MT; ++j)
-            ve_tok[i * MT + j] = -1;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        const int32_t k = key_s[i];
-        int f = i, r = 0;
-        for (int j = i - 1; j >= 0; --j)
-            if (key_s[j] == k) {
-                f = j;
-                ++r;
-            }
-        first_s[i] = f;
-        rank_s[i] = r;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        int c = 0;
-        if (first_s[i] == i)
-            for (int q = i; q < P; ++q)
-                c += key_s[q] == key_s[i];
-        cnt_s[i] = (c + MT - 1) / MT;      // virtual entries of the group (0 unless first)
-    }
-    __syncthreads();
-    // Virtual entries of the groups whose first entry precedes i, summed in entry order.
-    for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        int base = 0;
-        for (int j = 0; j < i; ++j)
-            base += cnt_s[j];
-        vbase_s[i] = base;
-        if (i == P - 1)
-            nve_s[0] = base + cnt_s[i];
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        const int v = vbase_s[first_s[i]] + rank_s[i] / MT;
-        ve_tok[v * MT + rank_s[i] % MT] = i;
-        if (rank_s[i] % MT == 0)
-            ve_e[v] = key_s[i];
-    }
+    moe_group_entries<MT>(ids, P, E, key_s, first_s, rank_s, cnt_s, vbase_s, ve_e, ve_tok,
+                          nve_s);
     __syncthreads();   // the grouping scratch is overwritten by the activations below
-
-    // ---- stage the activations of every token
-    for (int t = 0; t < M; ++t) {
-        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
-        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
-            const uint4 v = xg[w];
-            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
-            float sum = 0.0f;
-            sum = dot2(v.x, 0x3F803F80u, sum);
-            sum = dot2(v.y, 0x3F803F80u, sum);
-            sum = dot2(v.z, 0x3F803F80u, sum);
-            sum = dot2(v.w, 0x3F803F80u, sum);
-            sum += dpp_partner(sum, 0);
-            sum += dpp_partner(sum, 1);
-            if ((w & 3) == 0)
-                bs[t * CPR + (w >> 2)] = -kOffset * sum;
-        }
-    }
+    moe_stage_activations(X, ldx, M, K, xs, bs);
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
@@ -1190,6 +1216,193 @@ gemv_moe_batched_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict
                 if (pr == 0 && tok[j] >= 0)
                     Y[(int64_t)tok[j] * N + row] = e >= 0 ? r[0] : 0.0f;
                 acc[j] = 0.0f;
+            }
+        }
+        const bool wrap = cp_b + 1 == nb;
+        cp_b = wrap ? 0 : cp_b + 1;
+        cp_st += wrap ? (uint32_t)GW : 0u;
+    };
+
+    Buf bufA, bufB;
+    load(bufA);
+    int64_t i = 0;
+    for (; i + 2 < n_items; i += 2) {
+        load(bufB);
+        compute(bufA);
+        load(bufA);
+        compute(bufB);
+    }
+    if (i + 1 < n_items) {
+        load(bufB);
+        compute(bufA);
+        compute(bufB);
+    } else {
+        compute(bufA);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Grouped-expert GEMV for several tokens on the 4x4x4 matrix cores. The same set-up as the VALU
+// form (entries grouped by expert in LDS, activations of every token staged re-paired with their
+// chunk offsets), with virtual entries of up to 4 entries of one expert. Items are (virtual entry,
+// block of rows) in expert-major order: the tokens that share an expert share its items, so the
+// block-major order the VALU form needs for L2 reuse is not needed, and consecutive waves stream
+// an expert's rows contiguously (16 tokens x top-8 of 256: 58.1 us against 60.5 block-major and
+// 63.2 for the VALU form). Within an item the lanes take the 4x4x4 layout of the split-K MFMA
+// kernel: lane 4b+q, b = BR h + c, reads chunk c (of each run of BR) of row 4h + q of each row
+// step (64 / BR rows; U steps per block, one measured fastest), decodes it once, and supplies the
+// activations of the virtual entry's slot q as column q of B -- so the tokens that chose an expert
+// share every decode, and the products run on the matrix cores. Empty slots repeat slot 0's token
+// (their outputs are never stored). After the last chunk batch of an item the BR blocks' partials
+// are added across lanes and the lanes with c < 4 store row 4h + c for their slot's entry.
+// ------------------------------------------------------------------------------------------
+template <int BR, int CL, int U>
+__global__ void __launch_bounds__(512)
+gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
+                              const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y,
+                              const int32_t *__restrict__ ids, int32_t M, int32_t topk, int32_t E,
+                              int64_t N, int32_t K)
+{
+    constexpr int MT = 4;
+    constexpr int R = 4 * (16 / BR) * U; // rows per block: U row steps of 64 / BR rows
+    extern __shared__ uint4 smem[];
+    const int KW = K >> 3;
+    const int CPR = K >> 5;
+    const int GPR = K >> 7;
+    const int P = M * topk;
+    // Region A holds the grouping scratch first and the staged activations afterwards.
+    const int a16 = (M * KW > (5 * P + 3) / 4) ? M * KW : (5 * P + 3) / 4;   // 16-byte units
+    uint4 *xs = smem;                                              // [M][4][CPR]
+    int32_t *key_s = reinterpret_cast<int32_t *>(smem);           // grouping scratch, 5 x [P]
+    float *bs = reinterpret_cast<float *>(smem + a16);            // [M][CPR]
+    int32_t *ve_e = reinterpret_cast<int32_t *>(bs + M * CPR);    // [P]
+    int32_t *ve_tok = ve_e + P;                                     // [P][MT]
+    int32_t *nve_s = ve_tok + P * MT;                               // [1]
+    moe_group_entries<MT>(ids, P, E, key_s, key_s + P, key_s + 2 * P, key_s + 3 * P,
+                          key_s + 4 * P, ve_e, ve_tok, nve_s);
+    __syncthreads();   // the grouping scratch is overwritten by the activations below
+    moe_stage_activations(X, ldx, M, K, xs, bs);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 3;
+    const int blk = lane >> 2;
+    const int h = blk / BR;              // row group: rows 4h .. 4h + 3 of the block
+    const int bc = blk % BR;             // chunk of each run of BR chunks
+    const int wpb = blockDim.x >> 6;
+    const int64_t gw = (int64_t)blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t GW = (int64_t)gridDim.x * wpb;
+    const int nve = nve_s[0];
+    // Token of an entry: entry / topk as a multiply-high by ceil(2^32 / topk), exact for
+    // entry, topk <= 256 (entry * topk < 2^32).
+    const uint32_t tk_magic = (uint32_t)((0x100000000ull + (uint32_t)topk - 1) / (uint32_t)topk);
+    // P * N < 2^31 (checked by the host), so block counts and item indices fit in 32 bits.
+    const uint32_t n_blocks = (uint32_t)((N + R - 1) / R);
+    const uint32_t n_super = (uint32_t)nve * n_blocks;
+    const int nb = CPR / (BR * CL);
+    if (gw >= (int64_t)n_super)
+        return;
+    const int64_t n_items = ((n_super - 1 - gw) / GW + 1) * nb;
+
+    // Row r of block b: the last block is pulled back to end at row N - 1 (rows computed twice
+    // give identical bits); with fewer than R rows the rows are clamped.
+    auto block_row = [&](uint32_t b, int r) -> int64_t {
+        if (N < R)
+            return r < N ? r : N - 1;
+        const int64_t r0 = (int64_t)b * R + R <= N ? (int64_t)b * R : N - R;
+        return r0 + r;
+    };
+    struct Buf {
+        uint4 w[CL][U];
+        uint16_t s[CL][U];
+    };
+    uint32_t ld_st = (uint32_t)gw;
+    int ld_b = 0;
+    // Item st: virtual entry v = st / n_blocks, block b = st % n_blocks (expert-major).
+    auto split_item = [&](uint32_t st, uint32_t &b, uint32_t &v) {
+        v = st / n_blocks;
+        b = st - v * n_blocks;
+    };
+    auto load = [&](Buf &buf) {
+        uint32_t b, v;
+        split_item(ld_st, b, v);
+        const int32_t e = ve_e[v];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row =
+                (int64_t)(e >= 0 ? e : 0) * N + block_row(b, (64 / BR) * u + 4 * h + q);
+            const uint4 *wr = pick(e >= 0, qw + row * CPR, reinterpret_cast<const uint4 *>(X));
+            const uint16_t *sr = pick(e >= 0, sc + row * GPR, X);
+#pragma unroll
+            for (int j = 0; j < CL; ++j) {
+                const int c = bc + BR * (j + CL * ld_b);
+                buf.w[j][u] = load_weights(wr + c);
+                buf.s[j][u] = sr[c >> 2];
+            }
+        }
+        const bool wrap = ld_b + 1 == nb;
+        ld_b = wrap ? 0 : ld_b + 1;
+        ld_st += wrap ? (uint32_t)GW : 0u;
+    };
+
+    f32x4_t acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        acc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t cp_st = (uint32_t)gw;
+    int cp_b = 0;
+    auto compute = [&](const Buf &buf) {
+        uint32_t bb, v;
+        split_item(cp_st, bb, v);
+        const int32_t e_q = ve_tok[v * MT + q];
+        const uint32_t e_t = (uint32_t)(e_q >= 0 ? e_q : ve_tok[v * MT]);   // empty: slot 0
+        const int m = (int)__umulhi(e_t, tk_magic);
+#pragma unroll
+        for (int j = 0; j < CL; ++j) {
+            const int c = bc + BR * (j + CL * cp_b);
+            uint4 xv[4];                 // slot q's activations for chunk c, shared by the steps
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                xv[w] = xs[m * KW + w * CPR + c];
+            const float o = bs[m * CPR + c];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                uint32_t p[4][4];
+                unpack_chunk(buf.w[j][u], p);
+                const int sv = buf.s[j][u];
+                const float s4[4] = {
+                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0x00, 0xF, 0xF, false)),
+                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0x55, 0xF, 0xF, false)),
+                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xAA, 0xF, 0xF, false)),
+                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xFF, 0xF, 0xF, false))};
+                f32x4_t d = {o, o, o, o};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                        as_bf16x4(p[w][0], p[w][1]), as_bf16x4(xv[w].x, xv[w].y), d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                        as_bf16x4(p[w][2], p[w][3]), as_bf16x4(xv[w].z, xv[w].w), d, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[u][r] = fmaf(s4[r], d[r], acc[u][r]);
+            }
+        }
+        if (cp_b == nb - 1) {
+            const int32_t e = ve_e[v];
+            const int32_t entry = ve_tok[v * MT + q];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float vv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    vv[r] = sum_over_blocks<BR>(acc[u][r]);
+                if (bc < 4 && entry >= 0) {
+                    const float val = bc == 0 ? vv[0] : bc == 1 ? vv[1] : bc == 2 ? vv[2] : vv[3];
+                    Y[(int64_t)entry * N + block_row(bb, (64 / BR) * u + 4 * h + bc)] =
+                        e >= 0 ? val : 0.0f;
+                }
+                acc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
         const bool wrap = cp_b + 1 == nb;
@@ -1719,6 +1932,17 @@ static hipError_t launch_splitk_t(const GemvArgs &a, const Plan &p, hipStream_t 
                            args, (size_t)p.lds_bytes, stream);
 }
 
+template <int BR, int CL, int U>
+static hipError_t launch_moe_batched_mfma4_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
+{
+    auto kern = gemv_moe_batched_mfma4_kernel<BR, CL, U>;
+    void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X,    (void *)&a.ldx,
+                    (void *)&a.Y,       (void *)&a.ids,    (void *)&a.M,    (void *)&a.topk,
+                    (void *)&a.E,       (void *)&a.N,      (void *)&a.K};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(p.blocks), dim3(p.threads),
+                           args, (size_t)p.lds_bytes, stream);
+}
+
 template <int TG, int CL, int U, int BR>
 static hipError_t launch_mfma4_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
@@ -1792,10 +2016,18 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
     if (p.L == L_ && p.V == V_)                                                              \
         return launch_moe_batched_t<L_, V_>(a, p, stream);
 
+#define W4A16_MOE_BATCHED_MFMA4_CASE(BR_, CL_, U_)                                            \
+    if (p.L == BR_ && p.V == CL_ && p.U == U_)                                               \
+        return launch_moe_batched_mfma4_t<BR_, CL_, U_>(a, p, stream);
+
 hipError_t launch(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
     if (p.kind == PLAN_MOE_BATCHED) {
         W4A16_MOE_BATCHED_CONFIGS(W4A16_MOE_BATCHED_CASE)
+        return hipErrorInvalidConfiguration;
+    }
+    if (p.kind == PLAN_MOE_BATCHED_MFMA4) {
+        W4A16_MOE_BATCHED_MFMA4_CONFIGS(W4A16_MOE_BATCHED_MFMA4_CASE)
         return hipErrorInvalidConfiguration;
     }
     if (p.kind == PLAN_VALU) {

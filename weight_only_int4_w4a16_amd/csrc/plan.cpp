@@ -38,6 +38,12 @@ bool plan_instantiated(const Plan &p)
     if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ && p.xlds == (XL_ == 1 || XL_ == 2) && \
         p.lines == (XL_ >= 2) && p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))    \
         return true;
+#define W4A16_MOE_BATCHED_MATCH(L_, V_)                                                       \
+    if (p.kind == PLAN_MOE_BATCHED && p.L == L_ && p.V == V_)                                   \
+        return true;
+#define W4A16_MOE_BATCHED_MFMA4_MATCH(BR_, CL_, U_)                                           \
+    if (p.kind == PLAN_MOE_BATCHED_MFMA4 && p.L == BR_ && p.V == CL_ && p.U == U_)              \
+        return true;
 #define W4A16_MFMA4_MATCH(TG_, CL_, U_, BR_)                                                  \
     if (p.kind == PLAN_MFMA4 && p.MT == TG_ && p.V == CL_ && p.U == U_ && p.L == BR_)           \
         return true;
@@ -45,6 +51,8 @@ bool plan_instantiated(const Plan &p)
     W4A16_TAIL_CONFIGS(W4A16_TAIL_MATCH)
     W4A16_MFMA_CONFIGS(W4A16_MFMA_MATCH)
     W4A16_MFMA4_CONFIGS(W4A16_MFMA4_MATCH)
+    W4A16_MOE_BATCHED_CONFIGS(W4A16_MOE_BATCHED_MATCH)
+    W4A16_MOE_BATCHED_MFMA4_CONFIGS(W4A16_MOE_BATCHED_MFMA4_MATCH)
     W4A16_SPLITK_CONFIGS(W4A16_SPLITK_MATCH)
     W4A16_GATHER_CONFIGS(W4A16_GATHER_MATCH)
 #undef W4A16_SPLITK_MATCH
@@ -53,6 +61,8 @@ bool plan_instantiated(const Plan &p)
 #undef W4A16_TAIL_MATCH
 #undef W4A16_MFMA_MATCH
 #undef W4A16_MFMA4_MATCH
+#undef W4A16_MOE_BATCHED_MATCH
+#undef W4A16_MOE_BATCHED_MFMA4_MATCH
     return false;
 }
 
@@ -527,50 +537,87 @@ bool make_tail_plan(int mode, int64_t N, int64_t K, int64_t KR, int topk, int cu
 #ifndef W4A16_MOE_BATCHED_MT
 #define W4A16_MOE_BATCHED_MT 1
 #endif
+#ifndef W4A16_MOE_BATCHED_MFMA4_U
+#define W4A16_MOE_BATCHED_MFMA4_U 1    // row steps per item (2: 74.6 against 58.1 us, 16 tokens)
+#endif
 
 // Grouped experts for M tokens: the grouped-expert launch shape of the one-token form (8 lanes
 // with 3 chunks per item for rows of 72 chunks, else the widest lanes per row), persistent
 // work-groups of 8 waves, two per CU (one if LDS holds only one): 16 waves per CU is what the
 // kernel's registers allow, and fewer, longer-lived work-groups amortise the grouping set-up
 // (measured on MI355X over 2-16 tokens).
-bool make_moe_batched_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit,
-                           Plan *p)
+bool make_moe_batched_plan_of(int kind, int M, int64_t N, int64_t K, int topk, int cus,
+                              int64_t lds_limit, Plan *p)
 {
     *p = Plan{};
     if (M < 1 || M > 16 || topk < 1 || M * topk > 256 || N < 1 || K < 128 || K % 128 != 0 ||
         cus < 1)
         return false;
     const int64_t cpr = K / 32;
-    int L = pow2_lanes(cpr), V = 1;
-    if (L == 8 && (cpr / 8) % 3 == 0)
-        V = 3;
-    if (L < 4)
-        return false;
     const int64_t P = (int64_t)M * topk;
-    p->kind = PLAN_MOE_BATCHED;
-    p->MT = W4A16_MOE_BATCHED_MT;
-    p->L = L;
-    p->V = V;
-    p->U = 1;
+    int64_t R;
+    int64_t ve_ints;      // virtual-entry tables in LDS
+    if (kind == PLAN_MOE_BATCHED_MFMA4) {
+        // 16 blocks per row group with 2 chunks per lane (or 1), else 8 with 3 (K = 2304) or 1.
+        if (cpr % 16 == 0) {
+            p->L = 16;
+            p->V = cpr % 32 == 0 ? 2 : 1;
+        } else if (cpr % 8 == 0) {
+            p->L = 8;
+            p->V = (cpr / 8) % 3 == 0 ? 3 : 1;
+        } else {
+            return false;
+        }
+        p->MT = 4;
+        p->U = W4A16_MOE_BATCHED_MFMA4_U;
+        R = 4 * (16 / p->L) * p->U;
+        ve_ints = P + P * 4 + 1;        // experts, entries of up to 4 slots, count
+    } else if (kind == PLAN_MOE_BATCHED) {
+        int L = pow2_lanes(cpr), V = 1;
+        if (L == 8 && (cpr / 8) % 3 == 0)
+            V = 3;
+        if (L < 4)
+            return false;
+        p->L = L;
+        p->V = V;
+        p->MT = W4A16_MOE_BATCHED_MT;
+        R = 64 / L;
+        ve_ints = P + P * W4A16_MOE_BATCHED_MT + 1;
+    } else {
+        return false;
+    }
+    p->kind = kind;
+    if (kind == PLAN_MOE_BATCHED)
+        p->U = 1;
     p->moe = true;
     p->threads = 512;
+    if (!plan_instantiated(*p))
+        return false;
     // Region A (activations, or the grouping scratch before them) + chunk offsets + the
-    // virtual entries (expert and MT pairs each) + their count.
+    // virtual-entry tables.
     const int64_t xs_bytes = (int64_t)M * K * 2;
     const int64_t scratch = ((20 * P + 15) / 16) * 16;
-    p->lds_bytes = (xs_bytes > scratch ? xs_bytes : scratch) + (int64_t)M * cpr * 4 +
-                   4 * (P + P * W4A16_MOE_BATCHED_MT + 1);
+    p->lds_bytes = (xs_bytes > scratch ? xs_bytes : scratch) + (int64_t)M * cpr * 4 + 4 * ve_ints;
     if (p->lds_bytes > lds_limit)
         return false;
     int64_t per_cu = lds_limit / p->lds_bytes;
     if (per_cu > 2)
         per_cu = 2;
-    const int64_t R = 64 / L;
     const int64_t most = (P * ((N + R - 1) / R) + 7) / 8;   // work-groups that could have work
     p->blocks = (int64_t)cus * per_cu;
     if (p->blocks > most)
         p->blocks = most;
     return p->blocks >= 1 && p->blocks < (1LL << 31);
+}
+
+// Grouped experts for several tokens: the 4x4x4-MFMA form wherever its lane layout fits the
+// rows, which decodes each weight once for all the tokens that chose its expert; else the VALU
+// form (one decode and dot product per token).
+bool make_moe_batched_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit,
+                           Plan *p)
+{
+    return make_moe_batched_plan_of(PLAN_MOE_BATCHED_MFMA4, M, N, K, topk, cus, lds_limit, p) ||
+           make_moe_batched_plan_of(PLAN_MOE_BATCHED, M, N, K, topk, cus, lds_limit, p);
 }
 
 int describe_plan(const Plan &p, char *buf, size_t len)
@@ -600,6 +647,11 @@ int describe_plan(const Plan &p, char *buf, size_t len)
                      "blocks_per_row=%d threads=%d blocks=%lld rows_per_block=%lld lds=%lld",
                      p.MT, p.V, p.U, p.L, p.threads, (long long)p.blocks, (long long)p.rows_per_block,
                      (long long)p.lds_bytes);
+    else if (p.kind == PLAN_MOE_BATCHED_MFMA4)
+        n = snprintf(buf, len,
+                     "moe_batched_mfma4x4x4 slots=%d blocks_per_row=%d chunks_per_lane=%d "
+                     "threads=%d blocks=%lld lds=%lld",
+                     p.MT, p.L, p.V, p.threads, (long long)p.blocks, (long long)p.lds_bytes);
     else if (p.kind == PLAN_MOE_BATCHED)
         n = snprintf(buf, len,
                      "moe_batched tokens_per_pass=%d lanes_per_row=%d chunks_per_item=%d "

@@ -8,7 +8,7 @@
 namespace w4a16 {
 
 enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3,
-                PLAN_MOE_BATCHED = 4, PLAN_MFMA4 = 5 };
+                PLAN_MOE_BATCHED = 4, PLAN_MFMA4 = 5, PLAN_MOE_BATCHED_MFMA4 = 6 };
 
 // What the rows of a staged VALU launch are: one matrix, expert rows, the gate+up experts with
 // the SwiGLU epilogue, or the down experts summed with router weights.
@@ -37,6 +37,11 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
 #endif
 
 // Grouped-expert kernels for M tokens with their own experts: X(lanes per row, chunks per item).
+// Grouped-expert GEMV for several tokens on 4x4x4 MFMA: X(blocks per row group, chunks per lane,
+// row steps per item).
+#ifndef W4A16_MOE_BATCHED_MFMA4_CONFIGS
+#define W4A16_MOE_BATCHED_MFMA4_CONFIGS(X) X(8, 3, 1) X(8, 1, 1) X(16, 1, 1) X(16, 2, 1)
+#endif
 #ifndef W4A16_MOE_BATCHED_CONFIGS
 #define W4A16_MOE_BATCHED_CONFIGS(X) X(8, 3) X(64, 1) X(32, 1) X(16, 1) X(8, 1) X(4, 1)
 #endif
@@ -126,6 +131,9 @@ bool make_tail_plan(int mode, int64_t N, int64_t K, int64_t KR, int topk, int cu
 // the activations of the M tokens do not fit in LDS.
 bool make_moe_batched_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit,
                            Plan *p);
+// The grouped-expert plan of one form (PLAN_MOE_BATCHED or PLAN_MOE_BATCHED_MFMA4).
+bool make_moe_batched_plan_of(int kind, int M, int64_t N, int64_t K, int topk, int cus,
+                              int64_t lds_limit, Plan *p);
 
 // Launch-shape override for tuning: keeps the caller's kernel choice, fills in grid and LDS.
 bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit,
