@@ -229,8 +229,11 @@ def test_valid_arguments_reach_the_device_check_only():
                         "blocks_per_row=16"),
     (3, 8192, 8192, 0, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=2"),
     (8, 4096, 14336, 0, "mfma4x4x4_splitk token_groups=2 chunks_per_lane=4"),
-    (5, 7, 256, 0, "mfma4x4x4_splitk token_groups=2 chunks_per_lane=1 row_steps=2 blocks_per_row=8"),
-    (8, 14336, 2048, 0, "mfma16x16x32_lines"), (2, 28672, 4096, 0, "splitk "),
+    (5, 7, 256, 0, "mfma4x4x4_splitk token_groups=2 chunks_per_lane=1 row_steps=1 blocks_per_row=8"),
+    (8, 14336, 2048, 0, "mfma4x4x4_splitk token_groups=2 chunks_per_lane=1 row_steps=1"),
+    (8, 28672, 4096, 0, "mfma16x16x32_lds_lines"), (2, 28672, 4096, 0, "splitk "),
+    (2, 14336, 2048, 0, "splitk tokens=2"), (4, 14336, 2048, 0, "mfma4x4x4_splitk token_groups=1 "
+                                                              "chunks_per_lane=1 row_steps=2"),
     (16, 8192, 8192, 0, "mfma16x16x32_lines tiles_per_wave=2 k_split=4"),
     (16, 14336, 2048, 0, "mfma16x16x32_lines tiles_per_wave=4 k_split=4"),
     (16, 300, 2688, 0, "mfma16x16x32 tiles_per_wave=1 k_split=1 groups_per_item=1"),

@@ -383,7 +383,7 @@ static bool mfma4_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, 
     } else if (cpr % 8 == 0 && cpr <= 64) {
         c.L = 8;
         c.V = 1;
-        c.U = 2;
+        c.U = c.MT == 1 ? 2 : 1;     // 14336 x 2048 at 8 tokens: 8.6 us with one step, 9.0 two
     } else if (cpr % 8 == 0) {
         c.L = 8;
         c.V = (cpr / 8) % 3 == 0 ? 3 : 1;
@@ -434,7 +434,7 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     // 3-4 tokens: the 4x4x4-MFMA split-K kernel wherever its lane layout fits the row.
     if (!moe && M >= 3 && M <= 4 && mfma4_plan(M, N, K, cus, lds_limit, p))
         return true;
-    if (!moe && k2048 && (c64 >= 2 || M == 1) && c64 <= 8 && M <= 4) {
+    if (!moe && k2048 && (c64 >= 2 || M <= 2) && c64 <= 8 && M <= 4) {
         if (M == 1 && rows <= 16LL * cus &&
             try_plan(splitk(1, 32, 1, 2, false), 2, M, N, K, topk, cus, lds_limit, p))
             return true;
@@ -472,11 +472,13 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
             return true;
         return try_plan(valu(1, L, 1, 1, moe), 6, M, N, K, topk, cus, lds_limit, p);
     }
-    // 2 tokens where split-K VALU does not apply (8192 x 8192 at 2 tokens: split-K VALU 9.2 us,
-    // 4x4x4 MFMA 9.5), and 5-8 tokens on matrices of up to 8192 rows (8192 x 8192 at 5-6 tokens:
-    // 12.4-12.7 against 13.1-14.0 us; 4096 x 2304 at 8: 5.7 against 10.8). Taller matrices at
-    // 5-8 tokens keep the 16x16x32 kernels (163840 x 2304 at 8: 39 against 52 us).
-    if (!moe && (M == 2 || (M >= 5 && M <= 8 && N <= 8192)) &&
+    // 2 tokens where split-K VALU does not apply (it wins where it does: 8192 x 8192 at 2 tokens
+    // 9.0 us against 9.7, 14336 x 2048 5.9 against 6.2), and 5-8 tokens on matrices of up to
+    // 16384 rows (8192 x 8192 at 5-6 tokens: 12.4-12.7 against 13.1-14.0 us; 16384 x 4096 at 8:
+    // 13.5 against 13.8; 4096 x 2304 at 8: 5.7 against 10.8). Taller matrices at 5-8 tokens
+    // keep the 16x16x32 kernels (28672 x 4096 at 8: 18.5 against 19.5 us; 163840 x 2304 at 6:
+    // 37.0 against 48.6).
+    if (!moe && (M == 2 || (M >= 5 && M <= 8 && N <= 16384)) &&
         mfma4_plan(M, N, K, cus, lds_limit, p))
         return true;
     if (!moe && mfma_for_few_tokens(M, N, K, cus) && mfma_plan(M, N, K, cus, lds_limit, p))
