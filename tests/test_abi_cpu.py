@@ -216,7 +216,8 @@ def test_valid_arguments_reach_the_device_check_only():
 @pytest.mark.parametrize("M,N,K,topk,kind", [
     (1, 1024, 2048, 0, "splitk "), (1, 4096, 7168, 0, "splitk "), (1, 16384, 3072, 0, "splitk "),
     (1, 16384, 1536, 0, "valu tokens=1 lanes_per_row=8 chunks_per_item=3"),
-    (1, 8192, 1024, 0, "valu "), (1, 4096, 4096, 0, "splitk "), (1, 28672, 4096, 0, "valu "),
+    (1, 8192, 1024, 0, "valu "), (1, 4096, 4096, 0, "splitk "),
+    (1, 28672, 4096, 0, "splitk tokens=1 lanes_per_row=32 chunks_per_lane=1 row_steps=2"),
     (1, 14336, 2048, 0, "valu tokens=1 lanes_per_row=32 chunks_per_item=2"),
     (1, 4096, 14336, 0, "splitk "), (1, 8192, 8192, 0, "splitk "), (1, 163840, 2304, 0, "valu "),
     (1, 2048, 2304, 8, "valu_moe"), (1, 5, 128, 0, "valu "), (1, 64, 65536, 0, "splitk "),

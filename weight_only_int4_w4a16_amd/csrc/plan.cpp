@@ -420,10 +420,11 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     const bool k2048 = cpr % 64 == 0;
 
     const int split_bpc = (int)(c64 >= 8 ? 1 : 8 / (c64 > 0 ? c64 : 1));
-    // K = 4096, one token, tall: 32 lanes x 2 chunks per item, 3 work-groups per CU (28672 x
-    // 4096: 12.0 us against 12.2 with 8).
+    // K = 4096, one token, tall: split K over 4 waves of 32 lanes with 2 row steps in flight,
+    // 2 work-groups per CU (28672 x 4096: 11.44 us against 11.86 for the staged kernel; 16384 x
+    // 4096: 7.80 against 8.05; 57344 x 4096: 20.3 against 21.1).
     if (!moe && M == 1 && K == 4096 && rows >= 16384 &&
-        try_plan(valu(1, 32, 2, 1, false), 3, M, N, K, topk, cus, lds_limit, p))
+        try_plan(splitk(1, 32, 1, 2, false), 2, M, N, K, topk, cus, lds_limit, p))
         return true;
     // K = 2048, one token: tall matrices take the staged kernel with 32 lanes and 2 chunks per
     // item (14336 x 2048: 4.9 us against 6.9 us for 64 lanes), the others split K like the
