@@ -1304,62 +1304,84 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
         return;
     const int64_t n_items = ((n_super - 1 - gw) / GW + 1) * nb;
 
-    // Row r of block b: the last block is pulled back to end at row N - 1 (rows computed twice
-    // give identical bits); with fewer than R rows the rows are clamped.
-    auto block_row = [&](uint32_t b, int r) -> int64_t {
+    // Rows of block b: a wave-uniform first row (the last block is pulled back to end at row
+    // N - 1; rows computed twice give identical bits) plus fixed per-lane offsets (with fewer
+    // than R rows, clamped to row N - 1).
+    auto block_row0 = [&](uint32_t b) -> int64_t {
         if (N < R)
-            return r < N ? r : N - 1;
-        const int64_t r0 = (int64_t)b * R + R <= N ? (int64_t)b * R : N - R;
-        return r0 + r;
+            return 0;
+        return (int64_t)b * R + R <= N ? (int64_t)b * R : N - R;
     };
+    auto lane_row = [&](int r) -> int { return N < R && r > N - 1 ? (int)N - 1 : r; };
+    uint32_t woff[U], soff[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int r = lane_row((64 / BR) * u + 4 * h + q);
+        woff[u] = (uint32_t)(r * CPR + bc);
+        soff[u] = (uint32_t)(r * GPR);
+    }
     struct Buf {
         uint4 w[CL][U];
         uint16_t s[CL][U];
     };
-    uint32_t ld_st = (uint32_t)gw;
-    int ld_b = 0;
-    // Item st: virtual entry v = st / n_blocks, block b = st % n_blocks (expert-major).
-    auto split_item = [&](uint32_t st, uint32_t &b, uint32_t &v) {
-        v = st / n_blocks;
-        b = st - v * n_blocks;
+    // Cursors over the items: virtual entry v and block b (expert-major, st = v * n_blocks + b),
+    // advanced by the grid's wave count without divisions after the first item.
+    struct Cursor {
+        uint32_t v, b;
+        int batch;
     };
+    const uint32_t gw_v = (uint32_t)GW / n_blocks, gw_b = (uint32_t)GW % n_blocks;
+    auto advance = [&](Cursor &cur) {
+        if (++cur.batch < nb)
+            return;
+        cur.batch = 0;
+        cur.v += gw_v;
+        cur.b += gw_b;
+        if (cur.b >= n_blocks) {
+            cur.b -= n_blocks;
+            cur.v += 1;
+        }
+    };
+    const Cursor first = {(uint32_t)gw / n_blocks, (uint32_t)gw % n_blocks, 0};
+    Cursor ld = first;
     auto load = [&](Buf &buf) {
-        uint32_t b, v;
-        split_item(ld_st, b, v);
-        const int32_t e = ve_e[v];
+        // past the last item (clamped to a valid entry): loads of valid rows, never consumed
+        const uint32_t v = ld.v < (uint32_t)nve ? ld.v : (uint32_t)nve - 1;
+        const int32_t e = __builtin_amdgcn_readfirstlane(ve_e[v]);
+        const int64_t row0 = (int64_t)(e >= 0 ? e : 0) * N + block_row0(ld.b);
+        const uint4 *wr = pick(e >= 0, qw + row0 * CPR, reinterpret_cast<const uint4 *>(X));
+        const uint16_t *sr = pick(e >= 0, sc + row0 * GPR, X);
+        const uint32_t c0 = (uint32_t)(BR * CL * ld.batch);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t row =
-                (int64_t)(e >= 0 ? e : 0) * N + block_row(b, (64 / BR) * u + 4 * h + q);
-            const uint4 *wr = pick(e >= 0, qw + row * CPR, reinterpret_cast<const uint4 *>(X));
-            const uint16_t *sr = pick(e >= 0, sc + row * GPR, X);
+            // an invalid expert reads the activations (valid memory of K * 2 bytes per row
+            // step's first row: the offsets stay below one row there)
+            const uint32_t wo = e >= 0 ? woff[u] : (uint32_t)bc;
+            const uint32_t so = e >= 0 ? soff[u] : 0u;
 #pragma unroll
-            for (int j = 0; j < CL; ++j) {
-                const int c = bc + BR * (j + CL * ld_b);
-                buf.w[j][u] = load_weights(wr + c);
-                buf.s[j][u] = sr[c >> 2];
+            for (int jj = 0; jj < CL; ++jj) {
+                const uint32_t c = c0 + BR * jj;
+                buf.w[jj][u] = load_weights(wr + wo + c);
+                buf.s[jj][u] = sr[so + ((bc + c) >> 2)];
             }
         }
-        const bool wrap = ld_b + 1 == nb;
-        ld_b = wrap ? 0 : ld_b + 1;
-        ld_st += wrap ? (uint32_t)GW : 0u;
+        advance(ld);
     };
 
     f32x4_t acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
         acc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    uint32_t cp_st = (uint32_t)gw;
-    int cp_b = 0;
+    Cursor cp = first;
     auto compute = [&](const Buf &buf) {
-        uint32_t bb, v;
-        split_item(cp_st, bb, v);
+        const uint32_t v = cp.v;
+        const int cp_b = cp.batch;
         const int32_t e_q = ve_tok[v * MT + q];
         const uint32_t e_t = (uint32_t)(e_q >= 0 ? e_q : ve_tok[v * MT]);   // empty: slot 0
         const int m = (int)__umulhi(e_t, tk_magic);
 #pragma unroll
         for (int j = 0; j < CL; ++j) {
-            const int c = bc + BR * (j + CL * cp_b);
+            const int c = bc + BR * (j + CL * cp_b);   // this lane's chunk
             uint4 xv[4];                 // slot q's activations for chunk c, shared by the steps
 #pragma unroll
             for (int w = 0; w < 4; ++w)
@@ -1389,25 +1411,23 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
             }
         }
         if (cp_b == nb - 1) {
-            const int32_t e = ve_e[v];
-            const int32_t entry = ve_tok[v * MT + q];
+            const int32_t e = __builtin_amdgcn_readfirstlane(ve_e[v]);
+            const int64_t r0 = block_row0(cp.b);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float vv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     vv[r] = sum_over_blocks<BR>(acc[u][r]);
-                if (bc < 4 && entry >= 0) {
+                if (bc < 4 && e_q >= 0) {
                     const float val = bc == 0 ? vv[0] : bc == 1 ? vv[1] : bc == 2 ? vv[2] : vv[3];
-                    Y[(int64_t)entry * N + block_row(bb, (64 / BR) * u + 4 * h + bc)] =
+                    Y[(int64_t)e_q * N + r0 + lane_row((64 / BR) * u + 4 * h + bc)] =
                         e >= 0 ? val : 0.0f;
                 }
                 acc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
-        const bool wrap = cp_b + 1 == nb;
-        cp_b = wrap ? 0 : cp_b + 1;
-        cp_st += wrap ? (uint32_t)GW : 0u;
+        advance(cp);
     };
 
     Buf bufA, bufB;
