@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan.h"
 
 namespace w4a16 {
@@ -354,11 +356,20 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         p = p0 + (rr & (HALF - 1));
         p = p < I ? p : I - 1;
     };
-    auto rows_of = [&](int64_t st, Rows &r) {
+    // Expert id of a slot: from global memory for the first item (no weight load is outstanding
+    // yet, so waiting for it costs nothing extra), from the LDS copy afterwards (a global load
+    // would complete behind the weight loads in flight).
+    auto expert_of = [&](int64_t slot, auto first) -> int32_t {
+        if constexpr (decltype(first)::value)
+            return ids[slot];
+        else
+            return ids_s[slot];
+    };
+    auto rows_of = [&](int64_t st, Rows &r, auto first) {
         if constexpr (MODE == VALU_SWIGLU) {
             int64_t slot, p;
             swiglu_row(st, slot, p);
-            const int32_t e = ids_s[slot];
+            const int32_t e = expert_of(slot, first);
             const bool ok = e >= 0 && e < E;
             const int64_t row = (int64_t)(ok ? e : 0) * N + (rr >= HALF ? I : 0) + p;
             r.w[0] = pick(ok, qw + row * CPR, reinterpret_cast<const uint4 *>(X));
@@ -371,7 +382,7 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             vrow = vrow < rows_total ? vrow : rows_total - 1;
             if (MOE) {
                 const int64_t slot = vrow / N;
-                const int32_t e = ids_s[slot];
+                const int32_t e = expert_of(slot, first);
                 const bool ok = e >= 0 && e < E;
                 const int64_t row = (int64_t)(ok ? e : 0) * N + (vrow - slot * N);
                 r.w[u] = pick(ok, qw + row * CPR, reinterpret_cast<const uint4 *>(X));
@@ -385,10 +396,10 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     // Loads and computes each walk the items in order with their own cursor (row block, batch).
     int64_t ld_st = gw_c;
     int ld_b = 0;
-    auto load = [&](ValuBuf<L, V, U> &buf) {
+    auto load = [&](ValuBuf<L, V, U> &buf, auto first) {
         if constexpr (MOE) {
             Rows r;
-            rows_of(ld_st, r);
+            rows_of(ld_st, r, first);
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 const int c = pr + L * (v + V * ld_b);
@@ -405,7 +416,7 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             int cb = L * V * ld_b;   // first chunk of the batch within its weight row
             if constexpr (MODE == VALU_COMBINE) {
                 const int slot = cb / CPRW;
-                const int32_t e = ids_s[slot];
+                const int32_t e = expert_of(slot, first);
                 const int64_t ee = (e >= 0 && e < E) ? e : 0;
                 wq += ee * N * CPRW;
                 sq += ee * N * GPRW;
@@ -428,39 +439,77 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         ld_st += wrap ? GW : 0;
     };
 
-    ValuBuf<L, V, U> bufA, bufB;
-    if (MODE == VALU_DENSE)
-        load(bufA);     // overlaps the first weights with the activation fetch below
-
-    // ---- stage activations: re-pair, transpose to [j][c], and form per-chunk offsets
+    // Activation words of the first two staging passes are requested first, then the first item's
+    // weights (for expert forms after its expert ids); loads complete in issue order, so staging
+    // below waits only for the activations while the weights are still in flight. Rows of longer
+    // activations (K > 8 * 2 * threads) fetch the rest during staging.
+    constexpr int PF = 2;
+    uint4 xpre[MT][PF];
+#pragma unroll
     for (int t = 0; t < MT; ++t) {
         const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
-        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
-            const uint4 v = xg[w];
-            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
-            float sum = 0.0f;
-            sum = dot2(v.x, 0x3F803F80u, sum);
-            sum = dot2(v.y, 0x3F803F80u, sum);
-            sum = dot2(v.z, 0x3F803F80u, sum);
-            sum = dot2(v.w, 0x3F803F80u, sum);
-            // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
-            sum += dpp_partner(sum, 0);
-            sum += dpp_partner(sum, 1);
-            if ((w & 3) == 0)
-                bs[t * CPR + (w >> 2)] = -kOffset * sum;
+#pragma unroll
+        for (int f = 0; f < PF; ++f) {
+            const int w = threadIdx.x + f * blockDim.x;
+            xpre[t][f] = xg[w < KW ? w : KW - 1];
         }
     }
-    if (MODE != VALU_DENSE)
-        for (int i = threadIdx.x; i < topk; i += blockDim.x) {
+    // Expert ids and router weights for the LDS copy (one per thread; larger topk is read during
+    // staging).
+    int32_t id_pre = 0;
+    float rw_pre = 0.0f;
+    if constexpr (MODE != VALU_DENSE) {
+        const int i = threadIdx.x < topk ? threadIdx.x : topk - 1;
+        id_pre = ids[i];
+        if constexpr (MODE == VALU_COMBINE)
+            rw_pre = rw[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    ValuBuf<L, V, U> bufA, bufB;
+    load(bufA, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- stage activations: re-pair, transpose to [j][c], and form per-chunk offsets
+    auto stage = [&](int t, int w, uint4 v) {
+        xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
+        float sum = 0.0f;
+        sum = dot2(v.x, 0x3F803F80u, sum);
+        sum = dot2(v.y, 0x3F803F80u, sum);
+        sum = dot2(v.z, 0x3F803F80u, sum);
+        sum = dot2(v.w, 0x3F803F80u, sum);
+        // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
+        sum += dpp_partner(sum, 0);
+        sum += dpp_partner(sum, 1);
+        if ((w & 3) == 0)
+            bs[t * CPR + (w >> 2)] = -kOffset * sum;
+    };
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int f = 0; f < PF; ++f) {
+            const int w = threadIdx.x + f * blockDim.x;
+            if (w < KW)
+                stage(t, w, xpre[t][f]);
+        }
+        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
+        for (int w = threadIdx.x + PF * blockDim.x; w < KW; w += blockDim.x)
+            stage(t, w, xg[w]);
+    }
+    if constexpr (MODE != VALU_DENSE) {
+        if ((int)threadIdx.x < topk) {
+            ids_s[threadIdx.x] = id_pre;
+            if constexpr (MODE == VALU_COMBINE)
+                rw_s[threadIdx.x] = (id_pre >= 0 && id_pre < E) ? rw_pre : 0.0f;
+        }
+        for (int i = threadIdx.x + blockDim.x; i < topk; i += blockDim.x) {
             ids_s[i] = ids[i];
-            if (MODE == VALU_COMBINE)
+            if constexpr (MODE == VALU_COMBINE)
                 rw_s[i] = (ids[i] >= 0 && ids[i] < E) ? rw[i] : 0.0f;
         }
+    }
     __syncthreads();
     if (!active)
         return;
-    if (MODE != VALU_DENSE)
-        load(bufA);
 
     float acc[U][MT];
 #pragma unroll
@@ -549,13 +598,13 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     // and then consumes the previous ones.
     int64_t i = 0;
     for (; i + 2 < n_items; i += 2) {
-        load(bufB);
+        load(bufB, std::false_type{});
         compute(bufA);
-        load(bufA);
+        load(bufA, std::false_type{});
         compute(bufB);
     }
     if (i + 1 < n_items) {
-        load(bufB);
+        load(bufB, std::false_type{});
         compute(bufA);
         compute(bufB);
     } else {
