@@ -13,7 +13,9 @@ launch stream, with device synchronisation on both sides.
 Prints one JSON line. `value` is algorithmic bytes (packed weights + fp16 scales + bf16
 activations) per second over the whole step, in GB/s. `roofline` is for the dominant kernel
 (the 28672 x 4096 GEMV): the same bytes over its own average duration, timed the same way on a
-graph of back-to-back launches. `cpu_baseline` is the CPU oracle (single thread, float64) timed
+graph of back-to-back launches; `roofline.launch_floor_us` is the per-launch time of a kernel
+that reads 16 bytes, timed the same way (the part of every call that is not memory time).
+`cpu_baseline` is the CPU oracle (single thread, float64) timed
 on whole steps of the same workload.
 """
 from __future__ import annotations
@@ -197,6 +199,14 @@ def main():
                                                        out=ya), args.steps)
     down_us, _ = graph_avg_us(torch, lambda i: w.gemv(copies[i % R][2], copies[i % R][3], xb1,
                                                        out=yb), args.steps)
+    # ---- launch floor: the same graph timing for back-to-back launches of a kernel that reads
+    # one 16-byte chunk (the streaming-read kernel, one work-group per CU). Every call above
+    # pays this per-launch cost of the command processor (dispatch, completion and the cache
+    # operations between dependent kernels) on top of its memory time.
+    fbuf = torch.zeros(16, dtype=torch.uint8, device=dev)
+    fout = torch.empty(4 * props.multi_processor_count, dtype=torch.int32, device=dev)
+    floor_us, _ = graph_avg_us(torch, lambda i: w.stream_read(
+        fbuf, 16, fout, props.multi_processor_count, 1), args.steps)
     achieved = bytes_a / (gate_us * 1e-6) / 1e9
     plan_a = w.describe_plan(1, da.N, da.K, 0, props.multi_processor_count)
     digest = kernel_source_digest(plan_a)
@@ -241,6 +251,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": bytes_a,
             "avg_launch_us": round(gate_us, 3),
+            "launch_floor_us": round(floor_us, 3),
             "kernel_source_digest": digest,
         },
     }
