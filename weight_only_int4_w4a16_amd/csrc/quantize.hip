@@ -4,38 +4,45 @@
 // round-to-nearest scheme for the format:
 //   per row and 128-wide group: s = fp16(amax / 7) (float32 division, nearest-even, saturating
 //   at 65504), q = clamp(rint(w / s), -8, 7) (float32 division, ties to even), q = 0 when s = 0.
-// The divisions are IEEE float32 divisions (this library is built with correctly rounded
-// float32 division), so every code and scale is a deterministic function of the input bits.
-// Only the scale takes a division per group; a code is first estimated as w * fl(1/s), which is
-// within 7 * 1.5 * 2^-23 < 1.3e-6 of the quotient fl(w / s) (|w / s| <= 7.004), so rounding the
-// estimate gives rint(fl(w / s)) unless it lies within 4e-6 of a half-integer; only those
-// values (about one in 10^5) take the exact division.
+// The scale division is an IEEE float32 division (this library is built with correctly rounded
+// float32 division), so every scale is a deterministic function of the input bits. A code is
+// first estimated from r = 1/s taken with v_rcp_f32 (relative error <= 2^-23): the exact product
+// w * r is within 7.004 * 2^-23 < 8.4e-7 of w / s, which is within 7.004 * 2^-24 < 4.2e-7 of the
+// float32 quotient fl(w / s). One FMA against C = 1.5 * 2^23 rounds w * r to the nearest integer
+// (ties to even) and leaves it in the low mantissa bits of C + q, and a second FMA gives the
+// residual w * r - q with one rounding (error < 3e-8). Where every residual of a lane is at most
+// 1/2 - 4e-6, fl(w / s) lies strictly within 1/2 - 2.7e-6 of q, so q = rint(fl(w / s)); a lane
+// with a residual closer to 1/2 (about one value in 10^5) recomputes its codes with the exact
+// division. The clamp to [-8, 7] is a med3 of C + q against C - 8 and C + 7, and the two's
+// complement nibble is the low 4 bits of C + q (C is a multiple of 16).
 //
-// Layout: a wave quantises 4 groups at a time, 16 lanes per group; lane p of a group loads the
-// 8 bf16 values 8p..8p+7 (16 bytes), so a wave reads 4 x 256 contiguous bytes and writes the 16
-// words of each group as one 64-byte run. The group maximum is reduced with DPP inside the
-// 16-lane row. Memory-bound: 2 bytes read and 0.5 + 2/128 bytes written per weight.
+// Layout: 8 lanes per group, a wave quantises 8 groups at a time; lane p of a group loads the 16-byte
+// slices p and p + 8 (bf16 values 8p..8p+7 and 64+8p..64+8p+7), so each load instruction covers one
+// whole 128-byte line of each of the 8 groups, and writes packed words p and p + 8. The group
+// maximum is reduced with DPP inside each half of a 16-lane row. Memory-bound: 2 bytes read and
+// 0.5 + 2/128 bytes written per weight.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace w4a16 {
 
-__device__ __forceinline__ float row16_max(float v)
+__device__ __forceinline__ float dpp_max(float v, int ctrl_id)
 {
-    // Butterfly maximum over the 16 lanes of a DPP row (quad permutes, half-row and row mirror).
-    int x = __builtin_bit_cast(int, v);
-    x = __builtin_bit_cast(int, fmaxf(v, __builtin_bit_cast(float,
-            __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true))));
-    v = __builtin_bit_cast(float, x);
-    x = __builtin_bit_cast(int, fmaxf(v, __builtin_bit_cast(float,
-            __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true))));
-    v = __builtin_bit_cast(float, x);
-    x = __builtin_bit_cast(int, fmaxf(v, __builtin_bit_cast(float,
-            __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true))));
-    v = __builtin_bit_cast(float, x);
-    x = __builtin_bit_cast(int, fmaxf(v, __builtin_bit_cast(float,
-            __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, true))));
-    return __builtin_bit_cast(float, x);
+    const int x = __builtin_bit_cast(int, v);
+    int y;
+    switch (ctrl_id) {
+    case 0: y = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true); break;    // quad [1,0,3,2]
+    case 1: y = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true); break;    // quad [2,3,0,1]
+    default: y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true); break;  // half-row mirror
+    }
+    return fmaxf(v, __builtin_bit_cast(float, y));
+}
+
+// Maximum over the 8 lanes of each half of a DPP row: the two quad swaps give every lane its
+// quad's maximum, and the half-row mirror pairs each lane with one of the other quad.
+__device__ __forceinline__ float row8_max(float v)
+{
+    return dpp_max(dpp_max(dpp_max(v, 0), 1), 2);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
@@ -44,89 +51,169 @@ __device__ __forceinline__ float bf16_hi(uint32_t w)
     return __builtin_bit_cast(float, w & 0xFFFF0000u);
 }
 
-// One group's codes and scale from the 8 values of lane p (the group's other 120 values sit in
-// the 15 other lanes of the same DPP row).
-__device__ __forceinline__ void quantize_slice(uint4 v, uint32_t &word, uint16_t &sb)
+// Eight codes, each in the low nibble of b[i], packed with value i in bits 4i..4i+3: the low
+// bytes of the even values go to one word and those of the odd values to another (v_perm), and
+// one bit-field insert keeps the low nibble of each byte of the first and the low nibble of each
+// byte of the second shifted up by 4.
+__device__ __forceinline__ uint32_t pack_nibbles(const uint32_t *b)
 {
-    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    // perm(hi, lo, sel): selector bytes 0-3 take bytes of lo, 4-7 bytes of hi, 0x0C gives zero
+    const uint32_t e01 = __builtin_amdgcn_perm(b[2], b[0], 0x0C0C0400u);   // [b0, b2, 0, 0]
+    const uint32_t e23 = __builtin_amdgcn_perm(b[6], b[4], 0x04000C0Cu);   // [0, 0, b4, b6]
+    const uint32_t o01 = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0400u);   // [b1, b3, 0, 0]
+    const uint32_t o23 = __builtin_amdgcn_perm(b[7], b[5], 0x04000C0Cu);   // [0, 0, b5, b7]
+    const uint32_t even = e01 | e23;
+    const uint32_t odd = o01 | o23;
+    return (even & 0x0F0F0F0Fu) | ((odd << 4) & 0xF0F0F0F0u);
+}
+
+// One group's scale and this lane's two packed words from its 16 values (slices a and b); the
+// group's other 112 values sit in the 7 other lanes of the same half row.
+__device__ __forceinline__ void quantize_lane(uint4 a, uint4 b, uint32_t &w0, uint32_t &w1,
+                                              uint16_t &sb)
+{
+    float f[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
+                   bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
+                   bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
+                   bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 16; ++i)
         amax = fmaxf(amax, fabsf(f[i]));
-    amax = row16_max(amax);
+    amax = row8_max(amax);
     const float s32 = amax / 7.0f;
     sb = __builtin_bit_cast(uint16_t, (_Float16)s32);   // nearest even
     if ((sb & 0x7FFFu) >= 0x7C00u && s32 == s32)        // overflow: saturate
         sb = (uint16_t)((sb & 0x8000u) | 0x7BFFu);
     const float s = (float)__builtin_bit_cast(_Float16, sb);
-    // rcp = 0 for a zero scale makes every estimate 0, so every code 0, as defined.
-    const float rcp = s != 0.0f ? 1.0f / s : 0.0f;
-    word = 0;
+    // r = 0 for a zero scale makes every code 0, as defined (and every residual 0).
+    const float r = s != 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+    constexpr float C = 12582912.0f;   // 1.5 * 2^23: C + q is exact for |q| < 2^22
+    float y[16];
+    float emax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float t = f[i] * rcp;
-        float r = rintf(t);
-        if (fabsf(t - r) > 0.5f - 4e-6f)            // near a rounding boundary: divide
-            r = rintf(f[i] / s);
-        const int q = (int)__builtin_amdgcn_fmed3f(r, -8.0f, 7.0f);
-        word |= ((uint32_t)q & 0xFu) << (4 * i);
+    for (int i = 0; i < 16; ++i) {
+        y[i] = fmaf(f[i], r, C);
+        emax = fmaxf(emax, fabsf(fmaf(f[i], r, C - y[i])));
     }
+    if (emax > 0.5f - 4e-6f) {
+        // near a rounding boundary: the exact quotient decides (s > 0 here)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            y[i] = C + __builtin_amdgcn_fmed3f(rintf(f[i] / s), -8.0f, 7.0f);
+    }
+    uint32_t q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        q[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(y[i], C - 8.0f, C + 7.0f));
+    w0 = pack_nibbles(q);
+    w1 = pack_nibbles(q + 8);
 }
 
-// A wave takes QU steps of 4 groups per pass: all QU loads are issued before the first group is
-// quantised, so each lane keeps QU x 16 bytes in flight.
-constexpr int QU = 4;
+// A wave takes QU steps of 8 groups per pass and works on one pass while the loads of the next
+// are in flight (two register buffers), so each lane keeps up to 2 x QU x 32 bytes requested.
+#ifndef W4A16_QUANT_QU
+#define W4A16_QUANT_QU 2
+#endif
+constexpr int QU = W4A16_QUANT_QU;
+constexpr int kGroupsPerWave = 8;
+
+struct QuantBuf {
+    uint4 a[QU], b[QU];
+};
 
 __global__ void __launch_bounds__(256)
 quantize_pack_kernel(const uint16_t *__restrict__ W, int64_t ldw, uint32_t *__restrict__ qw,
                      uint16_t *__restrict__ sc, int64_t N, int32_t K)
 {
     const int lane = threadIdx.x & 63;
-    const int gl = lane >> 4;     // group of the wave's four
-    const int pl = lane & 15;     // 16-byte slice of the group
+    const int gl = lane >> 3;     // group of the wave's eight
+    const int pl = lane & 7;      // slices pl and pl + 8 of the group
     const int64_t gpr = K >> 7;
     const int64_t groups = N * gpr;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
-    for (int64_t g0 = wave * 4; g0 < groups; g0 += waves * 4 * QU) {
-        uint4 v[QU];
-        int64_t n[QU], j[QU];
-        bool ok[QU];
+    const int64_t stride = waves * kGroupsPerWave;
+    const int64_t first = wave * kGroupsPerWave;
+    if (first >= groups)
+        return;
+    // passes of this wave: the first groups of its passes are first + p * stride * QU < groups
+    const int64_t n_pass = (groups - 1 - first) / (stride * QU) + 1;
+    // Group of step u of pass p for this lane, and whether it exists (past the end a lane
+    // re-reads the last group and stores nothing). Group indices fit in 32 bits (checked by the
+    // host), so the row is a 32-bit division.
+    auto group_of = [&](int64_t p, int u, uint32_t &n, uint32_t &j) -> bool {
+        const int64_t g = first + (p * QU + u) * stride + gl;
+        const bool ok = g < groups;
+        const uint32_t gc = (uint32_t)(ok ? g : groups - 1);
+        n = gc / (uint32_t)gpr;
+        j = gc - n * (uint32_t)gpr;
+        return ok;
+    };
+    auto load = [&](QuantBuf &buf, int64_t p) {
 #pragma unroll
         for (int u = 0; u < QU; ++u) {
-            const int64_t g = g0 + (int64_t)u * waves * 4 + gl;
-            ok[u] = g < groups;
-            // past the end: re-read the last group. Group indices fit in 32 bits (checked by
-            // the host), so the row is a 32-bit division.
-            const uint32_t gc = (uint32_t)(ok[u] ? g : groups - 1);
-            const uint32_t nn = gc / (uint32_t)gpr;
-            n[u] = nn;
-            j[u] = gc - nn * (uint32_t)gpr;
-            v[u] = reinterpret_cast<const uint4 *>(W + n[u] * ldw + j[u] * 128)[pl];
+            uint32_t n, j;
+            group_of(p, u, n, j);
+            const uint4 *src = reinterpret_cast<const uint4 *>(W + (int64_t)n * ldw + (int64_t)j * 128);
+            buf.a[u] = src[pl];
+            buf.b[u] = src[pl + 8];
         }
+    };
+    auto compute = [&](const QuantBuf &buf, int64_t p) {
 #pragma unroll
         for (int u = 0; u < QU; ++u) {
-            uint32_t word;
+            uint32_t w0, w1;
             uint16_t sb;
-            quantize_slice(v[u], word, sb);
-            if (ok[u]) {
-                qw[n[u] * (K >> 3) + j[u] * 16 + pl] = word;
+            quantize_lane(buf.a[u], buf.b[u], w0, w1, sb);
+            uint32_t n, j;
+            if (group_of(p, u, n, j)) {
+                uint32_t *dst = qw + (int64_t)n * (K >> 3) + (int64_t)j * 16;
+                dst[pl] = w0;
+                dst[pl + 8] = w1;
                 if (pl == 0)
-                    sc[n[u] * gpr + j[u]] = sb;
+                    sc[(int64_t)n * gpr + j] = sb;
             }
         }
+    };
+    QuantBuf bufA, bufB;
+    load(bufA, 0);
+    int64_t p = 0;
+    for (; p + 2 < n_pass; p += 2) {
+        load(bufB, p + 1);
+        compute(bufA, p);
+        load(bufA, p + 2);
+        compute(bufB, p + 1);
+    }
+    if (p + 1 < n_pass) {
+        load(bufB, p + 1);
+        compute(bufA, p);
+        compute(bufB, p + 1);
+    } else {
+        compute(bufA, p);
     }
 }
 
 hipError_t launch_quantize(const uint16_t *W, int64_t ldw, uint32_t *qw, uint16_t *sc, int64_t N,
                            int32_t K, int cus, hipStream_t stream)
 {
+    // Every wave makes the same number of passes of QU steps of 8 groups: the fewest passes
+    // that the resident waves (work-groups of 4 waves per CU, as many as the kernel's registers
+    // allow) can cover, then as few waves as that allows, so no work-group waits for a slot.
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, reinterpret_cast<const void *>(quantize_pack_kernel), 256, 0) != hipSuccess ||
+            n < 1)
+            n = 1;
+        return n;
+    }();
     const int64_t groups = N * (K / 128);
-    int64_t blocks = (groups + 15) / 16;           // 4 waves x 4 groups per work-group
-    const int64_t cap = (int64_t)cus * 8;
-    if (blocks > cap)
-        blocks = cap;
+    const int64_t steps = (groups + kGroupsPerWave - 1) / kGroupsPerWave;
+    const int64_t cap_waves = (int64_t)cus * per_cu * 4;
+    const int64_t passes = (steps + QU * cap_waves - 1) / (QU * cap_waves);
+    const int64_t waves = (steps + QU * passes - 1) / (QU * passes);
+    int64_t blocks = (waves + 3) / 4;
     if (blocks < 1)
         blocks = 1;
     void *args[] = {(void *)&W, (void *)&ldw, (void *)&qw, (void *)&sc, (void *)&N, (void *)&K};
