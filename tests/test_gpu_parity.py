@@ -240,6 +240,17 @@ def test_moe_reads_only_selected_experts():
     within(y, ref, mag, "c4 poisoned unselected experts")
 
 
+@pytest.mark.parametrize("E,N,K,topk", [(320, 8, 256, 300), (6, 50, 8192, 3)])
+def test_moe_many_slots_and_long_rows(E, N, K, topk):
+    """More slots than the 256 threads that stage the expert ids, and activations longer than
+    two staging passes (K = 8192), on the grouped-expert kernel."""
+    m = synthetic.moe(E=E, N=N, K=K, topk=topk, seed=9, config_id=805)
+    print(f"moe E={E} N={N} K={K} topk={topk} plan={w.describe_plan(1, N, K, topk)}", flush=True)
+    y = host(w.moe_gemv(words(m.qweight), f16(m.scales), i32(m.ids), bf16(m.x)))
+    ref, mag = oracle.moe_gemv(m.qweight, m.scales, m.ids, m.x, K)
+    within(y, ref, mag, f"moe E={E} N={N} K={K} top{topk}")
+
+
 def test_moe_invalid_and_repeated_ids():
     E, N, K = 5, 96, 2304
     m = synthetic.moe(E=E, N=N, K=K, topk=2, seed=3, config_id=803)

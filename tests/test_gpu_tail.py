@@ -75,8 +75,10 @@ def check_out(got, ref, mag, what, extra_rel=0.0):
 # (E, I, K, topk): K = 2304 takes 8 lanes x 3 chunks, K = 2048 32 lanes (one gate row per
 # wave half), K = 128 4 lanes with I below the 8 gate rows of a wave step; I not a multiple of
 # the gate rows per step in every case but one.
+# The last two: activations longer than two staging passes of 256 threads (K = 8192), and more
+# slots than threads (ids staged past the first 256).
 SWIGLU_SHAPES = [(6, 64, 384, 3), (4, 3, 128, 2), (5, 37, 2304, 4), (3, 100, 2048, 2),
-                 (2, 1000, 4096, 1), (9, 256, 2304, 8)]
+                 (2, 1000, 4096, 1), (9, 256, 2304, 8), (3, 64, 8192, 2), (300, 8, 256, 300)]
 
 
 @pytest.mark.parametrize("E,I,K,topk", SWIGLU_SHAPES)
@@ -106,9 +108,10 @@ def test_swiglu_invalid_and_repeated_ids():
 
 
 # (E, I, H, topk): I = 1024 takes 32 lanes per row, I = 384 4 lanes; H below and above the
-# rows of one wave step.
+# rows of one wave step. The last: 300 slots (more than the 256 threads that stage ids and
+# router weights) over a 38400-long activation, on the staged combine form.
 DOWN_SHAPES = [(6, 256, 300, 3), (4, 128, 1, 1), (5, 384, 77, 4), (12, 1024, 2304, 8),
-               (3, 2048, 129, 2), (40, 512, 1000, 16)]
+               (3, 2048, 129, 2), (40, 512, 1000, 16), (300, 128, 20, 300)]
 
 
 @pytest.mark.parametrize("E,I,H,topk", DOWN_SHAPES)
