@@ -222,10 +222,11 @@ def test_valid_arguments_reach_the_device_check_only():
     (1, 4096, 14336, 0, "splitk "), (1, 8192, 8192, 0, "splitk "), (1, 163840, 2304, 0, "valu "),
     (1, 2048, 2304, 8, "valu_moe"), (1, 5, 128, 0, "valu "), (1, 64, 65536, 0, "splitk "),
     (2, 8192, 8192, 0, "splitk "),
-    (4, 163840, 2304, 0, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=3 row_steps=1 "
-                         "blocks_per_row=8"),
-    (2, 163840, 2304, 0, "mfma4x4x4_splitk token_groups=1"),
-    (8, 163840, 2304, 0, "mfma16x16x32_lds_lines"), (3, 100, 384, 0, "valu "),
+    (4, 163840, 2304, 0, "mfma16x16x32_lds8_lines tiles_per_wave=1 k_split=1 groups_per_item=2 "
+                         "threads=512 blocks=512"),
+    (6, 163840, 2304, 0, "mfma16x16x32_lds8_lines"),
+    (2, 163840, 2304, 0, "mfma16x16x32_lds8_lines"), (4, 32768, 2048, 0, "mfma4x4x4_splitk"),
+    (8, 163840, 2304, 0, "mfma16x16x32_lds8_lines"), (3, 100, 384, 0, "valu "),
     (4, 28672, 4096, 0, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=2 row_steps=2 "
                         "blocks_per_row=16"),
     (3, 8192, 8192, 0, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=2"),

@@ -180,6 +180,21 @@ def test_batched_mfma4_plans(M, N, K):
     within(Y, ref, mag, f"batched M={M} {N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 26624, 2304), (3, 26624, 2304), (5, 26700, 2304),
+                                   (7, 26700, 2304), (8, 26880, 1536), (4, 30000, 256)])
+def test_batched_staged_8_slot_plans(M, N, K):
+    """The staged whole-line 16x16x32 form with 8 token slots (2-8 tokens, tall matrices): MFMA
+    rows 8-15 read slots 0-7 again and are never stored; ragged row counts pull the last block
+    back."""
+    plan = w.describe_plan(M, N, K)
+    assert plan.startswith("mfma16x16x32_lds8_lines"), plan
+    d = synthetic.dense(N=N, K=K, seed=M * 11 + N, M=M, config_id=806)
+    print(f"batched M={M} {N}x{K} plan={plan}", flush=True)
+    Y = host(w.gemv_batched(words(d.qweight), f16(d.scales), bf16(d.x)))
+    ref, mag = oracle.gemv_batched(d.qweight, d.scales, d.x, K)
+    within(Y, ref, mag, f"batched M={M} {N}x{K}")
+
+
 def test_batched_rows_match_single_token():
     N, K, M = 500, 8192, 16
     d = synthetic.dense(N=N, K=K, seed=9, M=M, config_id=802)

@@ -1583,8 +1583,11 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                  const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
                  int32_t M, int64_t N, int32_t K)
 {
-    constexpr bool XLDS = XMODE == 1 || XMODE == 2;   // activations staged in LDS
-    constexpr bool LINES = XMODE == 2;         // whole-line weight loads permuted through LDS
+    constexpr bool XLDS = XMODE == 1 || XMODE == 2 || XMODE == 4;   // activations staged in LDS
+    constexpr bool LINES = XMODE == 2 || XMODE == 4;   // whole-line weight loads permuted via LDS
+    // Token slots staged: 16, or 8 when M <= 8 (XMODE 4), where MFMA rows 8-15 read slots 0-7
+    // again; their outputs are never stored.
+    constexpr int SLOTS = XMODE == 4 ? 8 : 16;
     constexpr bool GLINES = XMODE == 3;        // global activations, whole-line loads via LDS
     static_assert(!LINES || (T == 1 && GU % 2 == 0), "line loads pair the groups of one tile");
     static_assert(!GLINES || GU % 2 == 0, "line loads pair the groups of an item");
@@ -1677,9 +1680,9 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
 
     if constexpr (XLDS) {
         static_assert(KS == 1, "staged activations serve whole rows");
-        uint4 *xl = lds;                                             // [GPR][4][64]
-        float *offl = reinterpret_cast<float *>(lds + GPR * 256);   // [GPR][16]
-        uint4 *stage = lds + GPR * 260 + wave * GU * 64;             // LINES: [GU/2][2][64]
+        uint4 *xl = lds;                                                 // [GPR][4][4*SLOTS]
+        float *offl = reinterpret_cast<float *>(lds + GPR * 16 * SLOTS);   // [GPR][16]
+        uint4 *stage = lds + GPR * (16 * SLOTS + 4) + wave * GU * 64;     // LINES: [GU/2][2][64]
         // A flat sequence of (row block, run of GU groups) items for this work-group.
         const int cpr_items = GPR / GU;
         const bool active = blockIdx.x < n_rb;
@@ -1712,10 +1715,10 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         Buf bufA, bufB;
         load(bufA);
 
-        // Stage the fragments of all 16 token slots and the per-(group, token) offsets.
-        for (int idx = threadIdx.x; idx < GPR * 256; idx += blockDim.x) {
-            const int s = idx >> 8, j = (idx >> 6) & 3, l = idx & 63;
-            const int m = l & 15, gg = l >> 4;
+        // Stage the fragments of the token slots and the per-(group, token) offsets.
+        for (int idx = threadIdx.x; idx < GPR * 16 * SLOTS; idx += blockDim.x) {
+            const int s = idx / (16 * SLOTS), j = (idx / (4 * SLOTS)) & 3, l = idx & (4 * SLOTS - 1);
+            const int m = l & (SLOTS - 1), gg = l / SLOTS;
             const int tm = m < M ? m : M - 1;
             const uint4 v = reinterpret_cast<const uint4 *>(X + (int64_t)tm * ldx)[16 * s + 4 * gg + j];
             xl[idx] = pair_activations(v);
@@ -1772,7 +1775,7 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 bf16x8_t xb[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    xb[j] = as_bf16x8(xl[(s * 4 + j) * 64 + lane]);
+                    xb[j] = as_bf16x8(xl[(s * 4 + j) * (4 * SLOTS) + (i & (SLOTS - 1)) + SLOTS * g]);
                 const float4 o4 = *reinterpret_cast<const float4 *>(offl + s * 16 + 4 * g);
                 const f32x4_t off = {o4.x, o4.y, o4.z, o4.w};
                 float scv[T];
@@ -2073,8 +2076,9 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
         return launch_splitk_t<1, L_, CL_, 1, true>(a, p, stream);
 
 #define W4A16_MFMA_CASE(T_, KS_, XL_, GU_, WPB_)                                             \
-    if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ == 1 || XL_ == 2) &&                      \
-        p.lines == (XL_ >= 2) && p.V == GU_ && p.threads == 64 * WPB_)                        \
+    if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ == 1 || XL_ == 2 || XL_ == 4) &&          \
+        p.lines == (XL_ >= 2) && p.slots8 == (XL_ == 4) && p.V == GU_ &&                      \
+        p.threads == 64 * WPB_)                                                              \
         return launch_mfma_t<T_, KS_, XL_, GU_, WPB_>(a, p, stream);
 
 #define W4A16_MFMA4_CASE(TG_, CL_, U_, BR_)                                                  \

@@ -35,8 +35,9 @@ bool plan_instantiated(const Plan &p)
         p.mode == PLAN_MODE_COMBINE)                                                          \
         return true;
 #define W4A16_MFMA_MATCH(T_, KS_, XL_, GU_, WPB_)                                            \
-    if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ && p.xlds == (XL_ == 1 || XL_ == 2) && \
-        p.lines == (XL_ >= 2) && p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))    \
+    if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ &&                                     \
+        p.xlds == (XL_ == 1 || XL_ == 2 || XL_ == 4) && p.lines == (XL_ >= 2) &&               \
+        p.slots8 == (XL_ == 4) && p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))     \
         return true;
 #define W4A16_MOE_BATCHED_MATCH(L_, V_)                                                       \
     if (p.kind == PLAN_MOE_BATCHED && p.L == L_ && p.V == V_)                                   \
@@ -198,13 +199,16 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
             return false;
         if (p->lines && (p->V % 2 != 0 || (p->xlds && p->T != 1)))
             return false;
+        if (p->slots8 && (M > 8 || !p->xlds || !p->lines))
+            return false;
         const int64_t rows_per_block = 16LL * p->T * (wpb / p->KS);
         const int64_t row_blocks = (N + rows_per_block - 1) / rows_per_block;
         if (p->xlds) {
             // 16 token slots of activation fragments (16 bytes per lane, word and group) plus
             // one fp32 offset per (group, token); with line loads, one 1 KiB staging slot per
             // group of an item and wave.
-            p->lds_bytes = gpr * 4096 + gpr * 64 + (p->lines ? (int64_t)wpb * p->V * 1024 : 0);
+            p->lds_bytes = gpr * (p->slots8 ? 2048 : 4096) + gpr * 64 +
+                           (p->lines ? (int64_t)wpb * p->V * 1024 : 0);
             if (p->lds_bytes > lds_limit)
                 return false;
             int per_cu = blocks_per_cu;
@@ -395,6 +399,27 @@ static bool mfma4_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, 
     return try_plan(c, bpc, M, N, K, 0, cus, lds_limit, p);
 }
 
+// The staged whole-line MFMA form with 8 token slots (M <= 8), 2 groups per item and 8 waves per
+// work-group, on matrices with enough 128-row blocks to fill the chip, when two work-groups fit
+// in one CU's LDS: halving the staged activations doubles the waves per CU.
+static bool mfma_slots8_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, Plan *p)
+{
+    const int64_t gpr = K / 128;
+    if (M > 8 || N / 128 < (int64_t)cus * 4 / 5 || gpr % 2 != 0 ||
+        2 * (gpr * 2048 + gpr * 64 + 8 * 2 * 1024) > lds_limit)
+        return false;
+    Plan c{};
+    c.kind = PLAN_MFMA;
+    c.T = 1;
+    c.KS = 1;
+    c.V = 2;
+    c.xlds = true;
+    c.lines = true;
+    c.slots8 = true;
+    c.threads = 512;
+    return try_plan(c, 2, M, N, K, 0, cus, lds_limit, p);
+}
+
 // Whether 3 or 4 tokens are better served by the MFMA kernel than by the VALU ones: tall
 // matrices whose rows are not a multiple of 2048 values (the split-K VALU kernel's shapes) and
 // hold an even number of groups (whole-line loads), where decoding each weight once for all tokens on the matrix cores beats 3-4 dot products
@@ -431,6 +456,14 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     // longer rows below.
     if (!moe && M == 1 && K == 2048 && rows >= 8192 &&
         try_plan(valu(1, 32, 2, 1, false), 4, M, N, K, topk, cus, lds_limit, p))
+        return true;
+    // 2-8 tokens on tall matrices (at least 0.8 x CUs blocks of 128 rows) whose rows are not a
+    // multiple of 2048 values: the staged whole-line 16x16x32 form with 8 token slots and 2 groups
+    // per item, where two 8-wave work-groups fit in one CU's LDS (163840 x 2304, same-box A/B:
+    // 33.0 us at 2 tokens and 34.3 at 4 against 34.4 and 37.0 for the 4x4x4 kernel; 35.1 at 5
+    // and 37.2 at 8 against 38.7 and 39.6 with 16 slots staged).
+    if (!moe && M >= 2 && M <= 8 && K % 2048 != 0 &&
+        mfma_slots8_plan(M, N, K, cus, lds_limit, p))
         return true;
     // 3-4 tokens: the 4x4x4-MFMA split-K kernel wherever its lane layout fits the row.
     if (!moe && M >= 3 && M <= 4 && mfma4_plan(M, N, K, cus, lds_limit, p))
@@ -664,7 +697,9 @@ int describe_plan(const Plan &p, char *buf, size_t len)
         n = snprintf(buf, len,
                      "mfma16x16x32%s tiles_per_wave=%d k_split=%d groups_per_item=%d threads=%d "
                      "blocks=%lld lds=%lld",
-                     p.lines ? (p.xlds ? "_lds_lines" : "_lines") : p.xlds ? "_lds" : "", p.T,
+                     p.lines ? (p.xlds ? (p.slots8 ? "_lds8_lines" : "_lds_lines") : "_lines")
+                             : p.xlds ? "_lds" : "",
+                     p.T,
                      p.KS, p.V, p.threads,
                      (long long)p.blocks, (long long)p.lds_bytes);
     else

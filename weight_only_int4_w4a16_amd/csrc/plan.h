@@ -60,13 +60,15 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
 
 // MFMA kernels: X(16-row tiles per wave, waves splitting K, activation mode, groups per item,
 // waves per work-group). Activation mode: 0 from global memory, 1 staged in LDS, 2 staged with
-// whole-line weight loads, 3 from global memory with whole-line weight and activation loads.
+// whole-line weight loads, 3 from global memory with whole-line weight and activation loads,
+// 4 as 2 with 8 token slots staged (M <= 8).
 #ifndef W4A16_MFMA_CONFIGS
 #define W4A16_MFMA_CONFIGS(X)                                                                \
     X(1, 1, 1, 6, 8) X(1, 1, 1, 4, 8) X(1, 1, 1, 2, 8) X(1, 1, 1, 1, 8)                       \
     X(1, 1, 2, 6, 8) X(1, 1, 2, 4, 8) X(1, 1, 2, 2, 8) X(1, 1, 2, 6, 4) X(1, 1, 2, 4, 4)      \
     X(1, 1, 2, 2, 4) X(2, 4, 3, 2, 4) X(1, 8, 3, 2, 8) X(4, 4, 3, 2, 4)                      \
-    X(2, 4, 0, 2, 4) X(2, 2, 0, 2, 4) X(2, 1, 0, 2, 4) X(1, 1, 0, 2, 4) X(1, 1, 0, 1, 4)
+    X(2, 4, 0, 2, 4) X(2, 2, 0, 2, 4) X(2, 1, 0, 2, 4) X(1, 1, 0, 2, 4) X(1, 1, 0, 1, 4)      \
+    X(1, 1, 4, 2, 8)
 #endif
 
 // 4x4x4-MFMA split-K kernels for 2..8 tokens: X(token groups of 4, chunks per lane, row steps per
@@ -85,6 +87,7 @@ struct Plan {
     int T, KS;         // MFMA: 16-row tiles per wave, waves splitting K (V: groups per item)
     bool xlds;         // MFMA: activations of all 16 token slots staged in LDS
     bool lines;        // MFMA (staged activations): whole-line weight loads permuted via LDS
+    bool slots8;       // MFMA (staged, whole lines, M <= 8): 8 token slots staged instead of 16
     bool moe;          // rows through expert ids (grouped and SwiGLU forms)
     int mode;          // PlanMode (staged VALU)
     int64_t kr;        // combine form: length of one weight row (K is the activation length)
