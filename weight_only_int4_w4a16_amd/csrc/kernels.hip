@@ -1098,28 +1098,58 @@ __device__ void moe_group_entries(const int32_t *__restrict__ ids, int P, int32_
 }
 
 // Activations of every token staged re-paired as [token][word j][chunk] (16 bytes each), with
-// the per-chunk offsets -136 * sum(x) in bs[token][chunk]. Ends without a barrier.
+// the per-chunk offsets -136 * sum(x) in bs[token][chunk]. The staging loop runs over the flat
+// (token, word) index; its first kMoeXPre passes use words requested by moe_prefetch_activations
+// before the expert grouping, so their latency overlaps the id load and the grouping, and only
+// the rest (more than kMoeXPre * threads words) is loaded here. Ends without a barrier.
+constexpr int kMoeXPre = 2;
+
+__device__ __forceinline__ void moe_prefetch_activations(const uint16_t *__restrict__ X,
+                                                         int64_t ldx, int M, int K,
+                                                         uint4 (&pre)[kMoeXPre])
+{
+    const int KW = K >> 3;
+    const int total = M * KW;
+#pragma unroll
+    for (int f = 0; f < kMoeXPre; ++f) {
+        int idx = threadIdx.x + f * blockDim.x;
+        idx = idx < total ? idx : total - 1;   // past the end: re-read the last word, unused
+        const int t = idx / KW;
+        pre[f] = reinterpret_cast<const uint4 *>(X + t * ldx)[idx - t * KW];
+    }
+}
+
 __device__ void moe_stage_activations(const uint16_t *__restrict__ X, int64_t ldx, int M, int K,
-                                      uint4 *xs, float *bs)
+                                      uint4 *xs, float *bs, const uint4 (&pre)[kMoeXPre])
 {
     const int KW = K >> 3;
     const int CPR = K >> 5;
-    for (int t = 0; t < M; ++t) {
-        const uint4 *xg = reinterpret_cast<const uint4 *>(X + t * ldx);
-        for (int w = threadIdx.x; w < KW; w += blockDim.x) {
-            const uint4 v = xg[w];
-            xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
-            float sum = 0.0f;
-            sum = dot2(v.x, 0x3F803F80u, sum);
-            sum = dot2(v.y, 0x3F803F80u, sum);
-            sum = dot2(v.z, 0x3F803F80u, sum);
-            sum = dot2(v.w, 0x3F803F80u, sum);
-            // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
-            sum += dpp_partner(sum, 0);
-            sum += dpp_partner(sum, 1);
-            if ((w & 3) == 0)
-                bs[t * CPR + (w >> 2)] = -kOffset * sum;
-        }
+    const int total = M * KW;
+    // The four words of a chunk sit in four consecutive lanes and the same token (KW and the
+    // thread count are multiples of 16), and a quad is either all below `total` or all above.
+    auto stage = [&](int idx, uint4 v) {
+        const int t = idx / KW;
+        const int w = idx - t * KW;
+        xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
+        float sum = 0.0f;
+        sum = dot2(v.x, 0x3F803F80u, sum);
+        sum = dot2(v.y, 0x3F803F80u, sum);
+        sum = dot2(v.z, 0x3F803F80u, sum);
+        sum = dot2(v.w, 0x3F803F80u, sum);
+        sum += dpp_partner(sum, 0);
+        sum += dpp_partner(sum, 1);
+        if ((w & 3) == 0)
+            bs[t * CPR + (w >> 2)] = -kOffset * sum;
+    };
+#pragma unroll
+    for (int f = 0; f < kMoeXPre; ++f) {
+        const int idx = threadIdx.x + f * blockDim.x;
+        if (idx < total)
+            stage(idx, pre[f]);
+    }
+    for (int idx = threadIdx.x + kMoeXPre * blockDim.x; idx < total; idx += blockDim.x) {
+        const int t = idx / KW;
+        stage(idx, reinterpret_cast<const uint4 *>(X + t * ldx)[idx - t * KW]);
     }
 }
 
@@ -1171,10 +1201,12 @@ gemv_moe_batched_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict
     int32_t *ve_tok = ve_e + P;                                     // [P][MT] entries or -1
     int32_t *nve_s = ve_tok + P * MT;                               // [1]
 
+    uint4 xpre[kMoeXPre];
+    moe_prefetch_activations(X, ldx, M, K, xpre);
     moe_group_entries<MT>(ids, P, E, key_s, first_s, rank_s, cnt_s, vbase_s, ve_e, ve_tok,
                           nve_s);
     __syncthreads();   // the grouping scratch is overwritten by the activations below
-    moe_stage_activations(X, ldx, M, K, xs, bs);
+    moe_stage_activations(X, ldx, M, K, xs, bs, xpre);
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
@@ -1327,10 +1359,12 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
     int32_t *ve_e = reinterpret_cast<int32_t *>(bs + M * CPR);    // [P]
     int32_t *ve_tok = ve_e + P;                                     // [P][MT]
     int32_t *nve_s = ve_tok + P * MT;                               // [1]
+    uint4 xpre[kMoeXPre];
+    moe_prefetch_activations(X, ldx, M, K, xpre);
     moe_group_entries<MT>(ids, P, E, key_s, key_s + P, key_s + 2 * P, key_s + 3 * P,
                           key_s + 4 * P, ve_e, ve_tok, nve_s);
     __syncthreads();   // the grouping scratch is overwritten by the activations below
-    moe_stage_activations(X, ldx, M, K, xs, bs);
+    moe_stage_activations(X, ldx, M, K, xs, bs, xpre);
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
