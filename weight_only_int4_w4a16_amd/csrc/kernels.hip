@@ -1059,24 +1059,29 @@ __device__ void moe_group_entries(const int32_t *__restrict__ ids, int P, int32_
             ve_tok[i * MT + j] = -1;
     }
     __syncthreads();
+    // One pass over all P keys per entry, four keys per LDS read (the reads past P stay inside
+    // the scratch arrays and are masked): the group's first entry f, this entry's rank r among
+    // the earlier ones, and the group size c.
+    const int4 *key4 = reinterpret_cast<const int4 *>(key_s);
     for (int i = threadIdx.x; i < P; i += blockDim.x) {
         const int32_t k = key_s[i];
-        int f = i, r = 0;
-        for (int j = i - 1; j >= 0; --j)
-            if (key_s[j] == k) {
-                f = j;
-                ++r;
+        int f = i, r = 0, c = 0;
+        for (int j0 = 0; j0 < P; j0 += 4) {
+            const int4 kk = key4[j0 >> 2];
+            const int32_t kv[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + q;
+                const bool m = j < P && kv[q] == k;
+                const bool before = m && j < i;
+                f = (before && r == 0) ? j : f;
+                r += before ? 1 : 0;
+                c += m ? 1 : 0;
             }
+        }
         first_s[i] = f;
         rank_s[i] = r;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        int c = 0;
-        if (first_s[i] == i)
-            for (int q = i; q < P; ++q)
-                c += key_s[q] == key_s[i];
-        cnt_s[i] = (c + MT - 1) / MT;      // virtual entries of the group (0 unless first)
+        cnt_s[i] = f == i ? (c + MT - 1) / MT : 0;   // virtual entries of the group (at its first)
     }
     __syncthreads();
     // Virtual entries of the groups whose first entry precedes i, summed in entry order.
