@@ -61,6 +61,51 @@ def test_graph_replays_match_eager_calls():
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
 
 
+def test_graph_replays_of_tail_and_quantise_match_eager_calls():
+    """The expert tail (SwiGLU gate+up, then the down projection with the router-weighted sum)
+    and quantise-and-pack, captured once and replayed with new inputs between replays."""
+    d = synthetic.moe_tail(10, 256, 300, 2304, 4, 5, config_id=962)
+    qg = words(d.gu_qweight)
+    sg = f16(d.gu_scales)
+    qd = words(d.down_qweight)
+    sd = f16(d.down_scales)
+    x = bf16(d.x).clone()
+    ids = torch.from_numpy(d.ids).cuda()
+    rw = torch.from_numpy(d.route_w).cuda()
+    h = torch.empty((4, 256), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(300, dtype=torch.float32, device="cuda")
+    wq = bf16(synthetic.draw_acts(np.random.default_rng(4), (96, 1024))).clone()
+    qo = torch.empty((96, 128), dtype=torch.int32, device="cuda")
+    so = torch.empty((96, 8), dtype=torch.float16, device="cuda")
+
+    def calls():
+        w.moe_gemv_swiglu(qg, sg, ids, x, out=h)
+        w.moe_down_combine(qd, sd, ids, rw, h, out=out)
+        w.quantize_pack(wq, out=(qo, so))
+
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    rng = np.random.default_rng(5)
+    for rep in range(4):
+        x.copy_(bf16(synthetic.draw_acts(rng, (2304,))))
+        ids.copy_(torch.from_numpy(rng.choice(10, 4, replace=False).astype(np.int32)).cuda())
+        rw.copy_(torch.from_numpy(rng.uniform(0.05, 1.0, 4).astype(np.float32)).cuda())
+        wq.copy_(bf16(synthetic.draw_acts(rng, (96, 1024))))
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (h, out, qo, so)]
+        calls()
+        torch.cuda.synchronize()
+        for a, b, name in zip(got, (h, out, qo, so), ("swiglu", "down_combine", "codes", "scales")):
+            assert torch.equal(a.view(torch.int16) if a.dtype in (torch.bfloat16, torch.float16)
+                               else a, b.view(torch.int16) if b.dtype in (torch.bfloat16,
+                                                                          torch.float16) else b), \
+                f"replay {rep}: {name} differs from the eager call"
+
+
 def test_concurrent_streams_give_eager_results():
     a = synthetic.dense(N=8192, K=4096, seed=4, M=1, config_id=962)
     b = synthetic.dense(N=4096, K=14336, seed=5, M=8, config_id=963)
