@@ -313,6 +313,30 @@ def stream_ceiling_us(torch, w, dev, nbytes, R, cus):
     return best
 
 
+def rotations(nbytes):
+    """Copies of an nbytes operand that together exceed the memory-side cache (>= 1 GiB)."""
+    return max(2, -(-ROTATE_BYTES // max(1, nbytes)))
+
+
+def copy_ceiling_us(torch, dev, nbytes_total):
+    """Median µs of the runtime's device-to-device copy that reads and writes nbytes_total / 2
+    bytes each (rotated sources, graph-timed): the practical ceiling of a call that moves
+    nbytes_total bytes of mixed reads and writes."""
+    half = nbytes_total // 2 // 256 * 256
+    R = rotations(half)
+    src = torch.empty(R * half, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(half, dtype=torch.uint8, device=dev)
+
+    def fn(i):
+        j = i % R
+        dst.copy_(src[j * half:(j + 1) * half])
+    fn(0)
+    med, _, _ = graph_replay_stats(torch, fn, max(2 * R, 16), 5)
+    del src, dst
+    torch.cuda.empty_cache()
+    return med
+
+
 def single_call_us(torch, call, reps=21):
     """Median µs of one eager call between two events, synchronising after each (latency
     context: includes the launch, unlike the graph-timed numbers)."""
@@ -439,12 +463,14 @@ def moe_batched(torch, np, w, synthetic, dev, cus):
         fn(0)
         med, p10, p90 = graph_replay_stats(torch, fn, 128, 10)
         b = uniq * per_expert + M * m.K * 2
+        ceil = stream_ceiling_us(torch, w, dev, int(b), rotations(int(b)), cus)
         out[f"c4_moe_batched_M{M}"] = {
             "experts": m.E, "topk": m.topk, "N": m.N, "K": m.K, "M": M,
             "mean_unique_experts": round(uniq, 2),
             "plan": w.describe_moe_batched_plan(M, m.N, m.K, m.topk, cus),
             "us_per_call": round(med, 3), "us_p10": round(p10, 3), "us_p90": round(p90, 3),
-            "GB_s": round(b / med / 1e3, 1), "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1)}
+            "GB_s": round(b / med / 1e3, 1), "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1),
+            "stream_read_us": round(ceil[0], 3), "pct_of_stream_read": round(100 * ceil[0] / med, 1)}
     del cp
     torch.cuda.empty_cache()
     return out
@@ -467,9 +493,12 @@ def quantize_rate(torch, np, w, dev):
     b = 2 * N * K + N * K // 2 + N * (K // 128) * 2
     del copies
     torch.cuda.empty_cache()
+    copy_us = copy_ceiling_us(torch, dev, b)
     return {"N": N, "K": K, "bytes": b, "us_per_call": round(med, 3), "us_p10": round(p10, 3),
             "us_p90": round(p90, 3), "GB_s": round(b / med / 1e3, 1),
-            "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1)}
+            "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1),
+            "copy_us_same_bytes": round(copy_us, 3),
+            "pct_of_copy": round(100 * copy_us / med, 1)}
 
 
 def tail_bytes(d):
@@ -517,13 +546,18 @@ def expert_tail(torch, np, w, synthetic, dev, cus):
     g_us, _, _ = graph_replay_stats(torch, gate, 128, 5)
     d_us, _, _ = graph_replay_stats(torch, down, 128, 5)
     b = tail_bytes(d)
+    b_gu = d.topk * (2 * d.I * d.K // 2 + 2 * d.I * (d.K // 128) * 2) + d.K * 2
+    ceil_us = (stream_ceiling_us(torch, w, dev, b_gu, rotations(b_gu), cus)[0] +
+               stream_ceiling_us(torch, w, dev, b - b_gu, rotations(b - b_gu), cus)[0])
     e = {"experts": d.E, "topk": d.topk, "gate_up": [2 * d.I, d.K], "down": [d.H, d.I],
          "plans": {"swiglu": w.describe_tail_plan(0, 0, d.K, d.I, d.topk, cus),
                    "down_combine": w.describe_tail_plan(1, d.H, 0, d.I, d.topk, cus)},
          "bytes": b, "us_per_call": round(med, 3), "us_p10": round(p10, 3),
          "us_p90": round(p90, 3), "us_swiglu": round(g_us, 3), "us_down_combine": round(d_us, 3),
          "GB_s": round(b / med / 1e3, 1),
-         "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1)}
+         "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1),
+         "stream_read_us_two_launches": round(ceil_us, 3),
+         "pct_of_stream_read": round(100 * ceil_us / med, 1)}
     del cp
     torch.cuda.empty_cache()
     return e
