@@ -204,9 +204,9 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
         const int64_t rows_per_block = 16LL * p->T * (wpb / p->KS);
         const int64_t row_blocks = (N + rows_per_block - 1) / rows_per_block;
         if (p->xlds) {
-            // 16 token slots of activation fragments (16 bytes per lane, word and group) plus
-            // one fp32 offset per (group, token); with line loads, one 1 KiB staging slot per
-            // group of an item and wave.
+            // 16 token slots (8 for the 8-slot form) of activation fragments (16 bytes per
+            // lane, word and group) plus one fp32 offset per (group, token); with line loads,
+            // one 1 KiB staging slot per group of an item and wave.
             p->lds_bytes = gpr * (p->slots8 ? 2048 : 4096) + gpr * 64 +
                            (p->lines ? (int64_t)wpb * p->V * 1024 : 0);
             if (p->lds_bytes > lds_limit)
@@ -244,7 +244,8 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
 //  * other K, and every grouped-expert call: the staged kernel with the widest power-of-two lanes
 //    per row dividing the row's 16-byte chunks; rows of 72 chunks (K = 2304) use 8 lanes with
 //    3 chunks per item;
-//  * 5-16 tokens: MFMA.
+//  * 2-16 tokens: MFMA (see mfma_slots8_plan, mfma4_plan and mfma_plan), except 2 tokens with K
+//    a multiple of 2048, which stay on split-K VALU.
 namespace {
 
 int pow2_lanes(int64_t cpr)
