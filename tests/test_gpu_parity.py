@@ -84,6 +84,26 @@ def test_batched_identity_rows_return_columns_bitwise():
     assert np.array_equal(Y, expect)
 
 
+@pytest.mark.parametrize("M", [2, 5, 8])
+def test_batched_identity_rows_staged_8_slot_form_bitwise(M):
+    """The 8-token-slot staged MFMA form on a tall matrix: X rows = unit vectors return columns
+    of W exactly, so every token lands in its own output row."""
+    N, K = 26624, 2304
+    assert w.describe_plan(M, N, K).startswith("mfma16x16x32_lds8_lines")
+    rng = np.random.default_rng(40 + M)
+    qw = rng.integers(0, 1 << 32, size=(N, K // 8), dtype=np.uint32)
+    s = rng.uniform(0.001, 0.01, size=(N, K // 128)).astype(np.float16)
+    js = np.array([0, 9, 127, 128, 1151, 1500, 2200, 2303])[:M]
+    # value k of a row: nibble k % 8 of word k // 8, two's complement
+    nib = (qw[:, js // 8] >> (4 * (js % 8)).astype(np.uint32)) & 0xF
+    q = nib.astype(np.int64) - 16 * (nib >= 8)
+    X = np.zeros((M, K), np.uint16)
+    X[np.arange(M), js] = 0x3F80
+    Y = host(w.gemv_batched(words(qw), f16(s.view(np.uint16)), bf16(X)))
+    expect = (q * s[:, js // 128].astype(np.float64)).T.astype(np.float32)
+    assert np.array_equal(Y, expect)
+
+
 def test_zero_scales_give_exact_zero():
     d = synthetic.dense(N=100, K=2048, seed=5, config_id=701)
     y = host(w.gemv(words(d.qweight), f16(np.zeros_like(d.scales)), bf16(d.x[0])))
