@@ -13,8 +13,9 @@
 // residual w * r - q with one rounding (error < 3e-8). Where every residual of a lane is at most
 // 1/2 - 4e-6, fl(w / s) lies strictly within 1/2 - 2.7e-6 of q, so q = rint(fl(w / s)); a lane
 // with a residual closer to 1/2 (about one value in 10^5) recomputes its codes with the exact
-// division. The clamp to [-8, 7] is a med3 of C + q against C - 8 and C + 7, and the two's
-// complement nibble is the low 4 bits of C + q (C is a multiple of 16).
+// division. Codes need no clamp except in groups with a subnormal or saturated scale, which take
+// the exact path with a clamp to [-8, 7]; the two's complement nibble is the low 4 bits of
+// C + q (C is a multiple of 16).
 //
 // Layout: 8 lanes per group, a wave quantises 8 groups at a time; lane p of a group loads the 16-byte
 // slices p and p + 8 (bf16 values 8p..8p+7 and 64+8p..64+8p+7), so each load instruction covers one
@@ -96,8 +97,13 @@ __device__ __forceinline__ void quantize_lane(uint4 a, uint4 b, uint32_t &w0, ui
         y[i] = fmaf(f[i], r, C);
         emax = fmaxf(emax, fabsf(fmaf(f[i], r, C - y[i])));
     }
-    if (emax > 0.5f - 4e-6f) {
-        // near a rounding boundary: the exact quotient decides (s > 0 here)
+    // With a normal, unsaturated fp16 scale, s >= (amax / 7)(1 - 2^-11), so |w / s| < 7.004 and
+    // every estimate rounds into [-7, 7]: no clamp is needed. A subnormal scale (relative
+    // rounding error up to 1/2) or a saturated one can give codes outside [-8, 7]; such groups,
+    // and lanes with a residual near 1/2, take the exact division with the clamp.
+    const uint32_t smag = sb & 0x7FFFu;
+    if (emax > 0.5f - 4e-6f || smag - 1u < 0x3FFu || smag == 0x7BFFu) {
+        // the exact quotient decides (s > 0 here: a zero scale has no residual and smag = 0)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             y[i] = C + __builtin_amdgcn_fmed3f(rintf(f[i] / s), -8.0f, 7.0f);
@@ -105,7 +111,7 @@ __device__ __forceinline__ void quantize_lane(uint4 a, uint4 b, uint32_t &w0, ui
     uint32_t q[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-        q[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(y[i], C - 8.0f, C + 7.0f));
+        q[i] = __builtin_bit_cast(uint32_t, y[i]);
     w0 = pack_nibbles(q);
     w1 = pack_nibbles(q + 8);
 }
