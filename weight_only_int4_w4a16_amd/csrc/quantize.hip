@@ -118,8 +118,11 @@ __device__ __forceinline__ void quantize_lane(uint4 a, uint4 b, uint32_t &w0, ui
 
 // A wave takes QU steps of 8 groups per pass and works on one pass while the loads of the next
 // are in flight (two register buffers), so each lane keeps up to 2 x QU x 32 bytes requested.
+// One step per pass (75 VGPRs, 6 waves per SIMD) measured faster than two (101 VGPRs, 4 waves):
+// 28672 x 4096 in 69.0-69.5 against 71.2-72.1 us, because more waves overlap the arithmetic
+// with the memory traffic.
 #ifndef W4A16_QUANT_QU
-#define W4A16_QUANT_QU 2
+#define W4A16_QUANT_QU 1
 #endif
 constexpr int QU = W4A16_QUANT_QU;
 constexpr int kGroupsPerWave = 8;
