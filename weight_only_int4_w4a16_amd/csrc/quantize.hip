@@ -70,17 +70,27 @@ __device__ __forceinline__ uint32_t pack_nibbles(const uint32_t *b)
 
 // One group's scale and this lane's two packed words from its 16 values (slices a and b); the
 // group's other 112 values sit in the 7 other lanes of the same half row.
+__device__ __forceinline__ void unpack8(uint4 v, float (&f)[8])
+{
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
 __device__ __forceinline__ void quantize_lane(uint4 a, uint4 b, uint32_t &w0, uint32_t &w1,
                                               uint16_t &sb)
 {
-    float f[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
-                   bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
-                   bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
-                   bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
     float amax = 0.0f;
+    {
+        float f[8];
+        unpack8(a, f);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        amax = fmaxf(amax, fabsf(f[i]));
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fabsf(f[i]));
+        unpack8(b, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fabsf(f[i]));
+    }
     amax = row8_max(amax);
     const float s32 = amax / 7.0f;
     sb = __builtin_bit_cast(uint16_t, (_Float16)s32);   // nearest even
@@ -90,37 +100,43 @@ __device__ __forceinline__ void quantize_lane(uint4 a, uint4 b, uint32_t &w0, ui
     // r = 0 for a zero scale makes every code 0, as defined (and every residual 0).
     const float r = s != 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
     constexpr float C = 12582912.0f;   // 1.5 * 2^23: C + q is exact for |q| < 2^22
-    float y[16];
-    float emax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        y[i] = fmaf(f[i], r, C);
-        emax = fmaxf(emax, fabsf(fmaf(f[i], r, C - y[i])));
-    }
     // With a normal, unsaturated fp16 scale, s >= (amax / 7)(1 - 2^-11), so |w / s| < 7.004 and
     // every estimate rounds into [-7, 7]: no clamp is needed. A subnormal scale (relative
     // rounding error up to 1/2) or a saturated one can give codes outside [-8, 7]; such groups,
     // and lanes with a residual near 1/2, take the exact division with the clamp.
     const uint32_t smag = sb & 0x7FFFu;
-    if (emax > 0.5f - 4e-6f || smag - 1u < 0x3FFu || smag == 0x7BFFu) {
-        // the exact quotient decides (s > 0 here: a zero scale has no residual and smag = 0)
+    const bool special = smag - 1u < 0x3FFu || smag == 0x7BFFu;
+    // The two 8-value slices one after the other, so only one slice's values are live.
+    auto slice = [&](uint4 v) -> uint32_t {
+        float f[8], y[8];
+        unpack8(v, f);
+        float emax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            y[i] = C + __builtin_amdgcn_fmed3f(rintf(f[i] / s), -8.0f, 7.0f);
-    }
-    uint32_t q[16];
+        for (int i = 0; i < 8; ++i) {
+            y[i] = fmaf(f[i], r, C);
+            emax = fmaxf(emax, fabsf(fmaf(f[i], r, C - y[i])));
+        }
+        if (emax > 0.5f - 4e-6f || special) {
+            // the exact quotient decides (s > 0 here: a zero scale has no residual and smag = 0)
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        q[i] = __builtin_bit_cast(uint32_t, y[i]);
-    w0 = pack_nibbles(q);
-    w1 = pack_nibbles(q + 8);
+            for (int i = 0; i < 8; ++i)
+                y[i] = C + __builtin_amdgcn_fmed3f(rintf(f[i] / s), -8.0f, 7.0f);
+        }
+        uint32_t q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            q[i] = __builtin_bit_cast(uint32_t, y[i]);
+        return pack_nibbles(q);
+    };
+    w0 = slice(a);
+    w1 = slice(b);
 }
 
 // A wave takes QU steps of 8 groups per pass and works on one pass while the loads of the next
 // are in flight (two register buffers), so each lane keeps up to 2 x QU x 32 bytes requested.
-// One step per pass (75 VGPRs, 6 waves per SIMD) measured faster than two (101 VGPRs, 4 waves):
-// 28672 x 4096 in 69.0-69.5 against 71.2-72.1 us, because more waves overlap the arithmetic
-// with the memory traffic.
+// Registers decide how well the arithmetic overlaps the memory traffic: one step per pass and
+// one 8-value slice at a time keep the kernel at 67 VGPRs, 7 waves per SIMD (28672 x 4096: 60.0
+// us, against 69.0 with both slices live at 75 VGPRs and 71.2-72.1 with two steps at 101).
 #ifndef W4A16_QUANT_QU
 #define W4A16_QUANT_QU 1
 #endif
