@@ -57,6 +57,15 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _experts(qw: np.ndarray, num_experts: Optional[int]) -> int:
+    """Expert count passed to the oracle: qw's leading size unless a smaller one is asked for."""
+    if num_experts is None:
+        return qw.shape[0]
+    if not 1 <= num_experts <= qw.shape[0]:
+        raise ValueError("num_experts must lie in [1, experts held]")
+    return int(num_experts)
+
+
 def _rows(rows, N):
     if rows is None:
         return None, N
@@ -143,11 +152,14 @@ class Oracle:
         return Y, mag
 
     def moe_gemv(self, qweight, scales, ids, x, K: int, group: int = 128,
-                 rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
-        """(y, mag) as float64 [topk][rows] for experts ids over qweight [E][N][K/8]."""
+                 rows: Optional[Sequence[int]] = None,
+                 num_experts: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """(y, mag) as float64 [topk][rows] for experts ids over qweight [E][N][K/8].
+        num_experts (default: qweight's leading size) is the E the oracle is told; a smaller
+        value leaves spare experts in memory past the last valid one."""
         qw, sc = _c(qweight, np.uint32), _c(scales, np.uint16)
         ii, xx = _c(ids, np.int32).reshape(-1), _c(x, np.uint16).reshape(-1)
-        E, N = qw.shape[0], qw.shape[1]
+        E, N = _experts(qw, num_experts), qw.shape[1]
         r, nr = _rows(rows, N)
         y, mag = np.empty((ii.size, nr)), np.empty((ii.size, nr))
         if self.lib.oracle_moe_gemv(_ptr(qw), _ptr(sc), _ptr(ii), ii.size, E, _ptr(xx), N, K,
@@ -161,12 +173,13 @@ class Oracle:
     def silu(self, g: float) -> float:
         return self.lib.oracle_silu(float(g))
 
-    def moe_swiglu(self, qweight, scales, ids, x, K: int, group: int = 128) -> dict:
+    def moe_swiglu(self, qweight, scales, ids, x, K: int, group: int = 128,
+                   num_experts: Optional[int] = None) -> dict:
         """Gate+up product of the selected experts (qweight [E][2I][K/8]) and SwiGLU.
         Returns float64 [topk][I] arrays h, g, u, mag_g, mag_u and uint16 h_bf16."""
         qw, sc = _c(qweight, np.uint32), _c(scales, np.uint16)
         ii, xx = _c(ids, np.int32).reshape(-1), _c(x, np.uint16).reshape(-1)
-        E, N2 = qw.shape[0], qw.shape[1]
+        E, N2 = _experts(qw, num_experts), qw.shape[1]
         if N2 % 2:
             raise ValueError("gate+up weights need an even row count")
         I, T = N2 // 2, ii.size
@@ -179,12 +192,13 @@ class Oracle:
         return out
 
     def moe_down_combine(self, qweight, scales, ids, weights, h, group: int = 128,
-                         rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                         rows: Optional[Sequence[int]] = None,
+                         num_experts: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
         """(out, mag) float64 [rows]: sum_t w[t] * W_down[ids[t]] h[t], qweight [E][H][I/8]."""
         qw, sc = _c(qweight, np.uint32), _c(scales, np.uint16)
         ii, ww = _c(ids, np.int32).reshape(-1), _c(weights, np.float32).reshape(-1)
         hh = _c(h, np.uint16)
-        E, H, I = qw.shape[0], qw.shape[1], qw.shape[2] * 8
+        E, H, I = _experts(qw, num_experts), qw.shape[1], qw.shape[2] * 8
         if ww.size != ii.size or hh.shape != (ii.size, I):
             raise ValueError("ids, weights and h disagree")
         r, nr = _rows(rows, H)
@@ -197,7 +211,8 @@ class Oracle:
 
 
     def moe_gemv_batched(self, qweight, scales, ids, X, K: int, group: int = 128,
-                         rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                         rows: Optional[Sequence[int]] = None,
+                         num_experts: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
         """(Y, mag) float64 [M][topk][rows]: token m times expert ids[m][t], qweight [E][N][K/8]."""
         qw, sc = _c(qweight, np.uint32), _c(scales, np.uint16)
         ii, XX = _c(ids, np.int32), _c(X, np.uint16)
@@ -206,7 +221,7 @@ class Oracle:
         M, ldx = XX.shape
         ii = ii.reshape(M, -1)
         topk = ii.shape[1]
-        E, N = qw.shape[0], qw.shape[1]
+        E, N = _experts(qw, num_experts), qw.shape[1]
         r, nr = _rows(rows, N)
         Y, mag = np.empty((M, topk, nr)), np.empty((M, topk, nr))
         if self.lib.oracle_moe_gemv_batched(_ptr(qw), _ptr(sc), _ptr(ii), M, topk, E, _ptr(XX),

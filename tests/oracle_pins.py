@@ -547,10 +547,55 @@ def pin_moe_batched(orc):
     assert np.array_equal(Ys, Y[:, :, [4, 0]]) and np.array_equal(ms, mag[:, :, [4, 0]])
 
 
+def pin_expert_id_upper_bound(orc):
+    """Ids E and E + 1 name no expert in every grouped form, even when the tensors hold more
+    experts past the E the oracle is told about (so reading expert E would find real weights):
+    their rows are zero, they add nothing to the combine, and the valid slots are unchanged."""
+    E, N, K = 3, 4, 256
+    rng = np.random.default_rng(61)
+    held = E + 2
+    q = rng.integers(-8, 8, size=(held, N, K))
+    q[E:] = np.where(q[E:] == 0, 5, q[E:])                  # spare experts: no zero codes
+    words = np.stack([pack_nibbles(q[e]) for e in range(held)])
+    scales = rng.uniform(0.001, 0.01, size=(held, N, K // 128)).astype(np.float16).view(np.uint16)
+    x = np.full(K, 0x3F80, np.uint16)                       # x = 1 everywhere
+    ids = np.array([1, E, 0, E + 1], np.int32)
+    valid = [0, 2]
+    y, mag = orc.moe_gemv(words, scales, ids, x, K, num_experts=E)
+    yv, mv = orc.moe_gemv(words, scales, ids[valid], x, K, num_experts=E)
+    assert np.all(y[[1, 3]] == 0) and np.all(mag[[1, 3]] == 0)
+    assert np.array_equal(y[valid], yv) and np.array_equal(mag[valid], mv)
+    yall, _ = orc.moe_gemv(words, scales, ids, x, K)         # told all held experts: nonzero
+    assert np.all(yall[[1, 3]] != 0)
+
+    X = np.stack([x, x ^ 0x8000])                            # token 1 is -x
+    idb = np.array([[E, 2], [0, E + 1]], np.int32)
+    Y, magb = orc.moe_gemv_batched(words, scales, idb, X, K, num_experts=E)
+    assert np.all(Y[0, 0] == 0) and np.all(Y[1, 1] == 0) and np.all(magb[0, 0] == 0)
+    assert np.array_equal(Y[0, 1], orc.gemv(words[2], scales[2], x, K)[0])
+
+    I = N // 2                                              # gate rows [0, I), up rows [I, 2I)
+    r = orc.moe_swiglu(words, scales, ids, x, K, num_experts=E)
+    for k in ("h", "g", "u", "mag_g", "mag_u"):
+        assert np.all(r[k][[1, 3]] == 0)
+    assert np.all(r["h_bf16"][[1, 3]] == 0)
+    rv = orc.moe_swiglu(words, scales, ids[valid], x, K, num_experts=E)
+    assert np.array_equal(r["h"][valid], rv["h"]) and r["h"].shape == (4, I)
+
+    h = np.stack([x] * 4)                                   # each slot's own row: all ones
+    w = np.array([0.25, 0.5, 0.75, 1.0], np.float32)
+    out, mo = orc.moe_down_combine(words, scales, ids, w, h, num_experts=E)
+    ov, mov = orc.moe_down_combine(words, scales, ids[valid], w[valid], h[valid], num_experts=E)
+    assert np.array_equal(out, ov) and np.array_equal(mo, mov)
+    oall, _ = orc.moe_down_combine(words, scales, ids, w, h)
+    assert not np.array_equal(oall, out)
+
+
 ALL_PINS = [
     pin_f16_decode, pin_bf16_decode, pin_w1, pin_w2, pin_unpack, pin_unit_probes,
     pin_zero_scale_groups, pin_linearity, pin_negation, pin_constant_rows, pin_brute_force,
     pin_mag_nonnegative, pin_batched, pin_moe, pin_row_subset, pin_bf16_round_brute,
     pin_bf16_round_ties, pin_silu, pin_swiglu_golden, pin_swiglu_brute, pin_down_combine,
     pin_quantize_golden, pin_quantize_brute, pin_quantize_gemv_roundtrip, pin_moe_batched,
+    pin_expert_id_upper_bound,
 ]

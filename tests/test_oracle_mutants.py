@@ -55,6 +55,14 @@ MUTANTS = {
     "moe_batched_token_row": ("X + m * ldx, K, G,\n                        &Y[o], &mag[o]);",
                               "X, K, G,\n                        &Y[o], &mag[o]);"),
     "moe_batched_id_index": ("ids[(int64_t)m * topk + t]", "ids[(int64_t)t * M + m]"),
+    "moe_id_upper_bound": ("            if (e < 0 || e >= E) {\n                *yo = 0.0;",
+                           "            if (e < 0 || e > E) {\n                *yo = 0.0;"),
+    "swiglu_id_upper_bound": ("            if (e < 0 || e >= E) {\n                h[o] = g[o]",
+                              "            if (e < 0 || e > E) {\n                h[o] = g[o]"),
+    "combine_id_upper_bound": ("            if (e < 0 || e >= E)\n                continue;",
+                               "            if (e < 0 || e > E)\n                continue;"),
+    "moe_batched_id_upper_bound": ("                if (e < 0 || e >= E) {\n                    Y[o] = 0.0;",
+                                   "                if (e < 0 || e > E) {\n                    Y[o] = 0.0;"),
     "quant_f16_subnormal": ("if (qexp < -24)\n        qexp = -24;", "if (qexp < -30)\n        qexp = -30;"),
 }
 
