@@ -26,12 +26,18 @@
  *   - On W4A16_OK the work is enqueued on `stream` (0 = the null stream) and the call returns
  *     without synchronising. Faults inside a kernel surface at the caller's next
  *     synchronisation, as for any HIP launch.
- *   - Results are computed in fp32 from exact products (|q| <= 8 and a binary16 scale and a
- *     bfloat16 activation multiply exactly in fp32); only the order of the fp32 sums differs
- *     from the plain definition, and that order is fixed, so repeated calls give identical
- *     bits. Activations must be finite and |x| <= 2^100: the kernels carry a constant offset
- *     of 136 per weight through the sum and remove it with the group sums of x, so an
- *     infinite or NaN activation turns every output that reads it into NaN.
+ *   - Precision. Every weight enters the arithmetic as the exact integer q. The activations of
+ *     each 128-value group of a token are multiplied by a power of two 2^e (e chosen from the
+ *     group's largest finite-or-not magnitude so that it lands in [2^15, 2^16)) and rounded to
+ *     binary16: this is exact for every activation of magnitude at least 2^-32 times the
+ *     largest of its group, and a smaller one moves by at most 2^-40 times that largest value.
+ *     Products q * x' are exact in fp32 and are summed in fp32 in a fixed order, then scaled by
+ *     2^-e (exact) and by the group's scale, so per output
+ *         |y - y_exact| <= (K/32 + 64) * 2^-24 * sum_k |q s x|
+ *                          + 2^-40 * sum_{k: |x_k| < 2^-32 max_g} |q_k s_k| * max_{g(k)}
+ *     (max_g: the largest |x| of k's group), and repeated calls give identical bits. Infinite
+ *     and NaN activations propagate as in the plain definition: every output that reads one
+ *     is +-inf or NaN exactly where the exact sum is (0 * inf is NaN).
  *   - Calls are thread-safe. The library keeps one cached record of device properties per
  *     device and no other global state.
  *   - No C++ exception crosses this boundary and nothing is printed.

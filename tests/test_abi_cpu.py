@@ -217,15 +217,18 @@ def test_valid_arguments_reach_the_device_check_only():
     (1, 1024, 2048, 0, "splitk "), (1, 4096, 7168, 0, "splitk "), (1, 16384, 3072, 0, "splitk "),
     (1, 16384, 1536, 0, "valu tokens=1 lanes_per_row=8 chunks_per_item=3"),
     (1, 8192, 1024, 0, "valu "), (1, 4096, 4096, 0, "splitk "),
-    (1, 28672, 4096, 0, "splitk tokens=1 lanes_per_row=32 chunks_per_lane=1 row_steps=2"),
+    (1, 28672, 4096, 0, "splitk tokens=1 lanes_per_row=32 chunks_per_lane=1 row_steps=4"),
     (1, 14336, 2048, 0, "valu tokens=1 lanes_per_row=32 chunks_per_item=2"),
     (1, 4096, 14336, 0, "splitk "), (1, 8192, 8192, 0, "splitk "), (1, 163840, 2304, 0, "valu "),
     (1, 2048, 2304, 8, "valu_moe"), (1, 5, 128, 0, "valu "), (1, 64, 65536, 0, "splitk "),
     (2, 8192, 8192, 0, "splitk "),
-    (4, 163840, 2304, 0, "mfma16x16x32_lds8_lines tiles_per_wave=1 k_split=1 groups_per_item=2 "
+    (4, 163840, 2304, 0, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=3 row_steps=1 "
+                         "blocks_per_row=8 threads=192 blocks=1024"),
+    (5, 163840, 2304, 0, "mfma16x16x32_lds8_lines tiles_per_wave=1 k_split=1 groups_per_item=2 "
                          "threads=512 blocks=512"),
+    (1, 163840, 2304, 0, "valu tokens=1 lanes_per_row=8 chunks_per_item=1 row_steps=2"),
     (6, 163840, 2304, 0, "mfma16x16x32_lds8_lines"),
-    (2, 163840, 2304, 0, "mfma16x16x32_lds8_lines"), (4, 32768, 2048, 0, "mfma4x4x4_splitk"),
+    (2, 163840, 2304, 0, "mfma4x4x4_splitk"), (4, 32768, 2048, 0, "mfma4x4x4_splitk"),
     (8, 163840, 2304, 0, "mfma16x16x32_lds8_lines"), (3, 100, 384, 0, "valu "),
     (4, 28672, 4096, 0, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=2 row_steps=2 "
                         "blocks_per_row=16"),
@@ -236,10 +239,10 @@ def test_valid_arguments_reach_the_device_check_only():
     (8, 28672, 4096, 0, "mfma16x16x32_lds_lines"), (2, 28672, 4096, 0, "splitk "),
     (2, 14336, 2048, 0, "splitk tokens=2"), (4, 14336, 2048, 0, "mfma4x4x4_splitk token_groups=1 "
                                                               "chunks_per_lane=1 row_steps=2"),
-    (16, 8192, 8192, 0, "mfma16x16x32_lines tiles_per_wave=2 k_split=4"),
+    (16, 8192, 8192, 0, "mfma16x16x32 tiles_per_wave=2 k_split=4"),
     (16, 14336, 2048, 0, "mfma16x16x32_lines tiles_per_wave=4 k_split=4"),
     (16, 300, 2688, 0, "mfma16x16x32 tiles_per_wave=1 k_split=1 groups_per_item=1"),
-    (16, 163840, 2304, 0, "mfma16x16x32_lds_lines"), (8, 8192, 8192, 0, "mfma"),
+    (16, 163840, 2304, 0, "mfma16x16x32_lds_lines tiles_per_wave=1 k_split=1 groups_per_item=2"), (8, 8192, 8192, 0, "mfma"),
     (16, 2048, 4096, 0, "mfma16x16x32_lines tiles_per_wave=1 k_split=8"),
     (16, 4096, 2304, 0, "mfma16x16x32_lds_lines tiles_per_wave=1 k_split=1 groups_per_item=6 threads=256"),
 ])

@@ -84,7 +84,7 @@ def test_batched_identity_rows_return_columns_bitwise():
     assert np.array_equal(Y, expect)
 
 
-@pytest.mark.parametrize("M", [2, 5, 8])
+@pytest.mark.parametrize("M", [5, 6, 8])
 def test_batched_identity_rows_staged_8_slot_form_bitwise(M):
     """The 8-token-slot staged MFMA form on a tall matrix: X rows = unit vectors return columns
     of W exactly, so every token lands in its own output row."""
@@ -186,7 +186,7 @@ def test_batched_mfma_plans(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(2, 5000, 2304), (3, 333, 4096), (4, 20001, 4096), (4, 33, 14336),
                                    (3, 1000, 2048), (4, 999, 1024), (5, 77, 2304), (6, 4096, 14336),
                                    (8, 1500, 8192), (7, 3, 4096), (8, 8192, 512), (2, 17, 256),
-                                   (3, 16384, 2304), (6, 1, 2304)])
+                                   (3, 16384, 2304), (6, 1, 2304), (2, 26624, 2304), (4, 26700, 2304)])
 def test_batched_mfma4_plans(M, N, K):
     """The 4x4x4-MFMA split-K kernel: 16 and 8 blocks per row group, one and two token groups
     (partial groups included), 1-4 chunks per lane, one and two row steps per item, fewer rows
@@ -200,10 +200,10 @@ def test_batched_mfma4_plans(M, N, K):
     within(Y, ref, mag, f"batched M={M} {N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(2, 26624, 2304), (3, 26624, 2304), (5, 26700, 2304),
-                                   (7, 26700, 2304), (8, 26880, 1536), (4, 30000, 256)])
+@pytest.mark.parametrize("M,N,K", [(5, 26624, 2304), (6, 26624, 2304), (5, 26700, 2304),
+                                   (7, 26700, 2304), (8, 26880, 1536), (6, 30000, 256)])
 def test_batched_staged_8_slot_plans(M, N, K):
-    """The staged whole-line 16x16x32 form with 8 token slots (2-8 tokens, tall matrices): MFMA
+    """The staged whole-line 16x16x32 form with 8 token slots (5-8 tokens, tall matrices): MFMA
     rows 8-15 read slots 0-7 again and are never stored; ragged row counts pull the last block
     back."""
     plan = w.describe_plan(M, N, K)

@@ -4,17 +4,30 @@
 // matrix-vector product over packed INT4 weights, walking the contiguous reduction axis K with a
 // single accumulator per output row, instead of a matrix-matrix kernel applied to one token.
 //
-// Decode path shared by every kernel here. A 32-bit word holds 8 two's-complement nibbles; one
-// v_bitop3 per pair turns nibbles (i, i+4) into two bf16 values 136 + q:
-//     ((w >> 4i) & 0x000F000F) ^ 0x43084308
-// The mask keeps nibble i in bits 0-3 of the low half and nibble i+4 in bits 0-3 of the high half;
-// the XOR sets the bf16 exponent of 128 (0x4300, one mantissa step = 1.0) and flips bit 3, which
-// maps the two's-complement code to q + 8. So each half reads 128 + (q + 8) = 136 + q exactly.
-// The products (136 + q) * x are formed by v_dot2c_f32_bf16 against activation pairs (x_i, x_{i+4})
-// staged in that order, and the constant part 136 * sum(x) of each 32-value chunk is removed by
-// starting the chunk's accumulator at -136 * sum(x). The chunk total is then scaled by its fp16
-// group scale in fp32. All products are exact in fp32; only the summation order differs from the
-// plain definition.
+// Decode path shared by every kernel here. A 32-bit word holds 8 two's-complement nibbles n0..n7
+// (n0 in the low bits); they are decoded in the pairs (n0,n4) (n1,n5) (n2,n6) (n3,n7), each pair
+// as the two halves of one fp16 pair, by one v_bitop3 (mask and XOR with a magic constant) and
+// one v_pk_add_f16:
+//   nibbles in bits 0-3 and 16-19:  (w & 0x000F000F) ^ 0x64086408  ->  1032 + q,  minus 1032
+//   nibbles in bits 4-7 and 20-23:  (w & 0x00F000F0) ^ 0x54805480  ->    72 + q,  minus 72
+// The XOR sets the fp16 exponent at which one step of the nibble's mantissa bits is 1.0 (2^10
+// for bits 0-3, 2^6 for bits 4-7) and flips the nibble's top bit, which maps the two's-complement
+// code to q + 8; the subtraction leaves q itself, exactly (the magic-number conversion of
+// integers to floating point, applied to packed 4-bit codes). Pairs (n2,n6) and (n3,n7) take the
+// same two forms on w >> 8. Weights enter every product as the exact integer q: there is no
+// constant offset left to cancel later, so the fp32 rounding of a sum stays relative to the sum
+// of |q x|.
+//
+// Activations are staged as fp16 once per work-group (or per wave for register-resident forms).
+// Each run of 128 activations of one token (one scale group) is multiplied by a power of two 2^e
+// chosen so that its largest magnitude lands in [2^15, 2^16), then rounded to fp16. A bf16 value
+// has 8 significant bits, so the scaled value is exact in fp16 unless it falls below 2^-17, i.e.
+// unless it is smaller than about 2^-32 times the largest magnitude of its group; such values are
+// rounded to a multiple of 2^-24 (scaled). Products q * x' (4 + 11 significant bits) are exact in
+// fp32, group or chunk totals are accumulated in fp32 and multiplied by 2^-e (exact) and by the
+// group's fp16 scale. Non-finite activations stay non-finite (an infinity or NaN in a group only
+// moves that group's exponent), so every output that reads one is non-finite, as in the plain
+// definition (0 * inf is NaN there too).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,47 +38,44 @@
 
 namespace w4a16 {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
-static constexpr uint32_t kMask = 0x000F000Fu;
-static constexpr uint32_t kMagic = 0x43084308u;   // bf16 pair (128, 128) with bit 3 flipped
-static constexpr float kOffset = 136.0f;
-
+// fp32 sum c + a.lo * b.lo + a.hi * b.hi of two fp16 pairs (v_dot2c_f32_f16).
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                  false);
 }
 
-#ifndef W4A16_SHIFT64
-#define W4A16_SHIFT64 1
-#endif
+// The two codes in bits 0-3 and 16-19 of `bits` (other bits ignored) as the fp16 pair (q_lo, q_hi).
+__device__ __forceinline__ uint32_t decode_pair_lo(uint32_t bits)
+{
+    const f16x2_t v = __builtin_bit_cast(f16x2_t, (bits & 0x000F000Fu) ^ 0x64086408u);
+    return __builtin_bit_cast(uint32_t, v + __builtin_bit_cast(f16x2_t, 0xE408E408u));
+}
 
-// Weights are read exactly once per call: stream them past the caches when asked to.
-#ifndef W4A16_STREAM_LOADS
-#define W4A16_STREAM_LOADS 1
-#endif
+// The two codes in bits 4-7 and 20-23 of `bits` (other bits ignored) as the fp16 pair.
+__device__ __forceinline__ uint32_t decode_pair_hi(uint32_t bits)
+{
+    const f16x2_t v = __builtin_bit_cast(f16x2_t, (bits & 0x00F000F0u) ^ 0x54805480u);
+    return __builtin_bit_cast(uint32_t, v + __builtin_bit_cast(f16x2_t, 0xD480D480u));
+}
+
+// Weights are read exactly once per call: stream them past the caches.
 __device__ __forceinline__ uint4 load_weights(const uint4 *p)
 {
-#if W4A16_STREAM_LOADS
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
-#else
-    return *p;
-#endif
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 {
     return (float)__builtin_bit_cast(_Float16, h);
-}
-
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t b16)
-{
-    return __builtin_bit_cast(float, b16 << 16);
 }
 
 // a if take else b, computed with masks so it never becomes a branch (branches around the loads
@@ -78,97 +88,117 @@ __device__ __forceinline__ const T *pick(bool take, const T *a, const T *b)
                                        (reinterpret_cast<uintptr_t>(b) & ~m));
 }
 
-// Nibble pairs (0,4) (1,5) (2,6) (3,7) of w as bf16 pairs holding 136 + q.
+// Nibble pairs (0,4) (1,5) (2,6) (3,7) of w as fp16 pairs holding q.
 __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t p[4])
 {
-    p[0] = (w & kMask) ^ kMagic;
-    p[1] = ((w >> 4) & kMask) ^ kMagic;
-    p[2] = ((w >> 8) & kMask) ^ kMagic;
-    p[3] = ((w >> 12) & kMask) ^ kMagic;
+    const uint32_t w8 = w >> 8;
+    p[0] = decode_pair_lo(w);
+    p[1] = decode_pair_hi(w);
+    p[2] = decode_pair_lo(w8);
+    p[3] = decode_pair_hi(w8);
 }
 
-// Words 0-1 and 2-3 of a 16-byte chunk unpacked with one 64-bit shift per nibble position
-// (bits crossing from the high word land in bits 28-31 of the low word, which the mask drops):
-// p[j][0..3] are the four bf16 pairs of word j, as unpack_word would give.
+// The four words of a 16-byte chunk: p[j][0..3] are the four fp16 pairs of word j.
 __device__ __forceinline__ void unpack_chunk(uint4 wv, uint32_t p[4][4])
 {
-#if W4A16_SHIFT64
-    const uint64_t d2[2] = {((uint64_t)wv.y << 32) | wv.x, ((uint64_t)wv.w << 32) | wv.z};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint64_t s4, s8, s12;
-        const uint64_t s0 = d2[h];
-        asm("v_lshrrev_b64 %0, 4, %1" : "=v"(s4) : "v"(s0));
-        asm("v_lshrrev_b64 %0, 8, %1" : "=v"(s8) : "v"(s0));
-        asm("v_lshrrev_b64 %0, 12, %1" : "=v"(s12) : "v"(s0));
-        p[2 * h][0] = ((uint32_t)s0 & kMask) ^ kMagic;
-        p[2 * h][1] = ((uint32_t)s4 & kMask) ^ kMagic;
-        p[2 * h][2] = ((uint32_t)s8 & kMask) ^ kMagic;
-        p[2 * h][3] = ((uint32_t)s12 & kMask) ^ kMagic;
-        p[2 * h + 1][0] = ((uint32_t)(s0 >> 32) & kMask) ^ kMagic;
-        p[2 * h + 1][1] = ((uint32_t)(s4 >> 32) & kMask) ^ kMagic;
-        p[2 * h + 1][2] = ((uint32_t)(s8 >> 32) & kMask) ^ kMagic;
-        p[2 * h + 1][3] = ((uint32_t)(s12 >> 32) & kMask) ^ kMagic;
-    }
-#else
     unpack_word(wv.x, p[0]);
     unpack_word(wv.y, p[1]);
     unpack_word(wv.z, p[2]);
     unpack_word(wv.w, p[3]);
-#endif
 }
 
-// Eight consecutive bf16 activations (x0..x7 in natural order) re-paired as
-// (x0,x4) (x1,x5) (x2,x6) (x3,x7) to match unpack_word.
-__device__ __forceinline__ uint4 pair_activations(uint4 v)
+// Sum over one 32-weight chunk of q * x', the activations re-paired and staged as fp16.
+__device__ __forceinline__ float chunk_dot(uint4 wv, const uint4 xq[4])
 {
-    uint4 o;
-    o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-    o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-    o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-    o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-    return o;
-}
-
-__device__ __forceinline__ float chunk_dot(uint4 wv, const uint4 xq[4], float acc)
-{
-#if W4A16_SHIFT64
-    // One 64-bit shift moves the nibbles of two words at once; bits that cross from the high
-    // word land in bits 28-31 of the low word, which the 0x000F000F mask never keeps.
-    const uint64_t d2[2] = {((uint64_t)wv.y << 32) | wv.x, ((uint64_t)wv.w << 32) | wv.z};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint64_t s4, s8, s12;
-        const uint64_t s0 = d2[h];
-        asm("v_lshrrev_b64 %0, 4, %1" : "=v"(s4) : "v"(s0));
-        asm("v_lshrrev_b64 %0, 8, %1" : "=v"(s8) : "v"(s0));
-        asm("v_lshrrev_b64 %0, 12, %1" : "=v"(s12) : "v"(s0));
-        const uint4 &xa = xq[2 * h], &xb = xq[2 * h + 1];
-        acc = dot2(((uint32_t)s0 & kMask) ^ kMagic, xa.x, acc);
-        acc = dot2(((uint32_t)s4 & kMask) ^ kMagic, xa.y, acc);
-        acc = dot2(((uint32_t)s8 & kMask) ^ kMagic, xa.z, acc);
-        acc = dot2(((uint32_t)s12 & kMask) ^ kMagic, xa.w, acc);
-        acc = dot2(((uint32_t)(s0 >> 32) & kMask) ^ kMagic, xb.x, acc);
-        acc = dot2(((uint32_t)(s4 >> 32) & kMask) ^ kMagic, xb.y, acc);
-        acc = dot2(((uint32_t)(s8 >> 32) & kMask) ^ kMagic, xb.z, acc);
-        acc = dot2(((uint32_t)(s12 >> 32) & kMask) ^ kMagic, xb.w, acc);
-    }
-    return acc;
-#else
-    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+    uint32_t p[4][4];
+    unpack_chunk(wv, p);
+    float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        uint32_t p[4];
-        unpack_word(wd[j], p);
-        acc = dot2(p[0], xq[j].x, acc);
-        acc = dot2(p[1], xq[j].y, acc);
-        acc = dot2(p[2], xq[j].z, acc);
-        acc = dot2(p[3], xq[j].w, acc);
+        acc = dot2(p[j][0], xq[j].x, acc);
+        acc = dot2(p[j][1], xq[j].y, acc);
+        acc = dot2(p[j][2], xq[j].z, acc);
+        acc = dot2(p[j][3], xq[j].w, acc);
     }
     return acc;
-#endif
 }
 
+// ---- activation staging: bf16 -> fp16 with a power-of-two scale per 128-value group
+
+// Largest |x| of the two bf16 values of d, as a bf16 bit pattern in both halves (for finite
+// magnitudes the bit pattern orders like the value; NaN and infinity compare above them).
+__device__ __forceinline__ uint32_t abs_max2(uint32_t d, uint32_t m)
+{
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, d & 0x7FFF7FFFu),
+                                                        __builtin_bit_cast(u16x2_t, m)));
+}
+
+__device__ __forceinline__ uint32_t abs_max8(uint4 v, uint32_t m)
+{
+    return abs_max2(v.w, abs_max2(v.z, abs_max2(v.y, abs_max2(v.x, m))));
+}
+
+// The larger of the two 16-bit halves of m2, as a 32-bit integer (cross-lane maxima compare
+// these, never packed pairs).
+__device__ __forceinline__ uint32_t fold_halves(uint32_t m2)
+{
+    return (m2 >> 16) > (m2 & 0xFFFFu) ? (m2 >> 16) : (m2 & 0xFFFFu);
+}
+
+// Exponent e of a group from the bf16 pattern m of its largest magnitude: 2^e * max lands in
+// [2^15, 2^16). A bf16 pattern with exponent field b is in [2^(b-127), 2^(b-126)), so
+// e = 142 - b; e is capped at 126 so that 2^e and 2^-e are normal fp32 numbers (the groups it
+// affects hold only values below 2^-110, all exact in fp16 at that scale). An all-zero group
+// gets 126 too.
+__device__ __forceinline__ int group_exponent(uint32_t m)
+{
+    const int e = 142 - (int)(m >> 7);
+    return e < 126 ? e : 126;
+}
+
+__device__ __forceinline__ float pow2f(int e) { return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23); }
+
+// fp16 pair (a * p, b * p) of two fp32 values, each product rounded once (nearest even): one
+// v_fma_mixlo_f16 and one v_fma_mixhi_f16 with fp32 sources.
+__device__ __forceinline__ uint32_t pack_scaled(float a, float b, float p)
+{
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "=v"(r) : "v"(a), "v"(p));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "+v"(r) : "v"(b), "v"(p));
+    return r;
+}
+
+// Eight consecutive bf16 activations (x0..x7 in natural order) times p = 2^e as fp16, re-paired
+// as (x0,x4) (x1,x5) (x2,x6) (x3,x7) to match unpack_word. The products are exact, so each value
+// is rounded once, to fp16.
+__device__ __forceinline__ uint4 stage_words(uint4 v, float p)
+{
+    auto lo = [](uint32_t d) { return __builtin_bit_cast(float, d << 16); };
+    auto hi = [](uint32_t d) { return __builtin_bit_cast(float, d & 0xFFFF0000u); };
+    return make_uint4(pack_scaled(lo(v.x), lo(v.z), p), pack_scaled(hi(v.x), hi(v.z), p),
+                      pack_scaled(lo(v.y), lo(v.w), p), pack_scaled(hi(v.y), hi(v.w), p));
+}
+
+// Largest of a per-lane value over the 16 lanes of a DPP row (integer compare).
+__device__ __forceinline__ uint32_t row_max16(uint32_t m)
+{
+    int x = (int)m;
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));
+    return (uint32_t)x;
+}
+
+// Largest over each quad of lanes.
+__device__ __forceinline__ uint32_t quad_max(uint32_t m)
+{
+    int x = (int)m;
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+    return (uint32_t)x;
+}
 
 // Cross-lane exchange across lane-index bit `bit` without LDS: DPP within a 16-lane row for bits
 // 0-3 (quad permutes, then the half-row and row mirrors, each a bijection between the two halves of
@@ -239,8 +269,8 @@ __device__ __forceinline__ int fold_rows(float (&v)[U], int lane)
 // side, L lanes per row; lane p of a row owns the 16-byte chunks p, p+L, p+2L, ... of that row, so
 // each load instruction covers R runs of L*16 contiguous bytes (whole cache lines). Activations are
 // staged once per work-group in LDS, re-paired and laid out [token][word-in-chunk j][chunk c] so
-// the L lanes of a row read consecutive 16-byte slots, followed by the per-chunk offsets
-// -136*sum(x) and, for the grouped-expert form, the expert ids (so id lookups never wait on
+// the L lanes of a row read consecutive 16-byte slots, followed by the per-chunk factors 2^-e
+// of their groups and, for the grouped-expert form, the expert ids (so id lookups never wait on
 // outstanding weight loads). A wave walks a flat sequence of (row block, chunk batch) items with
 // one item of prefetch. Every load is unconditional: rows past the end re-read the last row,
 // rows of an out-of-range expert read the activation row (valid memory of at least K*2 bytes, so
@@ -469,19 +499,15 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     load(bufA, std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- stage activations: re-pair, transpose to [j][c], and form per-chunk offsets
+    // ---- stage activations: scale each group to fp16, re-pair, transpose to [j][c], and keep
+    // the per-chunk factor 2^-e of its group
     auto stage = [&](int t, int w, uint4 v) {
-        xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
-        float sum = 0.0f;
-        sum = dot2(v.x, 0x3F803F80u, sum);
-        sum = dot2(v.y, 0x3F803F80u, sum);
-        sum = dot2(v.z, 0x3F803F80u, sum);
-        sum = dot2(v.w, 0x3F803F80u, sum);
-        // The four words of a chunk sit in four consecutive lanes (KW is a multiple of 16).
-        sum += dpp_partner(sum, 0);
-        sum += dpp_partner(sum, 1);
+        // The 16 words of a scale group sit in the 16 lanes of one DPP row (KW is a multiple of
+        // 16 and the word index advances by a multiple of 64 per pass), all active or all not.
+        const int e = group_exponent(row_max16(fold_halves(abs_max8(v, 0u))));
+        xs[t * KW + (w & 3) * CPR + (w >> 2)] = stage_words(v, pow2f(e));
         if ((w & 3) == 0)
-            bs[t * CPR + (w >> 2)] = -kOffset * sum;
+            bs[t * CPR + (w >> 2)] = pow2f(-e);
     };
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -569,22 +595,32 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         for (int v = 0; v < V; ++v) {
             const int c = pr + L * (v + V * cp_b);
             uint4 xq[MT][4];
-            float off[MT];
+            float fct[MT];
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     xq[t][j] = xs[t * KW + j * CPR + c];
-                off[t] = bs[t * CPR + c];
+                fct[t] = bs[t * CPR + c];
+            }
+            // Combine form: a slot whose id names no expert adds nothing at all (its loads read
+            // expert 0, whose scales or products need not be finite).
+            bool take = true;
+            float wslot = 1.0f;
+            if constexpr (MODE == VALU_COMBINE) {
+                const int slot = (L * V * cp_b) / CPRW;
+                const int32_t e = ids_s[slot];
+                take = e >= 0 && e < E;
+                wslot = rw_s[slot];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float s = half_bits_to_float(buf.s[v][u]);
-                if constexpr (MODE == VALU_COMBINE)
-                    s *= rw_s[(L * V * cp_b) / CPRW];
+                const float s = half_bits_to_float(buf.s[v][u]) * wslot;
 #pragma unroll
-                for (int t = 0; t < MT; ++t)
-                    acc[u][t] = fmaf(s, chunk_dot(buf.w[v][u], xq[t], off[t]), acc[u][t]);
+                for (int t = 0; t < MT; ++t) {
+                    const float a = fmaf(s, chunk_dot(buf.w[v][u], xq[t]) * fct[t], acc[u][t]);
+                    acc[u][t] = take ? a : acc[u][t];
+                }
             }
         }
         if (cp_b == nb - 1)
@@ -617,7 +653,7 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
 // range of rows and split K: wave w owns the K slice of chunks [w*L*CL, (w+1)*L*CL). Inside a wave,
 // L lanes walk a row (lane p owns chunks p, p+L, ... of the slice) and R = 64/L rows sit side by
 // side, so every load instruction covers R runs of L*16 contiguous bytes. Each lane keeps its CL
-// chunks of activations (re-paired) and their -136*sum(x) offsets in registers for the whole
+// chunks of activations (as fp16, re-paired) and their group factors 2^-e in registers for the whole
 // kernel; they are requested before the first weights, so they are ready while the weights are
 // still in flight, with no LDS staging and no barrier before the stream starts. Rows go U*R at a
 // time with one item of prefetch and unconditional loads (rows past the block's end re-read its
@@ -686,6 +722,7 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
     const uint4 *wq[CL];
     const uint16_t *sq[CL];
     float wt[CL];
+    bool take[CL];   // combine form: false for a slot whose id names no expert (adds nothing)
 #pragma unroll
     for (int j = 0; j < CL; ++j) {
         if constexpr (GATHER) {
@@ -697,10 +734,12 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
             wq[j] = qw + ee * N * CPR + (c0 - slot * CPR);
             sq[j] = sc + ee * N * GPR + ((c0 - slot * CPR) >> 2);
             wt[j] = ok ? rw[slot] : 0.0f;
+            take[j] = ok;
         } else {
             wq[j] = qw + wave * (L * CL) + L * j;
             sq[j] = sc + ((wave * (L * CL) + L * j) >> 2);
             wt[j] = 1.0f;
+            take[j] = true;
         }
     }
     int ld_item = 0;
@@ -732,22 +771,23 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
     __builtin_amdgcn_sched_barrier(0);   // keep the activation loads ahead of the weight loads
     Buf bufA, bufB;
     load(bufA);
-    float off[MT][CL];
+    // Stage the activations in registers as fp16: chunk cbase + L*j of a group sits in four
+    // consecutive lanes (L is a multiple of 4 and chunk runs start at multiples of 4).
+    float fct[MT][CL];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
         for (int j = 0; j < CL; ++j) {
-            float sum = 0.0f;
+            uint32_t m = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 v = xq[t][j][q];
-                sum = dot2(v.x, 0x3F803F80u, sum);
-                sum = dot2(v.y, 0x3F803F80u, sum);
-                sum = dot2(v.z, 0x3F803F80u, sum);
-                sum = dot2(v.w, 0x3F803F80u, sum);
-                xq[t][j][q] = pair_activations(v);
-            }
-            off[t][j] = -kOffset * sum;
+            for (int q = 0; q < 4; ++q)
+                m = abs_max8(xq[t][j][q], m);
+            const int e = group_exponent(quad_max(fold_halves(m)));
+            const float p = pow2f(e);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xq[t][j][q] = stage_words(xq[t][j][q], p);
+            fct[t][j] = pow2f(-e);
         }
     }
 
@@ -763,12 +803,13 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
         for (int j = 0; j < CL; ++j)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float s = half_bits_to_float(buf.s[j][u]);
-                if constexpr (GATHER)
-                    s *= wt[j];
+                const float s = half_bits_to_float(buf.s[j][u]) * wt[j];
 #pragma unroll
-                for (int t = 0; t < MT; ++t)
-                    acc[u][t] = fmaf(s, chunk_dot(buf.w[j][u], xq[t][j], off[t][j]), acc[u][t]);
+                for (int t = 0; t < MT; ++t) {
+                    const float a =
+                        fmaf(s, chunk_dot(buf.w[j][u], xq[t][j]) * fct[t][j], acc[u][t]);
+                    acc[u][t] = take[j] ? a : acc[u][t];
+                }
             }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
@@ -812,7 +853,7 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
 }
 
 // ------------------------------------------------------------------------------------------
-// Split-K GEMV on the 4x4x4 matrix cores for 2..16 tokens. v_mfma_f32_4x4x4_16b_bf16 computes 16
+// Split-K GEMV on the 4x4x4 matrix cores for 2..16 tokens. v_mfma_f32_4x4x4_16b_f16 computes 16
 // independent 4x4x4 blocks per wave: block b lives in lanes 4b..4b+3, lane 4b+q supplies row q of
 // A and column q of B (four consecutive k values each) and receives D[r][q], r = 0..3, in its
 // four result registers. Here A holds weights and B activations (4 tokens per token group, TG
@@ -823,18 +864,26 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
 // fewer activation registers than padding the tokens to 16 columns. A row step is 64 / BR rows;
 // BR = 8 serves rows whose chunk count is a multiple of 8 but not of 16 (K = 2304). Each
 // decoded weight word feeds two MFMAs per token group (k order 0,4,1,5 and 2,6,3,7, the order of
-// the re-paired activations); a chunk's block sum starts at -136 * (the token's sum over the
-// chunk) and is scaled by its row's fp16 scale, broadcast from lane 4b+r by DPP. After an item
+// the re-paired activations); a chunk's block sum is multiplied by the factor 2^-e of the token's
+// group and by its row's fp16 scale, broadcast from lane 4b+r by DPP. After an item
 // the BR blocks' partials of a row group are added by DPP row rotations and permlane swaps
 // (all 16 lanes with the same lane % 4 and row group), and the waves of a
 // work-group, which split K as in the split-K kernel, meet in LDS after the last item.
 // ------------------------------------------------------------------------------------------
-typedef short bf16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
-
-__device__ __forceinline__ bf16x4_t as_bf16x4(uint32_t a, uint32_t b)
+__device__ __forceinline__ f16x4_t as_f16x4(uint32_t a, uint32_t b)
 {
     const uint2 v = {a, b};
-    return __builtin_bit_cast(bf16x4_t, v);
+    return __builtin_bit_cast(f16x4_t, v);
+}
+
+// Largest of a per-lane value over the lanes 4b + (lane % 4), b = 4k .. 4k + 3, of a DPP row
+// (the four blocks that hold the chunks of one scale group of one token).
+__device__ __forceinline__ uint32_t blocks_max4(uint32_t m)
+{
+    int x = (int)m;
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));
+    return (uint32_t)x;
 }
 
 // Sum of v over the BR lanes 4b + (lane % 4) of a row group, b = BR h .. BR h + BR - 1 (one value
@@ -934,22 +983,24 @@ gemv_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     __builtin_amdgcn_sched_barrier(0);   // keep the activation loads ahead of the weight loads
     Buf bufA, bufB;
     load(bufA);
-    float off[TG][CL];
+    // Stage the activations in registers as fp16. The chunks of one scale group of token 4g + q
+    // sit in lanes 4b + q for four consecutive blocks b of a DPP row (BR and the chunk steps are
+    // multiples of 4).
+    float fct[TG][CL];
 #pragma unroll
     for (int g = 0; g < TG; ++g)
 #pragma unroll
         for (int j = 0; j < CL; ++j) {
-            float sum = 0.0f;
+            uint32_t m = 0;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint4 v = xq[g][j][w];
-                sum = dot2(v.x, 0x3F803F80u, sum);
-                sum = dot2(v.y, 0x3F803F80u, sum);
-                sum = dot2(v.z, 0x3F803F80u, sum);
-                sum = dot2(v.w, 0x3F803F80u, sum);
-                xq[g][j][w] = pair_activations(v);
-            }
-            off[g][j] = -kOffset * sum;
+            for (int w = 0; w < 4; ++w)
+                m = abs_max8(xq[g][j][w], m);
+            const int e = group_exponent(blocks_max4(fold_halves(m)));
+            const float p = pow2f(e);
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                xq[g][j][w] = stage_words(xq[g][j][w], p);
+            fct[g][j] = pow2f(-e);
         }
 
     int cp_item = 0;
@@ -975,19 +1026,19 @@ gemv_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                     half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xFF, 0xF, 0xF, false))};
 #pragma unroll
                 for (int g = 0; g < TG; ++g) {
-                    const float o = off[g][j];
-                    f32x4_t d = {o, o, o, o};
+                    f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         const uint4 xv = xq[g][j][w];
-                        d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
-                            as_bf16x4(p[w][0], p[w][1]), as_bf16x4(xv.x, xv.y), d, 0, 0, 0);
-                        d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
-                            as_bf16x4(p[w][2], p[w][3]), as_bf16x4(xv.z, xv.w), d, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                            as_f16x4(p[w][0], p[w][1]), as_f16x4(xv.x, xv.y), d, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                            as_f16x4(p[w][2], p[w][3]), as_f16x4(xv.z, xv.w), d, 0, 0, 0);
                     }
+                    const float f = fct[g][j];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        acc[u][g][r] = fmaf(s4[r], d[r], acc[u][g][r]);
+                        acc[u][g][r] = fmaf(s4[r], d[r] * f, acc[u][g][r]);
                 }
             }
         // The BR blocks' partials of each (row, token), then lane 4b + q with bc = r < 4 parks
@@ -1103,7 +1154,7 @@ __device__ void moe_group_entries(const int32_t *__restrict__ ids, int P, int32_
 }
 
 // Activations of every token staged re-paired as [token][word j][chunk] (16 bytes each), with
-// the per-chunk offsets -136 * sum(x) in bs[token][chunk]. The staging loop runs over the flat
+// the per-chunk group factors 2^-e in bs[token][chunk]. The staging loop runs over the flat
 // (token, word) index; its first kMoeXPre passes use words requested by moe_prefetch_activations
 // before the expert grouping, so their latency overlaps the id load and the grouping, and only
 // the rest (more than kMoeXPre * threads words) is loaded here. Ends without a barrier.
@@ -1130,21 +1181,16 @@ __device__ void moe_stage_activations(const uint16_t *__restrict__ X, int64_t ld
     const int KW = K >> 3;
     const int CPR = K >> 5;
     const int total = M * KW;
-    // The four words of a chunk sit in four consecutive lanes and the same token (KW and the
-    // thread count are multiples of 16), and a quad is either all below `total` or all above.
+    // The 16 words of a scale group sit in the 16 lanes of one DPP row and the same token (KW
+    // and the thread count are multiples of 16), and a row is either all below `total` or all
+    // above.
     auto stage = [&](int idx, uint4 v) {
         const int t = idx / KW;
         const int w = idx - t * KW;
-        xs[t * KW + (w & 3) * CPR + (w >> 2)] = pair_activations(v);
-        float sum = 0.0f;
-        sum = dot2(v.x, 0x3F803F80u, sum);
-        sum = dot2(v.y, 0x3F803F80u, sum);
-        sum = dot2(v.z, 0x3F803F80u, sum);
-        sum = dot2(v.w, 0x3F803F80u, sum);
-        sum += dpp_partner(sum, 0);
-        sum += dpp_partner(sum, 1);
+        const int e = group_exponent(row_max16(fold_halves(abs_max8(v, 0u))));
+        xs[t * KW + (w & 3) * CPR + (w >> 2)] = stage_words(v, pow2f(e));
         if ((w & 3) == 0)
-            bs[t * CPR + (w >> 2)] = -kOffset * sum;
+            bs[t * CPR + (w >> 2)] = pow2f(-e);
     };
 #pragma unroll
     for (int f = 0; f < kMoeXPre; ++f) {
@@ -1169,7 +1215,7 @@ __device__ void moe_stage_activations(const uint16_t *__restrict__ X, int64_t ld
 // virtual entries of one expert read the same rows in consecutive waves of a work-group and a
 // second token of an expert finds those rows in the L2 cache; within an item the wave streams R
 // rows of the entry's expert like the staged kernel (activations of all M tokens staged in LDS,
-// re-paired, with their chunk offsets) and accumulates one product per pair. Empty pair slots are
+// re-paired, with their chunk factors) and accumulates one product per pair. Empty pair slots are
 // skipped by wave-uniform branches around the arithmetic only (the loads stay straight-line).
 // One pair per virtual entry (MT = 1) measured fastest on MI355X: larger MT costs registers, and
 // so waves, on every expert for the few that more than one token chose. Block-major order also
@@ -1287,7 +1333,7 @@ gemv_moe_batched_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict
 #pragma unroll
                 for (int h = 0; h < 4; ++h)
                     xq[h] = xs[m * KW + h * CPR + c];
-                acc[j] = fmaf(s, chunk_dot(buf.w[q], xq, bs[m * CPR + c]), acc[j]);
+                acc[j] = fmaf(s, chunk_dot(buf.w[q], xq) * bs[m * CPR + c], acc[j]);
             }
         }
         if (cp_b == nb - 1) {
@@ -1330,7 +1376,7 @@ gemv_moe_batched_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict
 // ------------------------------------------------------------------------------------------
 // Grouped-expert GEMV for several tokens on the 4x4x4 matrix cores. The same set-up as the VALU
 // form (entries grouped by expert in LDS, activations of every token staged re-paired with their
-// chunk offsets), with virtual entries of up to 4 entries of one expert. Items are (virtual entry,
+// chunk factors), with virtual entries of up to 4 entries of one expert. Items are (virtual entry,
 // block of rows) in expert-major order: the tokens that share an expert share its items, so the
 // block-major order the VALU form needs for L2 reuse is not needed, and consecutive waves stream
 // an expert's rows contiguously (16 tokens x top-8 of 256: 58.1 us against 60.5 block-major and
@@ -1474,7 +1520,7 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
 #pragma unroll
             for (int w = 0; w < 4; ++w)
                 xv[w] = xs[m * KW + w * CPR + c];
-            const float o = bs[m * CPR + c];
+            const float f = bs[m * CPR + c];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 uint32_t p[4][4];
@@ -1485,17 +1531,17 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
                     half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0x55, 0xF, 0xF, false)),
                     half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xAA, 0xF, 0xF, false)),
                     half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xFF, 0xF, 0xF, false))};
-                f32x4_t d = {o, o, o, o};
+                f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
-                        as_bf16x4(p[w][0], p[w][1]), as_bf16x4(xv[w].x, xv[w].y), d, 0, 0, 0);
-                    d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
-                        as_bf16x4(p[w][2], p[w][3]), as_bf16x4(xv[w].z, xv[w].w), d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                        as_f16x4(p[w][0], p[w][1]), as_f16x4(xv[w].x, xv[w].y), d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                        as_f16x4(p[w][2], p[w][3]), as_f16x4(xv[w].z, xv[w].w), d, 0, 0, 0);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[u][r] = fmaf(s4[r], d[r], acc[u][r]);
+                    acc[u][r] = fmaf(s4[r], d[r] * f, acc[u][r]);
             }
         }
         if (cp_b == nb - 1) {
@@ -1537,16 +1583,16 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
 }
 
 // ------------------------------------------------------------------------------------------
-// MFMA GEMV for 2..16 tokens (v_mfma_f32_16x16x32_bf16), computed as D = X * W^T so that each
+// MFMA GEMV for 2..16 tokens (v_mfma_f32_16x16x32_f16), computed as D = X * W^T so that each
 // lane's four outputs belong to one weight row: lane (i = l%16, g = l/16) supplies, for word j of
-// chunk 4s+g of a group s, the 8 activations of token i (A operand, re-paired) and the 8 decoded
-// weights 136+q of row i (B operand); D[4g+r][i] is token 4g+r of row i. The 136 offset is removed
-// by starting each group's D at -136 * (the token's sum over the group), and the group total is
-// scaled by row i's fp16 scale in fp32 -- one 2-byte scale load per tile and group.
+// chunk 4s+g of a group s, the 8 fp16 activations of token i (A operand, re-paired) and the 8
+// decoded weights q of row i (B operand); D[4g+r][i] is token 4g+r of row i over the group. Each
+// group total is multiplied by the factor 2^-e of token 4g+r's group and by row i's fp16 scale in
+// fp32 -- one 2-byte scale load per tile and group.
 //
 // XLDS (K*32 bytes fit in LDS): the activations of all 16 token slots are staged once per work-group
 // in fragment order ([group][word][lane], 16 bytes each) together with the per-(group, token)
-// offsets; work-groups are persistent and stream tiles of 16 rows in a flat (row block, group)
+// factors; work-groups are persistent and stream tiles of 16 rows in a flat (row block, group)
 // sequence with one item of prefetch. Otherwise each wave reads its activation fragments from
 // global memory with its weights, KS waves of a work-group split the groups of K, and their
 // partial sums are added through LDS in a fixed order.
@@ -1566,13 +1612,26 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
 // group, so the four lanes of a token cover 64 contiguous bytes) and exchanged through LDS into
 // operand order (lane (i, g), word j comes from lane (i, j) of instruction g).
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+__device__ __forceinline__ f16x8_t as_f16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
     u32x4_t v = {a, b, c, d};
-    return __builtin_bit_cast(bf16x8_t, v);
+    return __builtin_bit_cast(f16x8_t, v);
 }
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return as_bf16x8(v.x, v.y, v.z, v.w); }
+__device__ __forceinline__ f16x8_t as_f16x8(uint4 v) { return as_f16x8(v.x, v.y, v.z, v.w); }
+
+// Largest of a per-lane value over the lanes 16 and 32 apart (v_permlane16_swap and
+// v_permlane32_swap with both operands holding it; the same exchange as swap_fold).
+__device__ __forceinline__ uint32_t max_over_rows(uint32_t m)
+{
+    uint32_t a = m, b = m;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    m = a > b ? a : b;
+    a = m;
+    b = m;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return a > b ? a : b;
+}
 
 // Scale words of an item: with GU even, dword k holds the fp16 scales of groups 2k (low half) and
 // 2k + 1 (high half); with GU odd, word k holds group k's scale in its low half.
@@ -1644,7 +1703,6 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     const int CPR = K >> 5;
     const int GPR = K >> 7;
     const int tok = i < M ? i : M - 1;
-    const bf16x8_t c136 = as_bf16x8(0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u);
 
     // Rows of a wave: base(rb) + lane_row[t] for tile t. The base of the last row block is pulled
     // back so that the block ends at row N-1 (rows computed twice get identical bits); when N is
@@ -1681,20 +1739,22 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 r = (int)N - 1;
             loff[t][h] = (uint32_t)((r * CPR + (lane & 7)) * 16);
         }
-    auto mma_group = [&](const uint4 (&wv)[T], const float (&scv)[T], const bf16x8_t xb[4],
-                         f32x4_t off, f32x4_t (&acc)[T]) {
+    // One group of every tile: D[4g+r][i] over the group's 128 k values, times the factor 2^-e of
+    // token 4g+r's group (fac[r]) and row i's scale.
+    auto mma_group = [&](const uint4 (&wv)[T], const float (&scv)[T], const f16x8_t xb[4],
+                         f32x4_t fac, f32x4_t (&acc)[T]) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             uint32_t p[4][4];
             unpack_chunk(wv[t], p);
-            f32x4_t d = off;
+            f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    xb[j], as_bf16x8(p[j][0], p[j][1], p[j][2], p[j][3]), d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    xb[j], as_f16x8(p[j][0], p[j][1], p[j][2], p[j][3]), d, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                acc[t][r] = fmaf(scv[t], d[r], acc[t][r]);
+                acc[t][r] = fmaf(scv[t], d[r] * fac[r], acc[t][r]);
         }
     };
     auto store = [&](int64_t rb, const f32x4_t (&acc)[T]) {
@@ -1754,27 +1814,28 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         Buf bufA, bufB;
         load(bufA);
 
-        // Stage the fragments of the token slots and the per-(group, token) offsets.
-        for (int idx = threadIdx.x; idx < GPR * 16 * SLOTS; idx += blockDim.x) {
-            const int s = idx / (16 * SLOTS), j = (idx / (4 * SLOTS)) & 3, l = idx & (4 * SLOTS - 1);
-            const int m = l & (SLOTS - 1), gg = l / SLOTS;
-            const int tm = m < M ? m : M - 1;
-            const uint4 v = reinterpret_cast<const uint4 *>(X + (int64_t)tm * ldx)[16 * s + 4 * gg + j];
-            xl[idx] = pair_activations(v);
-        }
+        // Stage the token slots as fp16, one (group s, MFMA row m) per thread: the group's 16
+        // activation words of the token in slot m % SLOTS (rows past M repeat token M-1; with 8
+        // slots, rows 8-15 read slots 0-7 again), scaled by the group's power of two into
+        // fragment order ([group][word j][chunk gg][slot]), and its factor 2^-e for row m.
         for (int idx = threadIdx.x; idx < GPR * 16; idx += blockDim.x) {
             const int s = idx >> 4, m = idx & 15;
-            const int tm = m < M ? m : M - 1;
+            const int slot = m & (SLOTS - 1);
+            const int tm = slot < M ? slot : M - 1;
             const uint4 *xr = reinterpret_cast<const uint4 *>(X + (int64_t)tm * ldx) + 16 * s;
-            float sum = 0.0f;
-            for (int q = 0; q < 16; ++q) {
-                const uint4 v = xr[q];
-                sum = dot2(v.x, 0x3F803F80u, sum);
-                sum = dot2(v.y, 0x3F803F80u, sum);
-                sum = dot2(v.z, 0x3F803F80u, sum);
-                sum = dot2(v.w, 0x3F803F80u, sum);
+            uint32_t mx = 0;
+#pragma unroll 4
+            for (int q = 0; q < 16; ++q)
+                mx = abs_max8(xr[q], mx);
+            const int e = group_exponent(fold_halves(mx));
+            offl[idx] = pow2f(-e);
+            if (m < SLOTS) {
+                const float pe = pow2f(e);
+#pragma unroll 4
+                for (int q = 0; q < 16; ++q)
+                    xl[(s * 4 + (q & 3)) * (4 * SLOTS) + (q >> 2) * SLOTS + m] =
+                        stage_words(xr[q], pe);
             }
-            offl[idx] = -kOffset * sum;
         }
         __syncthreads();
         if (!active)
@@ -1811,12 +1872,12 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
 #pragma unroll
             for (int u = 0; u < GU; ++u) {
                 const int s = cp_s + u;
-                bf16x8_t xb[4];
+                f16x8_t xb[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    xb[j] = as_bf16x8(xl[(s * 4 + j) * (4 * SLOTS) + (i & (SLOTS - 1)) + SLOTS * g]);
-                const float4 o4 = *reinterpret_cast<const float4 *>(offl + s * 16 + 4 * g);
-                const f32x4_t off = {o4.x, o4.y, o4.z, o4.w};
+                    xb[j] = as_f16x8(xl[(s * 4 + j) * (4 * SLOTS) + (i & (SLOTS - 1)) + SLOTS * g]);
+                const float4 f4 = *reinterpret_cast<const float4 *>(offl + s * 16 + 4 * g);
+                const f32x4_t fac = {f4.x, f4.y, f4.z, f4.w};
                 float scv[T];
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
@@ -1826,7 +1887,7 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                         sw[k] = buf.s[k][t];
                     scv[t] = mfma_scale<GU>(sw, u);
                 }
-                mma_group(wl[u], scv, xb, off, acc);
+                mma_group(wl[u], scv, xb, fac, acc);
             }
             if (cp_s + GU == GPR) {
                 store(cp_rb, acc);
@@ -1859,6 +1920,10 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         // activation fragments [GU][4][64] (16 bytes each).
         uint4 *stage_w = lds + (KS > 1 ? WPB * T * 64 : 0) + wave * (T + 4) * GU * 64;
         uint4 *stage_x = stage_w + T * GU * 64;
+        // Per wave, the factors 2^-e of the item's groups for the 16 token rows: [GU][16].
+        float *stage_f = reinterpret_cast<float *>(lds + (KS > 1 ? WPB * T * 64 : 0) +
+                                                   (GLINES ? WPB * (T + 4) * GU * 64 : 0)) +
+                         wave * GU * 16;
         const int64_t rb = blockIdx.x;
         const int gpk = GPR / KS;
         const int n_items = gpk / GU;
@@ -1932,15 +1997,28 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                         xr[u][j] = buf.x[u][j];
                 }
             }
+            // Stage each group of the item as fp16: lane (i, g) holds chunk g of token i's group,
+            // so the four chunks of a token sit 16 lanes apart; lane (i, 0) parks the factor of
+            // token i in the wave's LDS slot and lane (i, g) reads those of tokens 4g..4g+3.
 #pragma unroll
             for (int u = 0; u < GU; ++u) {
-                bf16x8_t xb[4];
-                f32x4_t off = {0.0f, 0.0f, 0.0f, 0.0f};
+                uint32_t mx = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    xb[j] = as_bf16x8(pair_activations(xr[u][j]));
-                    off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], c136, off, 0, 0, 0);
-                }
+                for (int j = 0; j < 4; ++j)
+                    mx = abs_max8(xr[u][j], mx);
+                const int e = group_exponent(max_over_rows(fold_halves(mx)));
+                const float pe = pow2f(e);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xr[u][j] = stage_words(xr[u][j], pe);
+                if (g == 0)
+                    stage_f[u * 16 + i] = pow2f(-e);
+                f16x8_t xb[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xb[j] = as_f16x8(xr[u][j]);
+                const float4 f4 = *reinterpret_cast<const float4 *>(stage_f + u * 16 + 4 * g);
+                const f32x4_t fac = {f4.x, f4.y, f4.z, f4.w};
                 float scv[T];
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
@@ -1950,7 +2028,7 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                         sw[k] = buf.s[k][t];
                     scv[t] = mfma_scale<GU>(sw, u);
                 }
-                mma_group(wl[u], scv, xb, -off, acc);
+                mma_group(wl[u], scv, xb, fac, acc);
             }
         };
         // A ring of RING item buffers: the loads of item it + RING - 1 are issued before item it is
@@ -2006,8 +2084,9 @@ unpack_kernel(const uint32_t *__restrict__ qw, int8_t *__restrict__ out, int64_t
         int8_t q[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            q[i] = (int8_t)((int)bf16_bits_to_float(p[i] & 0xFFFFu) - 136);
-            q[i + 4] = (int8_t)((int)bf16_bits_to_float(p[i] >> 16) - 136);
+            const f16x2_t h = __builtin_bit_cast(f16x2_t, p[i]);
+            q[i] = (int8_t)(int)h.x;
+            q[i + 4] = (int8_t)(int)h.y;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)

@@ -9,7 +9,7 @@ static constexpr int kMaxWavesPerCu = 32;
 
 int64_t valu_max_k(int MT, int64_t lds_limit)
 {
-    // Activations (2 bytes per value) plus one fp32 offset per 32 values, per token.
+    // Activations (2 bytes per value) plus one fp32 group factor per 32 values, per token.
     const int64_t per_k = 2 * MT;
     int64_t k = (lds_limit * 32) / (per_k * 32 + 4 * MT);
     k -= k % 128;
@@ -205,7 +205,7 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
         const int64_t row_blocks = (N + rows_per_block - 1) / rows_per_block;
         if (p->xlds) {
             // 16 token slots (8 for the 8-slot form) of activation fragments (16 bytes per
-            // lane, word and group) plus one fp32 offset per (group, token); with line loads,
+            // lane, word and group) plus one fp32 factor per (group, token); with line loads,
             // one 1 KiB staging slot per group of an item and wave.
             p->lds_bytes = gpr * (p->slots8 ? 2048 : 4096) + gpr * 64 +
                            (p->lines ? (int64_t)wpb * p->V * 1024 : 0);
@@ -220,10 +220,12 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
             const int64_t cap = (int64_t)cus * per_cu;
             p->blocks = row_blocks < cap ? row_blocks : cap;
         } else {
-            // K-split partial sums, and with line loads a staging slot per wave for the
-            // weights (T x groups per item) and activation fragments (4 x groups per item).
+            // K-split partial sums, with line loads a staging slot per wave for the weights
+            // (T x groups per item) and activation fragments (4 x groups per item), and per wave
+            // the 16 token rows' group factors of an item (groups per item x 64 bytes).
             p->lds_bytes = (p->KS > 1 ? (int64_t)wpb * p->T * 64 * 16 : 0) +
-                           (p->lines ? (int64_t)wpb * (p->T + 4) * p->V * 1024 : 0);
+                           (p->lines ? (int64_t)wpb * (p->T + 4) * p->V * 1024 : 0) +
+                           (int64_t)wpb * p->V * 64;
             if (p->lds_bytes > lds_limit)
                 return false;
             p->blocks = row_blocks;
@@ -302,9 +304,11 @@ Plan splitk(int MT, int L, int CL, int U, bool moe)
 static bool mfma_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, Plan *p)
 {
     const int64_t gpr = K / 128;
+    // Groups per item: 2 first for 8-wave work-groups (163840 x 2304 at 16 tokens, same-box sweep:
+    // 45.1 us against 47.0 with 6), 6 first for the 4-wave form.
     auto lines = [&](int wpb, Plan *out) {
-        static const int gus[] = {6, 4, 2};
-        for (int gu : gus) {
+        static const int gus8[] = {2, 6, 4}, gus4[] = {6, 4, 2};
+        for (int gu : (wpb == 8 ? gus8 : gus4)) {
             Plan c{};
             c.kind = PLAN_MFMA;
             c.T = 1;
@@ -332,7 +336,7 @@ static bool mfma_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, P
         return true;
     if (N / 64 >= (int64_t)cus * 4 / 5 && global(4, 4, 2, 4, true, p))
         return true;
-    if (N / 32 >= cus && global(2, 4, 2, 4, true, p))
+    if (N / 32 >= cus && global(2, 4, 2, 4, false, p))
         return true;
     if (gpr % 16 == 0 && global(1, 8, 2, 8, true, p))
         return true;
@@ -382,7 +386,7 @@ static bool mfma4_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, 
     int bpc = 1;
     if (cpr % 16 == 0 && cpr >= 128) {
         c.L = 16;
-        c.V = (c.MT == 2 && cpr >= 256) || cpr / 32 > 8 ? 4 : 2;
+        c.V = cpr / 32 > 8 ? 4 : 2;
         c.U = c.MT == 1 && tall ? 2 : 1;
         bpc = tall ? 2 : 1;
     } else if (cpr % 8 == 0 && cpr <= 64) {
@@ -446,11 +450,11 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     const bool k2048 = cpr % 64 == 0;
 
     const int split_bpc = (int)(c64 >= 8 ? 1 : 8 / (c64 > 0 ? c64 : 1));
-    // K = 4096, one token, tall: split K over 4 waves of 32 lanes with 2 row steps in flight,
-    // 2 work-groups per CU (28672 x 4096: 11.44 us against 11.86 for the staged kernel; 16384 x
-    // 4096: 7.80 against 8.05; 57344 x 4096: 20.3 against 21.1).
+    // K = 4096, one token, tall: split K over 4 waves of 32 lanes with 4 row steps in flight,
+    // one work-group per CU (28672 x 4096, same-box sweep: 11.84 us against 12.25 with 2 row steps
+    // and 2 work-groups per CU and 11.92 for the staged kernel).
     if (!moe && M == 1 && K == 4096 && rows >= 16384 &&
-        try_plan(splitk(1, 32, 1, 2, false), 2, M, N, K, topk, cus, lds_limit, p))
+        try_plan(splitk(1, 32, 1, 4, false), 1, M, N, K, topk, cus, lds_limit, p))
         return true;
     // K = 2048, one token: tall matrices take the staged kernel with 32 lanes and 2 chunks per
     // item (14336 x 2048: 4.9 us against 6.9 us for 64 lanes), the others split K like the
@@ -458,12 +462,12 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     if (!moe && M == 1 && K == 2048 && rows >= 8192 &&
         try_plan(valu(1, 32, 2, 1, false), 4, M, N, K, topk, cus, lds_limit, p))
         return true;
-    // 2-8 tokens on tall matrices (at least 0.8 x CUs blocks of 128 rows) whose rows are not a
+    // 5-8 tokens on tall matrices (at least 0.8 x CUs blocks of 128 rows) whose rows are not a
     // multiple of 2048 values: the staged whole-line 16x16x32 form with 8 token slots and 2 groups
-    // per item, where two 8-wave work-groups fit in one CU's LDS (163840 x 2304, same-box A/B:
-    // 33.0 us at 2 tokens and 34.3 at 4 against 34.4 and 37.0 for the 4x4x4 kernel; 35.1 at 5
-    // and 37.2 at 8 against 38.7 and 39.6 with 16 slots staged).
-    if (!moe && M >= 2 && M <= 8 && K % 2048 != 0 &&
+    // per item, where two 8-wave work-groups fit in one CU's LDS. 2-4 tokens take the 4x4x4
+    // kernel below (163840 x 2304, same-box sweep: 36.1 us at 2 tokens and 38.3 at 4 against
+    // 40.3 and 39.6 for the 8-slot form).
+    if (!moe && M >= 5 && M <= 8 && K % 2048 != 0 &&
         mfma_slots8_plan(M, N, K, cus, lds_limit, p))
         return true;
     // 3-4 tokens: the 4x4x4-MFMA split-K kernel wherever its lane layout fits the row.
@@ -492,10 +496,14 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
         if (!moe && L == 16 && (cpr / 8) % 3 == 0 &&
             try_plan(valu(1, 8, 3, 1, false), 4, M, N, K, topk, cus, lds_limit, p))
             return true;
-        // 8 lanes x 3 chunks per item (rows of 72 chunks, K = 2304). Dense: 6 work-groups per
-        // CU (163840 x 2304: 31.1 us against 32.1 us with 2, same box).
+        // Rows of 72 chunks (K = 2304). Dense: 8 lanes x one chunk per item x 2 row steps, 6
+        // work-groups per CU (163840 x 2304, same-box sweep: 30.95 us against 32.7 for 3 chunks
+        // per item and one row step). Grouped experts: 8 lanes x 3 chunks per item.
+        if (!moe && L == 8 && (cpr / 8) % 3 == 0 &&
+            try_plan(valu(1, 8, 1, 2, false), 6, M, N, K, topk, cus, lds_limit, p))
+            return true;
         if (L == 8 && (cpr / 8) % 3 == 0 &&
-            try_plan(valu(1, 8, 3, 1, moe), moe ? 8 : 6, M, N, K, topk, cus, lds_limit, p))
+            try_plan(valu(1, 8, 3, 1, moe), 8, M, N, K, topk, cus, lds_limit, p))
             return true;
         if (L == 8 && try_plan(valu(1, 8, 1, 2, moe), 6, M, N, K, topk, cus, lds_limit, p))
             return true;
@@ -637,7 +645,7 @@ bool make_moe_batched_plan_of(int kind, int M, int64_t N, int64_t K, int topk, i
     p->threads = 512;
     if (!plan_instantiated(*p))
         return false;
-    // Region A (activations, or the grouping scratch before them) + chunk offsets + the
+    // Region A (activations, or the grouping scratch before them) + chunk factors + the
     // virtual-entry tables.
     const int64_t xs_bytes = (int64_t)M * K * 2;
     const int64_t scratch = ((20 * P + 15) / 16) * 16;

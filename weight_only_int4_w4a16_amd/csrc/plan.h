@@ -54,7 +54,7 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
 // Split-K VALU kernels (dense calls): X(tokens, lanes per row, chunks per lane, row steps).
 #ifndef W4A16_SPLITK_CONFIGS
 #define W4A16_SPLITK_CONFIGS(X)                                                              \
-    X(1, 64, 1, 4) X(1, 32, 1, 2) X(1, 64, 2, 4) X(1, 64, 4, 2)                               \
+    X(1, 64, 1, 4) X(1, 32, 1, 2) X(1, 32, 1, 4) X(1, 64, 2, 4) X(1, 64, 4, 2)               \
     X(2, 64, 1, 4) X(3, 64, 1, 4) X(4, 64, 1, 4)
 #endif
 
