@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle
+import par_oracle
 import synthetic
 import weight_only_int4_w4a16_amd as w
 from devhelp import host
@@ -88,14 +89,30 @@ def test_moe_batched_invalid_and_repeated_ids():
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
 def test_moe_batched_full_size(M):
-    """256 experts of 2048 x 2304 (the fused gate+up experts), top-8 per token; 256 sampled
-    rows of every (token, slot) output checked against the oracle."""
+    """256 experts of 2048 x 2304 (the fused gate+up experts), top-8 per token; every element
+    of every (token, slot) output checked against the oracle."""
     qw, sc, ids, X = operands(256, 2048, 2304, M, 8, 4)
     print(f"moe_batched full M={M} unique experts={len(np.unique(ids))}", flush=True)
     got = run(qw, sc, ids, X)
-    rows = np.sort(np.random.default_rng(M).choice(2048, 256, replace=False))
-    ref, mag = oracle.moe_gemv_batched(qw, sc, ids, X, 2304, rows=rows)
-    check(got[:, :, rows], ref, mag, f"moe_batched full M{M} (256 sampled rows)")
+    ref, mag = par_oracle.moe_gemv_batched(qw, sc, ids, X, 2304, np.arange(2048))
+    check(got, ref, mag, f"moe_batched full M{M} (all rows)")
+
+
+@pytest.mark.parametrize("E,N,K,M,form", [(256, 2048, 2304, 2, "moe_batched_mfma4x4x4"),
+                                          (256, 2048, 2304, 16, "moe_batched_mfma4x4x4"),
+                                          (40, 64, 384, 5, "moe_batched tokens_per_pass")])
+def test_moe_batched_reads_only_selected_experts(E, N, K, M, form):
+    """Every expert no token selected has NaN scales; any read of them would poison the
+    output (the 4x4x4 grouped form and the VALU form)."""
+    assert w.describe_moe_batched_plan(M, N, K, 8).startswith(form)
+    qw, sc, ids, X = operands(E, N, K, M, 8, 6)
+    poisoned = np.full_like(sc, 0x7E00)
+    used = np.unique(ids)
+    poisoned[used] = sc[used]
+    got = run(qw, poisoned, ids, X)
+    assert np.all(np.isfinite(got))
+    ref, mag = par_oracle.moe_gemv_batched(qw, sc, ids, X, K, np.arange(N))
+    check(got, ref, mag, f"moe_batched M{M} {form} poisoned unselected experts")
 
 
 def test_moe_batched_deterministic_and_no_allocation():

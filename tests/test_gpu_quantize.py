@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import par_oracle
 import weight_only_int4_w4a16_amd as w
 from devhelp import host
 
@@ -117,6 +118,5 @@ def test_quantize_full_size_gate_up():
     bits |= (rng.integers(0, 2, size=(N, K), dtype=np.uint16) << 15)
     print(f"quantize full N={N} K={K}", flush=True)
     qw, sc = run(bits, K)
-    rows = np.random.default_rng(12).choice(N, 512, replace=False)
-    rq, rs = oracle.quantize_pack(bits[rows], K)
-    assert np.array_equal(sc[rows], rs) and np.array_equal(qw[rows], rq)
+    rq, rs = par_oracle.quantize_pack(bits, K, np.arange(N))
+    assert np.array_equal(sc, rs) and np.array_equal(qw, rq)

@@ -186,3 +186,37 @@ def test_tail_deterministic_and_no_allocation():
     torch.cuda.synchronize()
     assert torch.cuda.memory_allocated() == before
     assert torch.equal(h1.view(torch.int16), h2.view(torch.int16)) and torch.equal(o1, o2)
+
+
+def test_tail_reads_only_selected_experts_and_skips_invalid_slots():
+    """Every expert no slot selects has NaN scales, in both the gate+up and the down weights,
+    and expert 0 (the one an invalid slot's loads are pointed at) has infinite down scales; two
+    slots carry ids outside [0, E) with nonzero router weights. The SwiGLU rows of the invalid
+    slots are zero, everything else is finite, and the combine equals the oracle's, which skips
+    the invalid slots altogether."""
+    E, I, H, K, topk = 12, 256, 384, 2304, 6
+    d = synthetic.moe_tail(E, I, H, K, topk, 7, config_id=906)
+    ids = np.array([3, E, 5, -2, 3, 9], np.int32)
+    rw = np.array([0.3, 0.5, 0.2, 0.25, 0.1, 0.4], np.float32)
+    valid = np.unique(ids[(ids >= 0) & (ids < E)])
+    assert 0 not in valid
+    gs = np.full_like(d.gu_scales, 0x7E00)
+    gs[valid] = d.gu_scales[valid]
+    ds = np.full_like(d.down_scales, 0x7E00)
+    ds[valid] = d.down_scales[valid]
+    ds[0] = 0x7C00                                   # +inf
+    qg = torch.from_numpy(d.gu_qweight.view(np.int32)).cuda()
+    x = torch.from_numpy(d.x.view(np.int16)).cuda().view(torch.bfloat16)
+    tid = torch.from_numpy(ids).cuda()
+    h = w.moe_gemv_swiglu(qg, torch.from_numpy(gs.view(np.float16)).cuda(), tid, x)
+    r = oracle.moe_swiglu(d.gu_qweight, d.gu_scales, ids, d.x, K)
+    check_h(h, r, "swiglu poisoned unselected experts")
+    hb = host(h.view(torch.int16)).view(np.uint16)
+    assert np.all(hb[[1, 3]] == 0)
+    out = w.moe_down_combine(torch.from_numpy(d.down_qweight.view(np.int32)).cuda(),
+                             torch.from_numpy(ds.view(np.float16)).cuda(), tid,
+                             torch.from_numpy(rw).cuda(), h)
+    torch.cuda.synchronize()
+    ref, mag = oracle.moe_down_combine(d.down_qweight, d.down_scales, ids, rw, r["h_bf16"])
+    check_out(out, ref, mag, "combine, invalid slots over an infinite expert 0",
+              extra_rel=2.0 ** -7)
