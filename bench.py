@@ -2,21 +2,23 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
 
-Workload: the MLP-shaped GEMV pair at M = 1 (one decode token): a 28672 x 4096 fused gate+up
-projection followed by a 4096 x 14336 down projection, INT4 weights packed 8 per uint32 along K,
-one fp16 scale per 128-wide group, bf16 activations, fp32 outputs; seeded synthetic operands.
-One step runs both GEMVs. The weights of a step rotate through enough copies (12 x 91 MB) that
-the 256 MB memory-side cache cannot hold them, so every step streams its weights from HBM.
-The K timed steps are captured in one HIP graph, replayed once between two HIP events on the
-launch stream, with device synchronisation on both sides.
+Workload (the headline): the largest single-GPU configuration, a wide output-head GEMV at M = 1
+(one decode token), N = 163840 rows by K = 2304, INT4 weights packed 8 per uint32 along K, one
+fp16 scale per 128-wide group, bf16 activations, fp32 output; seeded synthetic operands. One
+step is one call. The weights rotate through enough copies (6 x 195 MB) that the 256 MB
+memory-side cache cannot hold them, so every call streams its weights from HBM. The K timed
+steps are captured in one HIP graph, replayed once between two HIP events on the launch stream,
+with device synchronisation on both sides.
 
-Prints one JSON line. `value` is algorithmic bytes (packed weights + fp16 scales + bf16
-activations) per second over the whole step, in GB/s. `roofline` is for the dominant kernel
-(the 28672 x 4096 GEMV): the same bytes over its own average duration, timed the same way on a
-graph of back-to-back launches; `roofline.launch_floor_us` is the per-launch time of a kernel
-that reads 16 bytes, timed the same way (the part of every call that is not memory time).
-`cpu_baseline` is the CPU oracle (single thread, float64) timed
-on whole steps of the same workload.
+Prints one JSON line (last on stdout). `value` is algorithmic bytes (packed weights + fp16
+scales + bf16 activations) per second, in GB/s. `roofline` is for the headline kernel: the same
+bytes over its own average launch duration, timed on a graph of back-to-back launches, against
+8 TB/s, with the plain streaming read of the same bytes as the practical ceiling and the
+per-launch time of a kernel that reads 16 bytes (`launch_floor_us`). `config.mlp_pair` is the
+MLP-shaped pair at M = 1 (28672 x 4096 gate+up then 4096 x 14336 down). `per_workload` holds,
+for every other configuration, [us per call, % of 8 TB/s, % of the streaming-read ceiling] (the
+legend is in `per_workload_fields`); the launch plans are printed to stderr. `cpu_baseline` is
+the CPU oracle (single thread, float64) timed on whole calls of the headline workload.
 """
 from __future__ import annotations
 
@@ -33,7 +35,8 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 GEMV achieved HBM GB/s (% of MI355X peak) and µs/call at M=1"
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_28672x4096.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_163840x2304.json")
+HEADLINE = "c5b"
 # The sources that define the GEMV kernels and their template instances (not the validation or
 # dispatch layers). A recorded traffic measurement stays valid while these and the launch plan
 # of the measured kernel (its describe_plan text) are unchanged.
@@ -165,25 +168,21 @@ def main():
                          args.steps)
         return
 
-    # ---- operands: seed 0 of the gate+up and down shapes, rotated copies on the device
-    da = synthetic.config("c3a", 0)
-    db = synthetic.config("c3b", 0)
-    qa, sa, xa = to_dev(da, dev, torch, np)
-    qb, sb, xb = to_dev(db, dev, torch, np)
-    bytes_a = synthetic.algorithmic_bytes(da.N, da.K)
-    bytes_b = synthetic.algorithmic_bytes(db.N, db.K)
-    step_weight_bytes = qa.numel() * 4 + sa.numel() * 2 + qb.numel() * 4 + sb.numel() * 2
-    R = max(2, -(-ROTATE_BYTES // step_weight_bytes))
-    copies = list(zip(rotated(torch, qa, R), rotated(torch, sa, R), rotated(torch, qb, R),
-                      rotated(torch, sb, R)))
-    ya = torch.empty(da.N, dtype=torch.float32, device=dev)
-    yb = torch.empty(db.N, dtype=torch.float32, device=dev)
-    xa1, xb1 = xa[0], xb[0]
+    cus = props.multi_processor_count
+
+    # ---- headline operands: seed 0 of the 163840 x 2304 head, rotated copies on the device
+    dh = synthetic.config(HEADLINE, 0)
+    qh, sh, xh = to_dev(dh, dev, torch, np)
+    bytes_h = synthetic.algorithmic_bytes(dh.N, dh.K)
+    R = max(2, -(-ROTATE_BYTES // (qh.numel() * 4 + sh.numel() * 2)))
+    hcopies = list(zip(rotated(torch, qh, R), rotated(torch, sh, R)))
+    del qh, sh
+    yh = torch.empty(dh.N, dtype=torch.float32, device=dev)
+    xh1 = xh[0]
 
     def step(i):
-        c = copies[i % R]
-        w.gemv(c[0], c[1], xa1, out=ya)
-        w.gemv(c[2], c[3], xb1, out=yb)
+        c = hcopies[i % R]
+        w.gemv(c[0], c[1], xh1, out=yh)
 
     for i in range(args.warmup):
         step(i)
@@ -192,25 +191,25 @@ def main():
     # ---- timed region: exactly K steps in one graph
     step_us, _ = graph_avg_us(torch, step, args.steps)
     ms_per_step = step_us / 1e3
-    value = (bytes_a + bytes_b) / (step_us * 1e-6) / 1e9
+    value = bytes_h / (step_us * 1e-6) / 1e9
 
-    # ---- dominant kernel alone (28672 x 4096), same rotation, same timing method
-    gate_us, _ = graph_avg_us(torch, lambda i: w.gemv(copies[i % R][0], copies[i % R][1], xa1,
-                                                       out=ya), args.steps)
-    down_us, _ = graph_avg_us(torch, lambda i: w.gemv(copies[i % R][2], copies[i % R][3], xb1,
-                                                       out=yb), args.steps)
+    # ---- the headline kernel alone: back-to-back launches on the same rotation (a step is one
+    # launch, so this repeats the measurement as the kernel's own average duration)
+    head_us, _ = graph_avg_us(torch, step, args.steps)
     # ---- launch floor: the same graph timing for back-to-back launches of a kernel that reads
-    # one 16-byte chunk (the streaming-read kernel, one work-group per CU). Every call above
-    # pays this per-launch cost of the command processor (dispatch, completion and the cache
-    # operations between dependent kernels) on top of its memory time.
+    # one 16-byte chunk (the streaming-read kernel, one work-group per CU). Every call pays this
+    # per-launch cost of the command processor (dispatch, completion and the cache operations
+    # between dependent kernels) on top of its memory time.
     fbuf = torch.zeros(16, dtype=torch.uint8, device=dev)
-    fout = torch.empty(4 * props.multi_processor_count, dtype=torch.int32, device=dev)
-    floor_us, _ = graph_avg_us(torch, lambda i: w.stream_read(
-        fbuf, 16, fout, props.multi_processor_count, 1), args.steps)
-    achieved = bytes_a / (gate_us * 1e-6) / 1e9
-    plan_a = w.describe_plan(1, da.N, da.K, 0, props.multi_processor_count)
-    digest = kernel_source_digest(plan_a)
-    traffic = traffic_for(digest, bytes_a)
+    fout = torch.empty(4 * cus, dtype=torch.int32, device=dev)
+    floor_us, _ = graph_avg_us(torch, lambda i: w.stream_read(fbuf, 16, fout, cus, 1), args.steps)
+    ceil_us = stream_ceiling_us(torch, w, dev, bytes_h, rotations(bytes_h), cus)[0]
+    achieved = bytes_h / (head_us * 1e-6) / 1e9
+    plan_h = w.describe_plan(1, dh.N, dh.K, 0, cus)
+    digest = kernel_source_digest(plan_h)
+    traffic = traffic_for(digest, bytes_h)
+    del hcopies
+    torch.cuda.empty_cache()
 
     out = {
         "metric": METRIC,
@@ -227,49 +226,81 @@ def main():
         "data": "synthetic (seeded int4 weights uniform in [-8,7], fp16 scales uniform in "
                 "[0.001,0.01], bf16 activations ~N(0,1))",
         "config": {
-            "workload": "MLP GEMV pair at M=1: 28672x4096 gate+up then 4096x14336 down, "
-                        "int4 weights (8 per uint32 along K), fp16 scale per 128-group, bf16 x",
+            "workload": "W4A16 GEMV at M=1, output head 163840x2304 (int4 weights 8 per uint32 "
+                        "along K, fp16 scale per 128-group, bf16 x, fp32 y)",
             "M": 1,
-            "shapes": [[da.N, da.K], [db.N, db.K]],
-            "bytes_per_step": bytes_a + bytes_b,
+            "shape": [dh.N, dh.K],
+            "bytes_per_call": bytes_h,
             "rotated_weight_copies": R,
+            "us_per_call": round(step_us, 3),
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-            "us_per_call": {"gate_up_28672x4096": round(gate_us, 3),
-                            "down_4096x14336": round(down_us, 3)},
-            "plans": {"gate_up": plan_a,
-                      "down": w.describe_plan(1, db.N, db.K, 0, props.multi_processor_count)},
-            "device": f"{props.name} {getattr(props, 'gcnArchName', '')} "
-                      f"{props.multi_processor_count} CUs",
+            "device": f"{props.name} {getattr(props, 'gcnArchName', '')} {cus} CUs",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "w4a16_gemv 28672x4096",
+            "kernel": "w4a16_gemv 163840x2304",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": bytes_a,
-            "avg_launch_us": round(gate_us, 3),
+            "algorithmic_bytes_per_launch": bytes_h,
+            "avg_launch_us": round(head_us, 3),
+            "stream_read_us_same_bytes": round(ceil_us, 3),
+            "frac_of_stream_read": round(ceil_us / head_us, 4),
             "launch_floor_us": round(floor_us, 3),
             "kernel_source_digest": digest,
         },
     }
+    plans = {"c5b_M1": plan_h}
+    out["config"]["mlp_pair"] = mlp_pair(torch, np, w, synthetic, dev, cus, args.steps, plans)
 
     if not args.no_configs:
-        out["per_workload"] = per_workload(torch, np, w, synthetic, dev,
-                                           props.multi_processor_count,
-                                           with_oracle=not args.no_cpu_baseline)
-        ref = out["per_workload"]["c3a_M1"]
-        if "stream_read_us" in ref:
-            # the plain streaming read of the same bytes, the practical ceiling of this kernel
-            out["roofline"]["stream_read_us_same_bytes"] = ref["stream_read_us"]
-            out["roofline"]["frac_of_stream_read"] = round(ref["stream_read_us"] / gate_us, 4)
+        out["per_workload_fields"] = ["us_per_call", "pct_of_hbm_peak", "pct_of_stream_read"]
+        out["per_workload"] = per_workload(torch, np, w, synthetic, dev, cus, plans)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(da, db, bytes_a + bytes_b, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(dh, bytes_h, args.cpu_seconds)
 
-    print(json.dumps(out), flush=True)
+    for k, v in plans.items():
+        print(f"plan {k}: {v}", file=sys.stderr, flush=True)
+    print(json.dumps(out, separators=(",", ":")), flush=True)
+
+
+def mlp_pair(torch, np, w, synthetic, dev, cus, steps, plans):
+    """The MLP-shaped GEMV pair at M = 1 (28672 x 4096 gate+up then 4096 x 14336 down), graph-
+    timed on rotated copies: µs per pair and per call, and % of 8 TB/s of the pair."""
+    da = synthetic.config("c3a", 0)
+    db = synthetic.config("c3b", 0)
+    qa, sa, xa = to_dev(da, dev, torch, np)
+    qb, sb, xb = to_dev(db, dev, torch, np)
+    ba = synthetic.algorithmic_bytes(da.N, da.K)
+    bb = synthetic.algorithmic_bytes(db.N, db.K)
+    wbytes = qa.numel() * 4 + sa.numel() * 2 + qb.numel() * 4 + sb.numel() * 2
+    R = max(2, -(-ROTATE_BYTES // wbytes))
+    cp = list(zip(rotated(torch, qa, R), rotated(torch, sa, R), rotated(torch, qb, R),
+                  rotated(torch, sb, R)))
+    del qa, sa, qb, sb
+    ya = torch.empty(da.N, dtype=torch.float32, device=dev)
+    yb = torch.empty(db.N, dtype=torch.float32, device=dev)
+
+    def pair(i):
+        c = cp[i % R]
+        w.gemv(c[0], c[1], xa[0], out=ya)
+        w.gemv(c[2], c[3], xb[0], out=yb)
+    pair(0)
+    pair_us, _ = graph_avg_us(torch, pair, steps)
+    a_us, _ = graph_avg_us(torch, lambda i: w.gemv(cp[i % R][0], cp[i % R][1], xa[0], out=ya),
+                           steps)
+    b_us, _ = graph_avg_us(torch, lambda i: w.gemv(cp[i % R][2], cp[i % R][3], xb[0], out=yb),
+                           steps)
+    plans["c3a_M1"] = w.describe_plan(1, da.N, da.K, 0, cus)
+    plans["c3b_M1"] = w.describe_plan(1, db.N, db.K, 0, cus)
+    del cp
+    torch.cuda.empty_cache()
+    return {"us_per_pair": round(pair_us, 3), "us_28672x4096": round(a_us, 3),
+            "us_4096x14336": round(b_us, 3),
+            "pct_of_hbm_peak": round(100 * (ba + bb) / pair_us / 1e3 / HBM_PEAK_GBS, 2)}
 
 
 def graph_replay_stats(torch, fn, n, reps):
@@ -352,31 +383,25 @@ def single_call_us(torch, call, reps=21):
     return sorted(times)[reps // 2]
 
 
-def per_workload(torch, np, w, synthetic, dev, cus, with_oracle=False):
-    """µs per call and GB/s for every workload shape (graph-timed, rotated copies), with the
-    same call on one cache-resident copy and the plain streaming-read ceiling over the same
-    number of bytes, rotated the same way."""
+def per_workload(torch, np, w, synthetic, dev, cus, plans):
+    """[µs per call, % of 8 TB/s, % of the streaming-read ceiling] for every other workload
+    (graph-timed median over 10 replays, rotated copies); the streaming read covers the same
+    number of bytes, rotated the same way (two reads, one per launch, for the expert tail; a
+    device-to-device copy of the same total bytes for quantise)."""
     res = {}
 
     def rot(nbytes):
         return max(2, -(-ROTATE_BYTES // nbytes))
 
-    def record(key, N, K, M, b, stats, warm, ceil, plan):
-        med, p10, p90 = stats
-        e = {"N": N, "K": K, "M": M, "plan": plan, "us_per_call": round(med, 3),
-             "us_p10": round(p10, 3), "us_p90": round(p90, 3),
-             "GB_s": round(b / med / 1e3, 1),
-             "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1),
-             "us_cache_warm_same_copy": round(warm, 3)}
-        if ceil is not None:
-            e["stream_read_us"] = round(ceil[0], 3)
-            e["stream_read_launch"] = {"blocks": ceil[1], "unroll": ceil[2]}
-            e["pct_of_stream_read"] = round(100 * ceil[0] / med, 1)
-        res[key] = e
+    def record(key, b, med, ceil_us):
+        res[key] = [round(med, 2), round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1),
+                    round(100 * ceil_us / med, 1)]
 
     ceilings = {}
     for name in ("c1", "c2", "c3a", "c3b", "c5a", "c5b"):
         for M in ((1, 2, 4, 8, 16) if name in ("c5a", "c5b") else (1,)):
+            if name in ("c3a", "c3b", "c5b") and M == 1:
+                continue            # the headline and the MLP pair are timed above
             d = synthetic.config(name, 0, M=M)
             qw, sc, x = to_dev(d, dev, torch, np)
             R = rot(qw.numel() * 4 + sc.numel() * 2)
@@ -390,22 +415,14 @@ def per_workload(torch, np, w, synthetic, dev, cus, with_oracle=False):
                 def fn(i, cp=cp, x=x, y=y, R=R):
                     w.gemv_batched(cp[i % R][0], cp[i % R][1], x, out=y)
             fn(0)
-            n = max(2 * R, 64)
-            stats = graph_replay_stats(torch, fn, n, 10)
-            warm, _, _ = graph_replay_stats(torch, lambda i: fn(0), 64, 5)
-            single = single_call_us(torch, lambda: fn(0))
+            med, _, _ = graph_replay_stats(torch, fn, max(2 * R, 64), 10)
             b = synthetic.algorithmic_bytes(d.N, d.K, M)
             del cp
             torch.cuda.empty_cache()
             if b not in ceilings:
-                ceilings[b] = stream_ceiling_us(torch, w, dev, b, rot(b), cus)
-            record(f"{name}_M{M}", d.N, d.K, M, b, stats, warm, ceilings[b],
-                   w.describe_plan(M, d.N, d.K, 0, cus))
-            res[f"{name}_M{M}"]["us_single_call_not_graphed"] = round(single, 3)
-            if with_oracle:
-                ous = oracle_us(d, M, rows=512)
-                res[f"{name}_M{M}"]["oracle_us_1_core"] = round(ous, 1)
-                res[f"{name}_M{M}"]["oracle_GB_s"] = round(b / ous / 1e3, 4)
+                ceilings[b] = stream_ceiling_us(torch, w, dev, b, rot(b), cus)[0]
+            record(f"{name}_M{M}", b, med, ceilings[b])
+            plans[f"{name}_M{M}"] = w.describe_plan(M, d.N, d.K, 0, cus)
     m = synthetic.config("c4", 0)
     qw = torch.from_numpy(m.qweight.view(np.int32)).to(dev)
     sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
@@ -420,20 +437,22 @@ def per_workload(torch, np, w, synthetic, dev, cus, with_oracle=False):
     def fn(i):
         w.moe_gemv(cp[i % 2][0], cp[i % 2][1], idsets[i % 64], x, out=y)
     fn(0)
-    stats = graph_replay_stats(torch, fn, 128, 10)
-    warm, _, _ = graph_replay_stats(torch, lambda i: w.moe_gemv(cp[0][0], cp[0][1], idsets[0], x,
-                                                                out=y), 64, 5)
+    med, _, _ = graph_replay_stats(torch, fn, 128, 10)
     b = m.topk * (m.N * m.K // 2 + m.N * (m.K // 128) * 2) + m.K * 2
     del cp
     torch.cuda.empty_cache()
-    record("c4_moe_top8_of_256", m.N, m.K, 1, b, stats, warm,
-           stream_ceiling_us(torch, w, dev, b, rot(b), cus),
-           w.describe_plan(1, m.N, m.K, m.topk, cus))
+    record("c4_moe_top8_of_256", b, med, stream_ceiling_us(torch, w, dev, b, rot(b), cus)[0])
+    plans["c4_moe_top8_of_256"] = w.describe_plan(1, m.N, m.K, m.topk, cus)
     del m, x, y, idsets
     torch.cuda.empty_cache()
-    res["c4_expert_tail_top8_of_256"] = expert_tail(torch, np, w, synthetic, dev, cus)
-    res["quantize_pack_28672x4096"] = quantize_rate(torch, np, w, dev)
-    res.update(moe_batched(torch, np, w, synthetic, dev, cus))
+    for k, (b, med, ceil_us, plan) in expert_tail(torch, np, w, synthetic, dev, cus).items():
+        record(k, b, med, ceil_us)
+        plans[k] = plan
+    for k, (b, med, ceil_us, plan) in moe_batched(torch, np, w, synthetic, dev, cus).items():
+        record(k, b, med, ceil_us)
+        plans[k] = plan
+    b, med, copy_us = quantize_rate(torch, np, w, dev)
+    record("quantize_pack_28672x4096", b, med, copy_us)
     return res
 
 
@@ -464,13 +483,9 @@ def moe_batched(torch, np, w, synthetic, dev, cus):
         med, p10, p90 = graph_replay_stats(torch, fn, 128, 10)
         b = uniq * per_expert + M * m.K * 2
         ceil = stream_ceiling_us(torch, w, dev, int(b), rotations(int(b)), cus)
-        out[f"c4_moe_batched_M{M}"] = {
-            "experts": m.E, "topk": m.topk, "N": m.N, "K": m.K, "M": M,
-            "mean_unique_experts": round(uniq, 2),
-            "plan": w.describe_moe_batched_plan(M, m.N, m.K, m.topk, cus),
-            "us_per_call": round(med, 3), "us_p10": round(p10, 3), "us_p90": round(p90, 3),
-            "GB_s": round(b / med / 1e3, 1), "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1),
-            "stream_read_us": round(ceil[0], 3), "pct_of_stream_read": round(100 * ceil[0] / med, 1)}
+        out[f"c4_moe_batched_M{M}"] = (
+            b, med, ceil[0], w.describe_moe_batched_plan(M, m.N, m.K, m.topk, cus) +
+            f" mean_unique_experts={uniq:.2f}")
     del cp
     torch.cuda.empty_cache()
     return out
@@ -494,11 +509,7 @@ def quantize_rate(torch, np, w, dev):
     del copies
     torch.cuda.empty_cache()
     copy_us = copy_ceiling_us(torch, dev, b)
-    return {"N": N, "K": K, "bytes": b, "us_per_call": round(med, 3), "us_p10": round(p10, 3),
-            "us_p90": round(p90, 3), "GB_s": round(b / med / 1e3, 1),
-            "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1),
-            "copy_us_same_bytes": round(copy_us, 3),
-            "pct_of_copy": round(100 * copy_us / med, 1)}
+    return b, med, copy_us
 
 
 def tail_bytes(d):
@@ -549,18 +560,11 @@ def expert_tail(torch, np, w, synthetic, dev, cus):
     b_gu = d.topk * (2 * d.I * d.K // 2 + 2 * d.I * (d.K // 128) * 2) + d.K * 2
     ceil_us = (stream_ceiling_us(torch, w, dev, b_gu, rotations(b_gu), cus)[0] +
                stream_ceiling_us(torch, w, dev, b - b_gu, rotations(b - b_gu), cus)[0])
-    e = {"experts": d.E, "topk": d.topk, "gate_up": [2 * d.I, d.K], "down": [d.H, d.I],
-         "plans": {"swiglu": w.describe_tail_plan(0, 0, d.K, d.I, d.topk, cus),
-                   "down_combine": w.describe_tail_plan(1, d.H, 0, d.I, d.topk, cus)},
-         "bytes": b, "us_per_call": round(med, 3), "us_p10": round(p10, 3),
-         "us_p90": round(p90, 3), "us_swiglu": round(g_us, 3), "us_down_combine": round(d_us, 3),
-         "GB_s": round(b / med / 1e3, 1),
-         "pct_of_peak": round(100 * b / med / 1e3 / HBM_PEAK_GBS, 1),
-         "stream_read_us_two_launches": round(ceil_us, 3),
-         "pct_of_stream_read": round(100 * ceil_us / med, 1)}
+    plan = (f"swiglu: {w.describe_tail_plan(0, 0, d.K, d.I, d.topk, cus)}; down_combine: "
+            f"{w.describe_tail_plan(1, d.H, 0, d.I, d.topk, cus)}; us {g_us:.2f} + {d_us:.2f}")
     del cp
     torch.cuda.empty_cache()
-    return e
+    return {"c4_expert_tail_top8_of_256": (b, med, ceil_us, plan)}
 
 
 def profile_workload(torch, np, w, synthetic, dev, name, M, steps):
@@ -607,23 +611,22 @@ def profile_workload(torch, np, w, synthetic, dev, name, M, steps):
     print(json.dumps({"profile_workload": name, "M": M, "launches": steps, "plan": plan}))
 
 
-def cpu_baseline(da, db, bytes_per_step, target_s):
-    """The CPU oracle (one thread, float64) on whole steps of the same workload."""
+def cpu_baseline(d, bytes_per_call, target_s):
+    """The CPU oracle (one thread, float64) on whole calls of the headline workload."""
     import oracle
     orc = oracle.default()
-    steps, t0 = 0, time.perf_counter()
+    calls, t0 = 0, time.perf_counter()
     while True:
-        orc.gemv(da.qweight, da.scales, da.x[0], da.K)
-        orc.gemv(db.qweight, db.scales, db.x[0], db.K)
-        steps += 1
+        orc.gemv(d.qweight, d.scales, d.x[0], d.K)
+        calls += 1
         el = time.perf_counter() - t0
-        if el >= target_s or steps >= 8:
+        if el >= target_s or calls >= 16:
             break
-    return {"value": round(bytes_per_step * steps / el / 1e9, 4), "unit": "GB/s",
+    return {"value": round(bytes_per_call * calls / el / 1e9, 4), "unit": "GB/s",
             "cores": 1, "kind": "oracle",
-            "sample": f"{steps} whole steps (28672x4096 + 4096x14336 GEMV, every row), "
-                      f"{el:.1f} s, single-threaded C oracle in float64",
-            "ms_per_step": round(el / steps * 1e3, 1),
+            "sample": f"{calls} whole calls of the {d.N}x{d.K} GEMV (every row), {el:.1f} s, "
+                      f"single-threaded C oracle in float64",
+            "ms_per_call": round(el / calls * 1e3, 1),
             "host": host_description()}
 
 
@@ -643,20 +646,6 @@ def host_description():
     except (AttributeError, OSError):
         avail = os.cpu_count()
     return {"cpu": model, "cores_available": avail}
-
-
-def oracle_us(d, M, rows):
-    """µs of the CPU oracle for one call of workload d, timed on a row sample and scaled."""
-    import numpy as np
-    import oracle
-    orc = oracle.default()
-    sample = np.arange(0, d.N, max(1, d.N // rows))
-    t0 = time.perf_counter()
-    if M == 1:
-        orc.gemv(d.qweight, d.scales, d.x[0], d.K, rows=sample)
-    else:
-        orc.gemv_batched(d.qweight, d.scales, d.x, d.K, rows=sample)
-    return (time.perf_counter() - t0) * 1e6 * d.N / sample.size
 
 
 if __name__ == "__main__":

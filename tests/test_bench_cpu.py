@@ -16,10 +16,10 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def test_traffic_record_is_consistent():
     """The committed HBM-traffic record: fetched + written bytes per launch, its ratio to the
-    algorithmic bytes of the 28672 x 4096 GEMV, and the copy-kernel scale factors."""
-    with open(os.path.join(ROOT, "profiles", "traffic_gemv_28672x4096.json")) as f:
+    algorithmic bytes of the 163840 x 2304 GEMV, and the copy-kernel scale factors."""
+    with open(os.path.join(ROOT, "profiles", "traffic_gemv_163840x2304.json")) as f:
         t = json.load(f)
-    assert t["algorithmic_bytes_per_launch"] == 28672 * 4096 // 2 + 28672 * 32 * 2 + 4096 * 2
+    assert t["algorithmic_bytes_per_launch"] == 163840 * 2304 // 2 + 163840 * 18 * 2 + 2304 * 2
     fetched = t["fetch_size_kib_per_dispatch"] * 1024 * t["fetch_scale"]
     written = t["write_size_kib_per_dispatch"] * 1024 * t["write_scale"]
     assert abs(fetched + written - t["bytes_per_launch"]) <= 2
