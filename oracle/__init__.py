@@ -96,6 +96,8 @@ class Oracle:
                                           P, P, P, P, P, P]
         lib.oracle_moe_down_combine.argtypes = [P, P, P, P, i32, i32, P, i64, i64, i32, P, i64,
                                                 P, P]
+        lib.oracle_unpack3.argtypes = [P, P, i64, i64]
+        lib.oracle_moe_gemv3.argtypes = [P, P, P, i32, i32, P, i64, i64, i32, P, i64, P, P]
         lib.oracle_float_to_f16_sat.argtypes = [ctypes.c_float]
         lib.oracle_float_to_f16_sat.restype = ctypes.c_uint16
         lib.oracle_quantize_pack.argtypes = [P, i64, i64, i64, i32, P, P]
@@ -229,6 +231,29 @@ class Oracle:
             raise ValueError("oracle_moe_gemv_batched: bad arguments")
         return Y, mag
 
+    def unpack3(self, qweight3, K: int) -> np.ndarray:
+        """Signed three-bit codes int8 [N][K] of qweight3 uint32 [N][3K/32]."""
+        qw = _c(qweight3, np.uint32)
+        N = qw.shape[0] if qw.ndim == 2 else 1
+        out = np.empty((N, K), np.int8)
+        if self.lib.oracle_unpack3(_ptr(qw), _ptr(out), N, K):
+            raise ValueError("oracle_unpack3: bad arguments")
+        return out
+
+    def moe_gemv3(self, qweight3, scales, ids, x, K: int, group: int = 128,
+                  rows: Optional[Sequence[int]] = None,
+                  num_experts: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """(y, mag) float64 [topk][rows] for three-bit experts qweight3 [E][N][3K/32]."""
+        qw, sc = _c(qweight3, np.uint32), _c(scales, np.uint16)
+        ii, xx = _c(ids, np.int32).reshape(-1), _c(x, np.uint16).reshape(-1)
+        E, N = _experts(qw, num_experts), qw.shape[1]
+        r, nr = _rows(rows, N)
+        y, mag = np.empty((ii.size, nr)), np.empty((ii.size, nr))
+        if self.lib.oracle_moe_gemv3(_ptr(qw), _ptr(sc), _ptr(ii), ii.size, E, _ptr(xx), N, K,
+                                     group, _ptr(r), nr, _ptr(y), _ptr(mag)):
+            raise ValueError("oracle_moe_gemv3: bad arguments")
+        return y, mag
+
     def float_to_f16_sat(self, v: float) -> int:
         return int(self.lib.oracle_float_to_f16_sat(float(v)))
 
@@ -300,6 +325,14 @@ def moe_down_combine(*a, **kw):
 
 def moe_gemv_batched(*a, **kw):
     return default().moe_gemv_batched(*a, **kw)
+
+
+def unpack3(qweight3, K):
+    return default().unpack3(qweight3, K)
+
+
+def moe_gemv3(*a, **kw):
+    return default().moe_gemv3(*a, **kw)
 
 
 def quantize_pack(*a, **kw):

@@ -430,3 +430,98 @@ int oracle_moe_gemv_batched(const uint32_t *qweight, const uint16_t *scales, con
         }
     return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Three-bit expert weights. The local-kimi README's hardware section says that fitting a
+ * 24 GB card needs the expert weights near three bits and that the work is under way; the
+ * pages define no format. The reading taken here keeps everything of the INT4 format except
+ * the code width:
+ *   - a code is a 3-bit two's-complement integer q in [-4, 3] (no zero point), scaled by the
+ *     same fp16 scale per G-wide K group;
+ *   - a row of K values is K/32 blocks of three uint32 words (12 bytes, 32 codes); in block b,
+ *     code c (value k = 32 b + c) sits
+ *       c = 10 t + j,     t in {0,1,2}, j in 0..4:  bits [3j, 3j+2]       of word t,
+ *       c = 10 t + 5 + j, t in {0,1,2}, j in 0..4:  bits [16+3j, 16+3j+2] of word t,
+ *       c = 30:  its bit i is bit 15 of word i,  i = 0, 1, 2,
+ *       c = 31:  its bit i is bit 31 of word i;
+ *   - qweight3 uint32[E][N][3K/32] (experts, then rows, then blocks), scales fp16 [E][N][K/G].
+ * 3 bits per weight plus 16 bits per group: 0.390625 bytes per weight at G = 128.
+ * ---------------------------------------------------------------------------------------- */
+
+/* Code c (0..31) of one 3-word block, as a signed integer. */
+static int code3_of_block(const uint32_t *blk, int c)
+{
+    unsigned u;
+    if (c < 30) {
+        int t = c / 10, r = c % 10;
+        int shift = r < 5 ? 3 * r : 16 + 3 * (r - 5);
+        u = (blk[t] >> shift) & 7u;
+    } else {
+        int bit = c == 30 ? 15 : 31;
+        u = ((blk[0] >> bit) & 1u) | (((blk[1] >> bit) & 1u) << 1) | (((blk[2] >> bit) & 1u) << 2);
+    }
+    return u >= 4 ? (int)u - 8 : (int)u;
+}
+
+/* Signed codes of N rows of K values: q_out int8[N][K]. */
+int oracle_unpack3(const uint32_t *qweight3, int8_t *q_out, int64_t N, int64_t K)
+{
+    if (!qweight3 || !q_out || N < 1 || K < 32 || K % 32)
+        return ORACLE_BAD_ARG;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            q_out[n * K + k] = (int8_t)code3_of_block(qweight3 + n * (3 * K / 32) + 3 * (k / 32),
+                                                     (int)(k % 32));
+    return ORACLE_OK;
+}
+
+static void dot_row3(const uint32_t *row, const uint16_t *srow, const uint16_t *x, int64_t K,
+                     int32_t G, double *y, double *mag)
+{
+    double acc = 0.0, m = 0.0;
+    for (int64_t g = 0; g < K / G; ++g) {
+        double s = oracle_f16_to_double(srow[g]);
+        for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+            double w = (double)code3_of_block(row + 3 * (k / 32), (int)(k % 32)) * s;
+            double p = w * oracle_bf16_to_double(x[k]);
+            acc += p;
+            m += fabs(p);
+        }
+    }
+    *y = acc;
+    *mag = m;
+}
+
+/*
+ * Grouped-expert product over three-bit experts: y[t][r] = sum_k q3_e[n,k] s_e[n,k/G] x[k],
+ * e = ids[t], n = rows[r]. An id outside [0, E) gives a zero row (with mag zero).
+ */
+int oracle_moe_gemv3(const uint32_t *qweight3, const uint16_t *scales, const int32_t *ids,
+                     int32_t topk, int32_t E, const uint16_t *x, int64_t N, int64_t K,
+                     int32_t G, const int64_t *rows, int64_t n_rows, double *y, double *mag)
+{
+    if (!qweight3 || !scales || !ids || !x || !y || !mag)
+        return ORACLE_BAD_ARG;
+    if (topk < 1 || E < 1 || N < 1 || K < 32 || K % 32 || G < 32 || G % 32 || K % G ||
+        n_rows < 0 || (!rows && n_rows != N))
+        return ORACLE_BAD_ARG;
+    if (rows)
+        for (int64_t r = 0; r < n_rows; ++r)
+            if (rows[r] < 0 || rows[r] >= N)
+                return ORACLE_BAD_ARG;
+    for (int32_t t = 0; t < topk; ++t) {
+        int32_t e = ids[t];
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t n = rows ? rows[r] : r;
+            double *yo = &y[(int64_t)t * n_rows + r], *mo = &mag[(int64_t)t * n_rows + r];
+            if (e < 0 || e >= E) {
+                *yo = 0.0;
+                *mo = 0.0;
+                continue;
+            }
+            int64_t row = (int64_t)e * N + n;
+            dot_row3(qweight3 + row * (3 * K / 32), scales + row * (K / G), x, K, G, yo, mo);
+        }
+    }
+    return ORACLE_OK;
+}

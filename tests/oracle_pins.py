@@ -591,11 +591,86 @@ def pin_expert_id_upper_bound(orc):
     assert not np.array_equal(oall, out)
 
 
+# ---------------------------------------------------------------- three-bit experts
+def pack3(q):
+    """Independent packer for the three-bit layout, written from its statement: codes [N][K]
+    in [-4, 3] to uint32 [N][3K/32]. Block b of a row holds codes 32b..32b+31; code c = 10t + j
+    (j < 5) at bits 3j of word t, c = 10t + 5 + j at bits 16 + 3j, and bit i of codes 30 and 31
+    at bits 15 and 31 of word i."""
+    q = np.asarray(q, dtype=np.int64)
+    N, K = q.shape
+    f = (q & 7).astype(np.uint64).reshape(N, K // 32, 32)
+    words = np.zeros((N, K // 32, 3), np.uint64)
+    for t in range(3):
+        for j in range(5):
+            words[:, :, t] |= f[:, :, 10 * t + j] << np.uint64(3 * j)
+            words[:, :, t] |= f[:, :, 10 * t + 5 + j] << np.uint64(16 + 3 * j)
+        words[:, :, t] |= ((f[:, :, 30] >> np.uint64(t)) & np.uint64(1)) << np.uint64(15)
+        words[:, :, t] |= ((f[:, :, 31] >> np.uint64(t)) & np.uint64(1)) << np.uint64(31)
+    return words.reshape(N, 3 * K // 32).astype(np.uint32)
+
+
+def pin_w5_three_bit_golden(orc):
+    """The hand-derived block of tests/golden/w5_three_bit_layout.json: unit probes return the
+    codes written there, all ones gives their sum."""
+    g = json.load(open(os.path.join(GOLDEN, "w5_three_bit_layout.json")))
+    words = np.array(g["words"], np.uint32).reshape(1, 1, 12)
+    sc = np.array([[[g["scale_bits"]]]], np.uint16)
+    ids = np.array([0], np.int32)
+    for k, want in g["probes"].items():
+        x = np.zeros(128, np.uint16)
+        x[int(k)] = 0x3F80
+        y, _ = orc.moe_gemv3(words, sc, ids, x, 128)
+        assert y[0, 0] == want, (k, y[0, 0], want)
+    y, _ = orc.moe_gemv3(words, sc, ids, np.full(128, 0x3F80, np.uint16), 128)
+    assert y[0, 0] == g["all_ones"]
+
+
+def pin_three_bit_unpack_roundtrip(orc):
+    """Random codes packed by the independent packer come back from the oracle's decoder;
+    every code value at every position of a block."""
+    rng = np.random.default_rng(71)
+    q = rng.integers(-4, 4, size=(7, 256))
+    assert np.array_equal(orc.unpack3(pack3(q), 256).astype(np.int64), q)
+    q = np.array([[(c + p) % 8 - 4 for p in range(32)] for c in range(8)])
+    assert np.array_equal(orc.unpack3(pack3(q), 32).astype(np.int64), q)
+
+
+def pin_three_bit_brute_force(orc):
+    """Grouped three-bit product against numpy: dense dequantised weights times x in float64,
+    invalid ids (including E and E + 1 with spare experts in memory) give zeros, unit probes
+    return q * s exactly."""
+    E, held, N, K = 3, 5, 6, 384
+    rng = np.random.default_rng(72)
+    q = rng.integers(-4, 4, size=(held, N, K))
+    words = np.stack([pack3(q[e]) for e in range(held)])
+    sc = rng.uniform(0.001, 0.01, size=(held, N, K // 128)).astype(np.float16).view(np.uint16)
+    x = (rng.standard_normal(K).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ids = np.array([2, E, 0, -1, E + 1, 2], np.int32)
+    y, mag = orc.moe_gemv3(words, sc, ids, x, K, num_experts=E)
+    xv = bf16_bits_to_f64(x)
+    for t, e in enumerate(ids):
+        if not 0 <= e < E:
+            assert np.all(y[t] == 0) and np.all(mag[t] == 0)
+            continue
+        W = q[e] * np.repeat(sc[e].view(np.float16).astype(np.float64), 128, axis=1)
+        assert np.allclose(y[t], W @ xv, rtol=1e-12, atol=1e-14)
+        assert np.allclose(mag[t], np.abs(W * xv).sum(1), rtol=1e-12)
+    for k in (0, 9, 10, 15, 29, 30, 31, 32, 200, 383):
+        e1 = np.zeros(K, np.uint16)
+        e1[k] = 0x3F80
+        yk, _ = orc.moe_gemv3(words, sc, np.array([1], np.int32), e1, K, num_experts=E)
+        assert np.array_equal(yk[0], q[1][:, k] * sc[1][:, k // 128].view(np.float16).astype(np.float64))
+    ys, ms = orc.moe_gemv3(words, sc, ids, x, K, rows=[5, 0], num_experts=E)
+    assert np.array_equal(ys, y[:, [5, 0]]) and np.array_equal(ms, mag[:, [5, 0]])
+
+
 ALL_PINS = [
     pin_f16_decode, pin_bf16_decode, pin_w1, pin_w2, pin_unpack, pin_unit_probes,
     pin_zero_scale_groups, pin_linearity, pin_negation, pin_constant_rows, pin_brute_force,
     pin_mag_nonnegative, pin_batched, pin_moe, pin_row_subset, pin_bf16_round_brute,
     pin_bf16_round_ties, pin_silu, pin_swiglu_golden, pin_swiglu_brute, pin_down_combine,
     pin_quantize_golden, pin_quantize_brute, pin_quantize_gemv_roundtrip, pin_moe_batched,
-    pin_expert_id_upper_bound,
+    pin_expert_id_upper_bound, pin_w5_three_bit_golden, pin_three_bit_unpack_roundtrip,
+    pin_three_bit_brute_force,
 ]

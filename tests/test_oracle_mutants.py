@@ -63,6 +63,17 @@ MUTANTS = {
                                "            if (e < 0 || e > E)\n                continue;"),
     "moe_batched_id_upper_bound": ("                if (e < 0 || e >= E) {\n                    Y[o] = 0.0;",
                                    "                if (e < 0 || e > E) {\n                    Y[o] = 0.0;"),
+    "three_bit_high_half_shift": ("int shift = r < 5 ? 3 * r : 16 + 3 * (r - 5);",
+                                  "int shift = r < 5 ? 3 * r : 15 + 3 * (r - 5);"),
+    "three_bit_word_order": ("u = (blk[t] >> shift) & 7u;", "u = (blk[2 - t] >> shift) & 7u;"),
+    "three_bit_spare_bit_order": ("u = ((blk[0] >> bit) & 1u) | (((blk[1] >> bit) & 1u) << 1) | (((blk[2] >> bit) & 1u) << 2);",
+                                  "u = ((blk[2] >> bit) & 1u) | (((blk[1] >> bit) & 1u) << 1) | (((blk[0] >> bit) & 1u) << 2);"),
+    "three_bit_spare_codes_swapped": ("int bit = c == 30 ? 15 : 31;", "int bit = c == 30 ? 31 : 15;"),
+    "three_bit_offset_binary": ("return u >= 4 ? (int)u - 8 : (int)u;", "return (int)u - 4;"),
+    "three_bit_block_swap": ("double w = (double)code3_of_block(row + 3 * (k / 32), (int)(k % 32)) * s;",
+                             "double w = (double)code3_of_block(row + 3 * ((k / 32) ^ 1), (int)(k % 32)) * s;"),
+    "three_bit_id_upper_bound": ("            if (e < 0 || e >= E) {\n                *yo = 0.0;\n                *mo = 0.0;\n                continue;\n            }\n            int64_t row = (int64_t)e * N + n;\n            dot_row3",
+                                 "            if (e < 0 || e > E) {\n                *yo = 0.0;\n                *mo = 0.0;\n                continue;\n            }\n            int64_t row = (int64_t)e * N + n;\n            dot_row3"),
     "quant_f16_subnormal": ("if (qexp < -24)\n        qexp = -24;", "if (qexp < -30)\n        qexp = -30;"),
 }
 
