@@ -445,6 +445,9 @@ def per_workload(torch, np, w, synthetic, dev, cus, plans):
     plans["c4_moe_top8_of_256"] = w.describe_plan(1, m.N, m.K, m.topk, cus)
     del m, x, y, idsets
     torch.cuda.empty_cache()
+    b, med, ceil_us, plan = moe_three_bit(torch, np, w, synthetic, dev, cus)
+    record("c4_moe3_top8_of_256", b, med, ceil_us)
+    plans["c4_moe3_top8_of_256"] = plan
     for k, (b, med, ceil_us, plan) in expert_tail(torch, np, w, synthetic, dev, cus).items():
         record(k, b, med, ceil_us)
         plans[k] = plan
@@ -454,6 +457,32 @@ def per_workload(torch, np, w, synthetic, dev, cus, plans):
     b, med, copy_us = quantize_rate(torch, np, w, dev)
     record("quantize_pack_28672x4096", b, med, copy_us)
     return res
+
+
+def moe_three_bit(torch, np, w, synthetic, dev, cus):
+    """The c4 experts (256 of 2048 x 2304) as three-bit codes, one token, top-8 (64 id sets
+    rotated, two copies of the experts)."""
+    cid, N, K = synthetic.SHAPES["c4"]
+    m = synthetic.moe3(synthetic.MOE_EXPERTS, N, K, synthetic.MOE_TOPK, 0, config_id=cid)
+    qw = torch.from_numpy(m.qweight.view(np.int32)).to(dev)
+    sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
+    cp = list(zip(rotated(torch, qw, 2), rotated(torch, sc, 2)))
+    del qw, sc
+    x = torch.from_numpy(m.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    rng = np.random.default_rng([4, 3])
+    idsets = [torch.from_numpy(rng.choice(m.E, m.topk, replace=False).astype(np.int32)).to(dev)
+              for _ in range(64)]
+    y = torch.empty((m.topk, N), dtype=torch.float32, device=dev)
+
+    def fn(i):
+        w.moe_gemv3(cp[i % 2][0], cp[i % 2][1], idsets[i % 64], x, out=y)
+    fn(0)
+    med, _, _ = graph_replay_stats(torch, fn, 128, 10)
+    b = synthetic.algorithmic_bytes3(N, K, m.topk)
+    del cp
+    torch.cuda.empty_cache()
+    ceil_us = stream_ceiling_us(torch, w, dev, b, max(2, -(-ROTATE_BYTES // b)), cus)[0]
+    return b, med, ceil_us, w.describe_moe3_plan(N, K, m.topk, cus)
 
 
 def moe_batched(torch, np, w, synthetic, dev, cus):

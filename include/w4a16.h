@@ -174,6 +174,38 @@ w4a16_status_t w4a16_quantize_pack(const uint16_t *w, int64_t ldw, uint32_t *qwe
                                    hipStream_t stream);
 
 /*
+ * Grouped-expert GEMV over THREE-BIT expert weights, one token: y[t] = W3_{expert_ids[t]} x.
+ * The local-kimi README, hardware section, says a 24 GB card needs the expert weights near
+ * three bits and defines no format; this library reads the format as: a code is a 3-bit
+ * two's-complement integer q in [-4, 3] with one fp16 scale per 128-wide K group (as for
+ * INT4), and each row of K values is K/32 blocks of three uint32 words holding 32 codes. In
+ * block b, code c (k = 32 b + c) sits, for t < 3 and j < 5,
+ *     c = 10t + j      in bits [3j, 3j+2] of word t,
+ *     c = 10t + 5 + j  in bits [16+3j, 16+3j+2] of word t,
+ *     c = 30 / 31      with its bit i in bit 15 / bit 31 of word i (i = 0, 1, 2).
+ *   qweight3 uint32[E][N][3K/32] (4-byte aligned), scales fp16 bits [E][N][K/128],
+ *   expert_ids int32[topk] in DEVICE memory, x bf16 bits [K] (16-byte aligned),
+ *   y float[topk][N]. Only the listed experts are read; an id outside [0, E) gives a row of
+ *   +0.0f; 1 <= topk <= 1024, topk * N <= 2^31 - 1; K as for w4a16_gemv. Precision as stated
+ *   at the top of this file (codes enter as exact integers).
+ */
+w4a16_status_t w4a16_moe_gemv3(const uint32_t *qweight3, const uint16_t *scales,
+                               const int32_t *expert_ids, int32_t topk, int32_t num_experts,
+                               const uint16_t *x, float *y, int64_t N, int64_t K,
+                               int32_t group_size, hipStream_t stream);
+
+/*
+ * Test support for the three-bit format: q_out int8[N][K] receives every code, decoded with
+ * the GEMV's own decode steps. 1 <= N, 32 <= K, K % 32 == 0; qweight3 4-byte aligned.
+ */
+w4a16_status_t w4a16_unpack3_debug(const uint32_t *qweight3, int8_t *q_out, int64_t N,
+                                   int64_t K, hipStream_t stream);
+
+/* Launch plan of w4a16_moe_gemv3 for (N, K, topk) on `cus` compute units (host only). */
+w4a16_status_t w4a16_describe_moe3_plan(int64_t N, int64_t K, int32_t topk, int32_t cus,
+                                        char *buf, int64_t len);
+
+/*
  * Test support: q_out int8[N][K] receives the signed value of every packed nibble, so the
  * unpacking can be checked bit for bit. 1 <= N, 8 <= K, K % 8 == 0; qweight 4-byte aligned
  * (one word per thread); otherwise W4A16_ERR_MISALIGNED.

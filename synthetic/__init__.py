@@ -14,6 +14,8 @@ the concrete layout below is the plainest reading of that plus the workload size
   scales   fp16 bits [N][K/128] one scale per 128-wide K group, row-major
   x        bf16 bits [K]        (batched: X bf16 bits [M][K])
   MoE      qweight uint32[E][N][K/8], scales fp16 bits [E][N][K/128], ids int32[topk]
+  3-bit    qweight3 uint32[E][N][3K/32]: 32 three-bit codes per three words; any bits are
+           valid codes, so uniform words give codes uniform over [-4, 3]
 
 Draw recipe, per (config id, seed): numpy PCG64 seeded with [config_id, seed];
 draw order words, then scales, then activations, then expert ids.
@@ -120,6 +122,19 @@ def moe(E: int, N: int, K: int, topk: int, seed: int, config_id: int = 0) -> Moe
     return Moe(qw, sc, x, ids, E, N, K, topk)
 
 
+def moe3(E: int, N: int, K: int, topk: int, seed: int, config_id: int = 0) -> Moe:
+    """Three-bit grouped-expert operands: Moe with qweight uint32 [E][N][3K/32] (same draw
+    order as moe)."""
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    rng = rng_for(config_id, seed)
+    qw = draw_words(rng, (E, N, 3 * K // 32))
+    sc = draw_scales(rng, (E, N, K // GROUP))
+    x = draw_acts(rng, (K,))
+    ids = rng.choice(E, size=topk, replace=False).astype(np.int32)
+    return Moe(qw, sc, x, ids, E, N, K, topk)
+
+
 @dataclasses.dataclass
 class MoeTail:
     gu_qweight: np.ndarray    # uint32 [E][2I][K/8], rows [0, I) gate, [I, 2I) up
@@ -174,3 +189,9 @@ def config(name: str, seed: int, M: int = 1, experts: Optional[int] = None):
 def algorithmic_bytes(N: int, K: int, M: int = 1) -> int:
     """Bytes a W4A16 GEMV must move: packed weights + fp16 scales + bf16 activations."""
     return N * K // 2 + N * (K // GROUP) * 2 + M * K * 2
+
+
+def algorithmic_bytes3(N: int, K: int, topk: int) -> int:
+    """Bytes a one-token three-bit grouped-expert GEMV must move: topk experts' packed codes and
+    fp16 scales, the bf16 activation, and the topk ids."""
+    return topk * (N * 3 * K // 8 + N * (K // GROUP) * 2) + K * 2 + 4 * topk

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
               "w4a16_describe_plan", "w4a16_status_string", "w4a16_abi_version",
               "w4a16_stream_read", "w4a16_moe_gemv_swiglu", "w4a16_moe_down_combine",
               "w4a16_describe_tail_plan", "w4a16_quantize_pack", "w4a16_moe_gemv_batched",
-              "w4a16_describe_moe_batched_plan"):
+              "w4a16_describe_moe_batched_plan", "w4a16_moe_gemv3", "w4a16_unpack3_debug",
+              "w4a16_describe_moe3_plan"):
         assert n in names
 
 
@@ -177,6 +178,53 @@ def test_moe_batched_plans():
         w.describe_moe_batched_plan(16, 100, 8192, 8)    # activations do not fit in LDS
 
 
+def moe3(qw=A, sc=A, ids=A, topk=8, E=16, x=A, y=A, N=64, K=256, G=128):
+    return w.library().w4a16_moe_gemv3(qw, sc, ids, topk, E, x, y, N, K, G, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qw=None), NULLP), (dict(sc=None), NULLP), (dict(ids=None), NULLP), (dict(x=None), NULLP),
+    (dict(y=None), NULLP), (dict(G=64), GROUP), (dict(N=0), SHAPE), (dict(K=0), SHAPE),
+    (dict(K=200), SHAPE), (dict(K=65536 + 128), SHAPE), (dict(topk=0), SHAPE),
+    (dict(topk=1025), SHAPE), (dict(E=0), SHAPE), (dict(N=1 << 30, topk=4), SHAPE),
+    (dict(qw=A + 2), ALIGN), (dict(x=A + 8), ALIGN), (dict(sc=A + 1), ALIGN),
+    (dict(y=A + 2), ALIGN), (dict(ids=A + 2), ALIGN),
+])
+def test_moe3_validation(kw, status):
+    assert moe3(**kw) == status
+
+
+@pytest.mark.parametrize("N,K,topk,want", [
+    (2048, 2304, 8, "moe3 lanes_per_row=8 blocks_per_item=3 threads=256 blocks=512 lds=4928"),
+    (64, 384, 3, "moe3 lanes_per_row=4 blocks_per_item=3"),
+    (100, 128, 5, "moe3 lanes_per_row=4 blocks_per_item=1"),
+    (7, 65536, 1024, "moe3 lanes_per_row=8 blocks_per_item=1"),
+])
+def test_moe3_plans(N, K, topk, want):
+    assert w.describe_moe3_plan(N, K, topk).startswith(want)
+
+
+def test_every_valid_moe3_shape_has_a_plan():
+    """Every K that is a multiple of 128 up to 65536 has an instantiated three-bit kernel."""
+    for K in range(128, 65536 + 1, 128):
+        assert w.describe_moe3_plan(33, K, 8).startswith("moe3 ")
+
+
+def test_moe3_plan_rejects_bad_shapes():
+    for args in ((0, 128, 1), (4, 100, 1), (4, 128, 0)):
+        with pytest.raises(w.W4A16Error):
+            w.describe_moe3_plan(*args)
+
+
+def test_unpack3_validation():
+    lib = w.library()
+    assert lib.w4a16_unpack3_debug(None, A, 4, 64, None) == NULLP
+    assert lib.w4a16_unpack3_debug(A, None, 4, 64, None) == NULLP
+    assert lib.w4a16_unpack3_debug(A, A, 4, 48, None) == SHAPE
+    assert lib.w4a16_unpack3_debug(A, A, 0, 64, None) == SHAPE
+    assert lib.w4a16_unpack3_debug(A + 2, A, 4, 64, None) == ALIGN
+
+
 def test_unpack_validation():
     lib = w.library()
     assert lib.w4a16_unpack_debug(None, A, 4, 64, None) == NULLP
@@ -211,6 +259,8 @@ def test_valid_arguments_reach_the_device_check_only():
     assert down() == DEVICE
     assert quant() == DEVICE
     assert moeb() == DEVICE
+    assert moe3() == DEVICE
+    assert w.library().w4a16_unpack3_debug(A, A, 4, 64, None) == DEVICE
 
 
 @pytest.mark.parametrize("M,N,K,topk,kind", [

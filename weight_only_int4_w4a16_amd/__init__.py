@@ -64,6 +64,9 @@ def library() -> ctypes.CDLL:
     lib.w4a16_moe_gemv_batched.argtypes = [P, P, P, i32, i32, i32, P, i64, P, i64, i64, i32, P]
     lib.w4a16_describe_moe_batched_plan.argtypes = [i32, i64, i64, i32, i32, ctypes.c_char_p,
                                                     i64]
+    lib.w4a16_moe_gemv3.argtypes = [P, P, P, i32, i32, P, P, i64, i64, i32, P]
+    lib.w4a16_unpack3_debug.argtypes = [P, P, i64, i64, P]
+    lib.w4a16_describe_moe3_plan.argtypes = [i64, i64, i32, i32, ctypes.c_char_p, i64]
     lib.w4a16_status_string.argtypes = [ctypes.c_int]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_abi_version.argtypes = []
@@ -171,6 +174,55 @@ def moe_gemv(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tens
                                  topk, E, x.data_ptr(), out.data_ptr(), N, K, GROUP_SIZE,
                                  _stream(stream)), "w4a16_moe_gemv")
     return out
+
+
+def moe_gemv3(qweight3: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tensor,
+              x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[t] = W3_{expert_ids[t]} x over three-bit experts qweight3 int32 [E, N, 3K/32] (32 codes
+    per three words); reads only the selected experts. Returns float32 [topk, N]."""
+    _need(qweight3, torch.int32, "qweight3", 3)
+    _need(scales, torch.float16, "scales", 3)
+    _need(expert_ids, torch.int32, "expert_ids", 1)
+    _need(x, torch.bfloat16, "x", 1)
+    E, N = qweight3.shape[0], qweight3.shape[1]
+    if qweight3.shape[2] % 3:
+        raise ValueError("qweight3 rows must hold whole 3-word blocks")
+    K = qweight3.shape[2] // 3 * 32
+    topk = expert_ids.numel()
+    if not all(t.is_contiguous() for t in (qweight3, scales, expert_ids, x)):
+        raise ValueError("qweight3, scales, expert_ids and x must be contiguous")
+    if tuple(scales.shape) != (E, N, K // GROUP_SIZE) or x.numel() != K:
+        raise ValueError("shape mismatch between qweight3, scales and x")
+    if out is None:
+        out = torch.empty((topk, N), dtype=torch.float32, device=qweight3.device)
+    _need(out, torch.float32, "out", 2)
+    if tuple(out.shape) != (topk, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [topk, N] tensor")
+    _ok(library().w4a16_moe_gemv3(qweight3.data_ptr(), scales.data_ptr(), expert_ids.data_ptr(),
+                                  topk, E, x.data_ptr(), out.data_ptr(), N, K, GROUP_SIZE,
+                                  _stream(stream)), "w4a16_moe_gemv3")
+    return out
+
+
+def unpack3_debug(qweight3: torch.Tensor, stream=None) -> torch.Tensor:
+    """int8 [N, K]: every three-bit code of qweight3 int32 [N, 3K/32], decoded by the GEMV's
+    decode steps."""
+    _need(qweight3, torch.int32, "qweight3", 2)
+    if not qweight3.is_contiguous() or qweight3.shape[1] % 3:
+        raise ValueError("qweight3 must be contiguous with whole 3-word blocks per row")
+    N, K = qweight3.shape[0], qweight3.shape[1] // 3 * 32
+    out = torch.empty((N, K), dtype=torch.int8, device=qweight3.device)
+    _ok(library().w4a16_unpack3_debug(qweight3.data_ptr(), out.data_ptr(), N, K,
+                                      _stream(stream)), "w4a16_unpack3_debug")
+    return out
+
+
+def describe_moe3_plan(N: int, K: int, topk: int, cus: int = 256) -> str:
+    """Launch shape of w4a16_moe_gemv3 (host-only)."""
+    buf = ctypes.create_string_buffer(256)
+    _ok(library().w4a16_describe_moe3_plan(N, K, topk, cus, buf, len(buf)),
+        "w4a16_describe_moe3_plan")
+    return buf.value.decode()
 
 
 def moe_gemv_batched(qweight: torch.Tensor, scales: torch.Tensor, expert_ids: torch.Tensor,

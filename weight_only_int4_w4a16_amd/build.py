@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["kernels.hip", "quantize.hip", "stream_probe.hip", "api.hip", "plan.cpp"]
+SOURCES = ["kernels.hip", "kernels3.hip", "quantize.hip", "stream_probe.hip", "api.hip", "plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -15,6 +15,9 @@ hipError_t launch_unpack(const uint32_t *qw, int8_t *out, int64_t words, int cus
                          hipStream_t stream);
 hipError_t launch_stream_read(const void *buf, int64_t n16, uint32_t *out, int blocks,
                               int unroll, hipStream_t stream);
+hipError_t launch_moe3(const Moe3Args &a, const Plan &p, hipStream_t stream);
+hipError_t launch_unpack3(const uint32_t *qw, int8_t *out, int64_t blocks, int cus,
+                          hipStream_t stream);
 hipError_t launch_quantize(const uint16_t *W, int64_t ldw, uint32_t *qw, uint16_t *sc, int64_t N,
                            int32_t K, int cus, hipStream_t stream);
 
@@ -239,6 +242,62 @@ w4a16_status_t w4a16_quantize_pack(const uint16_t *w, int64_t ldw, uint32_t *qwe
     return launch_quantize(w, ldw, qweight, scales, N, (int32_t)K, dev->cus, stream) == hipSuccess
                ? W4A16_OK
                : W4A16_ERR_LAUNCH;
+}
+
+w4a16_status_t w4a16_moe_gemv3(const uint32_t *qweight3, const uint16_t *scales,
+                               const int32_t *expert_ids, int32_t topk, int32_t num_experts,
+                               const uint16_t *x, float *y, int64_t N, int64_t K,
+                               int32_t group_size, hipStream_t stream)
+{
+    if (!qweight3 || !scales || !expert_ids || !x || !y)
+        return W4A16_ERR_NULL_POINTER;
+    if (group_size != W4A16_GROUP_SIZE)
+        return W4A16_ERR_BAD_GROUP;
+    if (N < 1 || N > kMaxN || K < W4A16_GROUP_SIZE || K % W4A16_GROUP_SIZE != 0 ||
+        K > kMaxKDense || topk < 1 || topk > kMaxTopk || num_experts < 1 ||
+        (int64_t)topk * N > kMaxN)
+        return W4A16_ERR_BAD_SHAPE;
+    if (!aligned(qweight3, 4) || !aligned(x, 16) || !aligned(scales, 2) || !aligned(y, 4) ||
+        !aligned(expert_ids, 4))
+        return W4A16_ERR_MISALIGNED;
+    const DeviceInfo *dev = current_device();
+    if (!dev)
+        return W4A16_ERR_UNSUPPORTED_DEVICE;
+    Plan plan;
+    if (!make_moe3_plan(N, K, topk, dev->cus, dev->lds_limit, &plan))
+        return W4A16_ERR_BAD_SHAPE;
+    Moe3Args a{qweight3, scales, x, y, expert_ids, topk, num_experts, N, (int32_t)K};
+    return launch_moe3(a, plan, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+w4a16_status_t w4a16_unpack3_debug(const uint32_t *qweight3, int8_t *q_out, int64_t N, int64_t K,
+                                   hipStream_t stream)
+{
+    if (!qweight3 || !q_out)
+        return W4A16_ERR_NULL_POINTER;
+    if (N < 1 || K < 32 || K % 32 != 0 || N > kMaxN || K > kMaxKBatched)
+        return W4A16_ERR_BAD_SHAPE;
+    if (!aligned(qweight3, 4))
+        return W4A16_ERR_MISALIGNED;
+    const DeviceInfo *dev = current_device();
+    if (!dev)
+        return W4A16_ERR_UNSUPPORTED_DEVICE;
+    return launch_unpack3(qweight3, q_out, N * (K / 32), dev->cus, stream) == hipSuccess
+               ? W4A16_OK
+               : W4A16_ERR_LAUNCH;
+}
+
+w4a16_status_t w4a16_describe_moe3_plan(int64_t N, int64_t K, int32_t topk, int32_t cus,
+                                        char *buf, int64_t len)
+{
+    if (!buf || len < 1)
+        return W4A16_ERR_NULL_POINTER;
+    buf[0] = '\0';
+    Plan plan;
+    if (cus < 1 || !make_moe3_plan(N, K, topk, cus, 160 * 1024, &plan))
+        return W4A16_ERR_BAD_SHAPE;
+    describe_plan(plan, buf, (size_t)len);
+    return W4A16_OK;
 }
 
 w4a16_status_t w4a16_unpack_debug(const uint32_t *qweight, int8_t *q_out, int64_t N, int64_t K,

@@ -48,7 +48,11 @@ bool plan_instantiated(const Plan &p)
 #define W4A16_MFMA4_MATCH(TG_, CL_, U_, BR_)                                                  \
     if (p.kind == PLAN_MFMA4 && p.MT == TG_ && p.V == CL_ && p.U == U_ && p.L == BR_)           \
         return true;
+#define W4A16_MOE3_MATCH(L_, V_)                                                              \
+    if (p.kind == PLAN_MOE3 && p.L == L_ && p.V == V_)                                          \
+        return true;
     W4A16_VALU_CONFIGS(W4A16_VALU_MATCH)
+    W4A16_MOE3_CONFIGS(W4A16_MOE3_MATCH)
     W4A16_TAIL_CONFIGS(W4A16_TAIL_MATCH)
     W4A16_MFMA_CONFIGS(W4A16_MFMA_MATCH)
     W4A16_MFMA4_CONFIGS(W4A16_MFMA4_MATCH)
@@ -64,6 +68,7 @@ bool plan_instantiated(const Plan &p)
 #undef W4A16_MFMA4_MATCH
 #undef W4A16_MOE_BATCHED_MATCH
 #undef W4A16_MOE_BATCHED_MFMA4_MATCH
+#undef W4A16_MOE3_MATCH
     return false;
 }
 
@@ -535,6 +540,43 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     return mfma_plan(M, N, K, cus, lds_limit, p);
 }
 
+// Grouped-expert GEMV over three-bit experts: 8 lanes per row when they divide the row's 32-code
+// blocks, else 4; 3 blocks per item when the lanes' share divides by 3 (K = 2304: 72 blocks,
+// 8 lanes x 3 x 3 items), else 1; 4-wave work-groups, persistent, up to 8 per CU (the INT4
+// grouped-expert launch shape). At 256 experts of 2048 x 2304, top-8, more lanes per row (16,
+// 32, 64, with a ragged last item), one item per row step (9 blocks per lane), and 1- or 2-wave
+// work-groups all measured slower.
+bool make_moe3_plan(int64_t N, int64_t K, int topk, int cus, int64_t lds_limit, Plan *p)
+{
+    *p = Plan{};
+    if (N < 1 || K < 128 || K % 128 != 0 || topk < 1 || cus < 1)
+        return false;
+    const int64_t cpr = K / 32;
+    Plan c{};
+    c.kind = PLAN_MOE3;
+    c.MT = 1;
+    c.L = cpr % 8 == 0 ? 8 : 4;
+    c.V = (cpr / c.L) % 3 == 0 ? 3 : 1;
+    c.U = 1;
+    c.moe = true;
+    c.threads = 256;
+    c.lds_bytes = cpr * 68 + 4LL * topk;
+    if (c.lds_bytes > lds_limit || !plan_instantiated(c))
+        return false;
+    const int64_t R = 64 / c.L;
+    const int64_t steps = ((int64_t)topk * N + R - 1) / R;
+    const int64_t waves = c.threads / 64;
+    int64_t per_cu = 8;
+    const int64_t by_lds = lds_limit / c.lds_bytes;
+    if (per_cu > by_lds)
+        per_cu = by_lds;
+    const int64_t need = (steps + waves - 1) / waves;
+    const int64_t cap = (int64_t)cus * per_cu;
+    c.blocks = need < cap ? need : cap;
+    *p = c;
+    return true;
+}
+
 // Expert tail. SwiGLU gate+up: the grouped-expert launch shape (8 lanes with 3 chunks per item for
 // rows of 72 chunks, else the widest lanes per row up to 32, one chunk per item). Combine: the
 // widest lanes per row up to 32 that divide the chunks of one weight row, one chunk per item,
@@ -676,6 +718,10 @@ int describe_plan(const Plan &p, char *buf, size_t len)
 {
     if (!buf || len == 0)
         return 0;
+    if (p.kind == PLAN_MOE3)
+        return snprintf(buf, len,
+                        "moe3 lanes_per_row=%d blocks_per_item=%d threads=%d blocks=%lld lds=%lld",
+                        p.L, p.V, p.threads, (long long)p.blocks, (long long)p.lds_bytes);
     int n = 0;
     if (p.kind == PLAN_VALU)
         n = snprintf(buf, len,

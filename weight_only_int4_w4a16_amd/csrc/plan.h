@@ -8,7 +8,7 @@
 namespace w4a16 {
 
 enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3,
-                PLAN_MOE_BATCHED = 4, PLAN_MFMA4 = 5, PLAN_MOE_BATCHED_MFMA4 = 6 };
+                PLAN_MOE_BATCHED = 4, PLAN_MFMA4 = 5, PLAN_MOE_BATCHED_MFMA4 = 6, PLAN_MOE3 = 7 };
 
 // What the rows of a staged VALU launch are: one matrix, expert rows, the gate+up experts with
 // the SwiGLU epilogue, or the down experts summed with router weights.
@@ -81,6 +81,9 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
     X(1, 1, 1, 8) X(1, 1, 2, 8) X(1, 3, 1, 8) X(2, 1, 1, 8) X(2, 1, 2, 8) X(2, 3, 1, 8)
 #endif
 
+// Grouped-expert GEMV over three-bit experts: X(lanes per row, 32-code blocks per lane per item).
+#define W4A16_MOE3_CONFIGS(X) X(8, 3) X(8, 1) X(4, 3) X(4, 1)
+
 struct Plan {
     int kind;
     int MT, L, V, U;   // VALU: tokens, lanes per row, chunks per lane per item, row steps per item
@@ -113,6 +116,21 @@ struct GemvArgs {
     const float *route_w;  // combine form: router weights (device), else null
     int32_t KR;            // combine form: weight row length I (K = topk * I); else K
 };
+
+struct Moe3Args {
+    const void *qweight;   // uint32 [E][N][3K/32]: 32 three-bit codes per 3 words
+    const void *scales;    // fp16 bits [E][N][K/128]
+    const void *x;         // bf16 bits [K]
+    void *y;               // fp32 [topk][N]
+    const void *ids;       // int32 [topk] expert ids (device)
+    int32_t topk;
+    int32_t E;
+    int64_t N;
+    int32_t K;
+};
+
+// Grouped-expert three-bit GEMV, one token. Returns false when no kernel covers the shape.
+bool make_moe3_plan(int64_t N, int64_t K, int topk, int cus, int64_t lds_limit, Plan *p);
 
 // Largest K handled by the VALU kernel for MT tokens (activations staged in LDS).
 int64_t valu_max_k(int MT, int64_t lds_limit);
