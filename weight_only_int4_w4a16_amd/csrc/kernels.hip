@@ -411,7 +411,8 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             int64_t vrow = st * ROWS + u * R + rr;
             vrow = vrow < rows_total ? vrow : rows_total - 1;
             if (MOE) {
-                const int64_t slot = vrow / N;
+                // topk * N < 2^31 (checked by the entry point): a 32-bit division suffices
+                const int64_t slot = (uint32_t)vrow / (uint32_t)N;
                 const int32_t e = expert_of(slot, first);
                 const bool ok = e >= 0 && e < E;
                 const int64_t row = (int64_t)(ok ? e : 0) * N + (vrow - slot * N);
@@ -424,12 +425,14 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         }
     };
     // Loads and computes each walk the items in order with their own cursor (row block, batch).
+    // Expert forms look the rows of a row step up once, at its first batch.
     int64_t ld_st = gw_c;
     int ld_b = 0;
+    Rows r;
     auto load = [&](ValuBuf<L, V, U> &buf, auto first) {
         if constexpr (MOE) {
-            Rows r;
-            rows_of(ld_st, r, first);
+            if (decltype(first)::value || ld_b == 0)
+                rows_of(ld_st, r, first);
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 const int c = pr + L * (v + V * ld_b);
@@ -574,7 +577,7 @@ gemv_valu_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 if (vrow < rows_total) {
                     bool zero = false;
                     if (MODE == VALU_MOE) {
-                        const int32_t e = ids_s[vrow / N];
+                        const int32_t e = ids_s[(uint32_t)vrow / (uint32_t)N];
                         zero = e < 0 || e >= E;
                     }
                     Y[t * ldy + vrow] = zero ? 0.0f : v[0];
