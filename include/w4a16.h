@@ -70,7 +70,10 @@ typedef enum {
 } w4a16_status_t;
 
 /*
- * Dense single-token GEMV: y = W x.
+ * Dense single-token GEMV: y = W x. This is the dense W4A16 kernel of the local-kimi README
+ * (technical-detail section: the kernel-registry paragraph names a dense and a grouped W4A16
+ * operation), in the form its GEMV-rewrite paragraph gives both of them: the reduction axis K
+ * contiguous in memory and one accumulator per output row instead of a 16-row tile.
  *   qweight uint32[N][K/8], scales fp16 bits [N][K/128], x bf16 bits [K], y float[N].
  *   1 <= N <= 2^31 - 1;  128 <= K <= 65536, K % 128 == 0;  group_size == 128.
  */
@@ -79,7 +82,9 @@ w4a16_status_t w4a16_gemv(const uint32_t *qweight, const uint16_t *scales, const
                           hipStream_t stream);
 
 /*
- * Small-batch GEMV for decode of M tokens at once: Y = X W^T.
+ * Small-batch GEMV for decode of M tokens at once: Y = X W^T. The pages measure single-stream
+ * decode only and describe no batched kernel; this form (1..16 tokens over one weight
+ * matrix) is this library's addition, with the same storage and precision as w4a16_gemv.
  *   X bf16 bits, M rows with row stride ldx elements (ldx >= K, ldx % 8 == 0);
  *   Y float, M rows with row stride ldy elements (ldy >= N).
  *   1 <= M <= 16; N and K as for w4a16_gemv (K up to 2^20 when M >= 2).
@@ -91,7 +96,10 @@ w4a16_status_t w4a16_gemv_batched(const uint32_t *qweight, const uint16_t *scale
                                   hipStream_t stream);
 
 /*
- * Grouped-expert GEMV for one token: y[t] = W_{expert_ids[t]} x for t < topk.
+ * Grouped-expert GEMV for one token: y[t] = W_{expert_ids[t]} x for t < topk. This is the
+ * grouped W4A16 kernel of the local-kimi README's technical-detail section (the one its
+ * GEMV-rewrite paragraph measures before and after the rewrite), over the experts the router
+ * selected.
  *   qweight uint32[E][N][K/8], scales fp16 bits [E][N][K/128] (experts contiguous);
  *   expert_ids int32[topk] in DEVICE memory (read by the kernel, no host synchronisation);
  *   x bf16 bits [K]; y float[topk][N].
@@ -207,7 +215,9 @@ w4a16_status_t w4a16_describe_moe3_plan(int64_t N, int64_t K, int32_t topk, int3
 
 /*
  * Test support: q_out int8[N][K] receives the signed value of every packed nibble, so the
- * unpacking can be checked bit for bit. 1 <= N, 8 <= K, K % 8 == 0; qweight 4-byte aligned
+ * unpacking can be checked bit for bit against the storage format at the top of this file
+ * (this library's reading of the packed INT4 weights of the README's GEMV-rewrite paragraph,
+ * which fixes only that K is the contiguous axis). 1 <= N, 8 <= K, K % 8 == 0; qweight 4-byte aligned
  * (one word per thread); otherwise W4A16_ERR_MISALIGNED.
  */
 w4a16_status_t w4a16_unpack_debug(const uint32_t *qweight, int8_t *q_out, int64_t N, int64_t K,

@@ -218,15 +218,16 @@ __device__ __forceinline__ float dpp_partner(float v, int bit)
 
 // Swap the halves selected by lane bit 4 or 5 between a and b: afterwards a + b holds, in lanes with
 // the bit clear, a + partner's a, and in lanes with the bit set, b + partner's b.
-// The instruction rewrites both of its registers, so it is issued directly with both operands
-// read-write (the compiler builtin for it returns the first register twice on this toolchain).
+// v_permlane16_swap (v_permlane32_swap) exchanges the odd 16-lane rows (the upper 32 lanes) of its
+// first register with the even rows (the lower 32 lanes) of its second and rewrites both; the
+// builtin returns the two new registers, and the compiler inserts the wait states the instruction
+// needs after a VALU write of its operands.
 __device__ __forceinline__ float swap_fold(float a, float b, int bit)
 {
-    if (bit == 5)
-        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    else
-        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    return a + b;
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+    const auto r = bit == 5 ? __builtin_amdgcn_permlane32_swap(ua, ub, false, false)
+                            : __builtin_amdgcn_permlane16_swap(ua, ub, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 // Sum U per-lane values over groups of L lanes (L, U powers of two, U <= L). Rows are folded while
@@ -1225,12 +1226,10 @@ __device__ void moe_stage_activations(const uint16_t *__restrict__ X, int64_t ld
 // measured faster than expert-major order (63.9 against 93.6 us for 16 tokens x top-8 of 256),
 // and 1024-thread groups no faster than 512.
 // ------------------------------------------------------------------------------------------
-#ifndef W4A16_MOE_BATCHED_MAX_THREADS
-#define W4A16_MOE_BATCHED_MAX_THREADS 512   // launch bound (the plan uses 512-thread groups)
-#endif
+constexpr int kMoeBatchedMaxThreads = 512;   // launch bound (the plan uses 512-thread groups)
 
 template <int L, int V, int MT>
-__global__ void __launch_bounds__(W4A16_MOE_BATCHED_MAX_THREADS)
+__global__ void __launch_bounds__(kMoeBatchedMaxThreads)
 gemv_moe_batched_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                         const uint16_t *__restrict__ X, int64_t ldx, float *__restrict__ Y,
                         const int32_t *__restrict__ ids, int32_t M, int32_t topk, int32_t E,
@@ -1627,13 +1626,10 @@ __device__ __forceinline__ f16x8_t as_f16x8(uint4 v) { return as_f16x8(v.x, v.y,
 // v_permlane32_swap with both operands holding it; the same exchange as swap_fold).
 __device__ __forceinline__ uint32_t max_over_rows(uint32_t m)
 {
-    uint32_t a = m, b = m;
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    m = a > b ? a : b;
-    a = m;
-    b = m;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    return a > b ? a : b;
+    const auto r = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+    m = r[0] > r[1] ? (uint32_t)r[0] : (uint32_t)r[1];
+    const auto q = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    return q[0] > q[1] ? (uint32_t)q[0] : (uint32_t)q[1];
 }
 
 // Scale words of an item: with GU even, dword k holds the fp16 scales of groups 2k (low half) and
@@ -2148,14 +2144,12 @@ static hipError_t launch_mfma4_t(const GemvArgs &a, const Plan &p, hipStream_t s
                            args, (size_t)p.lds_bytes, stream);
 }
 
-#ifndef W4A16_MOE_BATCHED_MT
-#define W4A16_MOE_BATCHED_MT 1   // tokens accumulated per pass over an expert's rows
-#endif
+constexpr int kMoeBatchedMT = 1;   // tokens accumulated per pass over an expert's rows
 
 template <int L, int V>
 static hipError_t launch_moe_batched_t(const GemvArgs &a, const Plan &p, hipStream_t stream)
 {
-    auto kern = gemv_moe_batched_kernel<L, V, W4A16_MOE_BATCHED_MT>;
+    auto kern = gemv_moe_batched_kernel<L, V, kMoeBatchedMT>;
     void *args[] = {(void *)&a.qweight, (void *)&a.scales, (void *)&a.X,    (void *)&a.ldx,
                     (void *)&a.Y,       (void *)&a.ids,    (void *)&a.M,    (void *)&a.topk,
                     (void *)&a.E,       (void *)&a.N,      (void *)&a.K};

@@ -621,17 +621,11 @@ bool make_tail_plan(int mode, int64_t N, int64_t K, int64_t KR, int topk, int cu
     return false;
 }
 
-#ifndef W4A16_MOE_BATCHED_MT
-#define W4A16_MOE_BATCHED_MT 1
-#endif
-#ifndef W4A16_MOE_BATCHED_MFMA4_U
-#define W4A16_MOE_BATCHED_MFMA4_U 1    // row steps per item (2: 74.6 against 58.1 us, 16 tokens)
-#endif
-#ifndef W4A16_MOE_BATCHED_MFMA4_CL3
+constexpr int kMoeBatchedMT = 1;        // tokens per pass (the kernel is built for 1)
+constexpr int kMoeBatchedMfma4U = 1;    // row steps per item (2: 74.6 against 58.1 us, 16 tokens)
 // chunks per lane for rows of 24k chunks (K = 768k); 9 (one batch per item at K = 2304) needs
 // 161 VGPRs, leaves one work-group per CU and was slower (2 tokens: 16.8 against 12.1 us)
-#define W4A16_MOE_BATCHED_MFMA4_CL3 3
-#endif
+constexpr int kMoeBatchedMfma4CL3 = 3;
 
 // Grouped experts for M tokens: the grouped-expert launch shape of the one-token form (8 lanes
 // with 3 chunks per item for rows of 72 chunks, else the widest lanes per row), persistent
@@ -656,14 +650,14 @@ bool make_moe_batched_plan_of(int kind, int M, int64_t N, int64_t K, int topk, i
             p->V = cpr % 32 == 0 ? 2 : 1;
         } else if (cpr % 8 == 0) {
             p->L = 8;
-            p->V = (cpr / 8) % 3 == 0 ? W4A16_MOE_BATCHED_MFMA4_CL3 : 1;
+            p->V = (cpr / 8) % 3 == 0 ? kMoeBatchedMfma4CL3 : 1;
         } else {
             return false;
         }
         if (cpr % (p->L * p->V) != 0)
             return false;
         p->MT = 4;
-        p->U = W4A16_MOE_BATCHED_MFMA4_U;
+        p->U = kMoeBatchedMfma4U;
         R = 4 * (16 / p->L) * p->U;
         ve_ints = P + P * 4 + 1;        // experts, entries of up to 4 slots, count
     } else if (kind == PLAN_MOE_BATCHED) {
@@ -674,9 +668,9 @@ bool make_moe_batched_plan_of(int kind, int M, int64_t N, int64_t K, int topk, i
             return false;
         p->L = L;
         p->V = V;
-        p->MT = W4A16_MOE_BATCHED_MT;
+        p->MT = kMoeBatchedMT;
         R = 64 / L;
-        ve_ints = P + P * W4A16_MOE_BATCHED_MT + 1;
+        ve_ints = P + P * kMoeBatchedMT + 1;
     } else {
         return false;
     }

@@ -15,71 +15,54 @@ enum PlanKind { PLAN_NONE = 0, PLAN_VALU = 1, PLAN_MFMA = 2, PLAN_SPLITK = 3,
 enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
                 PLAN_MODE_COMBINE = 3 };
 
-// Instantiated kernels. A build may supply its own lists (for launch-shape sweeps) by defining
-// the macros first.
+// Instantiated kernels (the only ones compiled into the library).
 //
 // Staged-activation VALU kernels: X(tokens, lanes per row, chunks per lane per item, row steps).
 // Every (tokens, L, 1, 1) with L in {4..64} is present so that any K that is a multiple of 128
 // has a kernel; the others are the shapes the dispatch rules pick.
-#ifndef W4A16_VALU_CONFIGS
 #define W4A16_VALU_CONFIGS(X)                                                                \
     X(1, 64, 1, 1) X(1, 32, 1, 1) X(1, 16, 1, 1) X(1, 8, 1, 1) X(1, 4, 1, 1)                 \
     X(1, 32, 1, 2) X(1, 32, 2, 1) X(1, 16, 1, 2) X(1, 8, 1, 2) X(1, 8, 3, 1) X(1, 4, 1, 2)   \
     X(2, 64, 1, 1) X(2, 32, 1, 1) X(2, 16, 1, 1) X(2, 8, 1, 1) X(2, 4, 1, 1) X(2, 8, 1, 2)    \
     X(3, 64, 1, 1) X(3, 32, 1, 1) X(3, 16, 1, 1) X(3, 8, 1, 1) X(3, 4, 1, 1)                 \
     X(4, 64, 1, 1) X(4, 32, 1, 1) X(4, 16, 1, 1) X(4, 8, 1, 1) X(4, 4, 1, 1)
-#endif
 
 // Expert-tail kernels (staged VALU, one token, one row step): X(lanes per row, chunks per item),
 // each instantiated for the SwiGLU gate+up form (lanes per row <= 32) and the combine form.
-#ifndef W4A16_TAIL_CONFIGS
 #define W4A16_TAIL_CONFIGS(X) X(8, 3) X(32, 1) X(16, 1) X(8, 1) X(4, 1)
-#endif
 
-// Grouped-expert kernels for M tokens with their own experts: X(lanes per row, chunks per item).
 // Grouped-expert GEMV for several tokens on 4x4x4 MFMA: X(blocks per row group, chunks per lane,
 // row steps per item).
-#ifndef W4A16_MOE_BATCHED_MFMA4_CONFIGS
 #define W4A16_MOE_BATCHED_MFMA4_CONFIGS(X) X(8, 3, 1) X(8, 1, 1) X(16, 1, 1) X(16, 2, 1)
-#endif
-#ifndef W4A16_MOE_BATCHED_CONFIGS
+// Grouped-expert kernels for M tokens with their own experts: X(lanes per row, chunks per item).
 #define W4A16_MOE_BATCHED_CONFIGS(X) X(8, 3) X(64, 1) X(32, 1) X(16, 1) X(8, 1) X(4, 1)
-#endif
 
 // Split-K kernels in the combine form of the expert tail: X(lanes per row, chunks per lane).
-#ifndef W4A16_GATHER_CONFIGS
 #define W4A16_GATHER_CONFIGS(X) X(32, 1) X(32, 2) X(16, 2) X(16, 4) X(8, 4) X(8, 8) X(4, 8)
-#endif
 
 // Split-K VALU kernels (dense calls): X(tokens, lanes per row, chunks per lane, row steps).
-#ifndef W4A16_SPLITK_CONFIGS
 #define W4A16_SPLITK_CONFIGS(X)                                                              \
     X(1, 64, 1, 4) X(1, 32, 1, 2) X(1, 32, 1, 4) X(1, 64, 2, 4) X(1, 64, 4, 2)               \
     X(2, 64, 1, 4) X(3, 64, 1, 4) X(4, 64, 1, 4)
-#endif
 
 // MFMA kernels: X(16-row tiles per wave, waves splitting K, activation mode, groups per item,
 // waves per work-group). Activation mode: 0 from global memory, 1 staged in LDS, 2 staged with
 // whole-line weight loads, 3 from global memory with whole-line weight and activation loads,
 // 4 as 2 with 8 token slots staged (M <= 8).
-#ifndef W4A16_MFMA_CONFIGS
 #define W4A16_MFMA_CONFIGS(X)                                                                \
     X(1, 1, 1, 6, 8) X(1, 1, 1, 4, 8) X(1, 1, 1, 2, 8) X(1, 1, 1, 1, 8)                       \
     X(1, 1, 2, 6, 8) X(1, 1, 2, 4, 8) X(1, 1, 2, 2, 8) X(1, 1, 2, 6, 4) X(1, 1, 2, 4, 4)      \
     X(1, 1, 2, 2, 4) X(2, 4, 3, 2, 4) X(1, 8, 3, 2, 8) X(4, 4, 3, 2, 4)                      \
     X(2, 4, 0, 2, 4) X(2, 2, 0, 2, 4) X(2, 1, 0, 2, 4) X(1, 1, 0, 2, 4) X(1, 1, 0, 1, 4)      \
     X(1, 1, 4, 2, 8)
-#endif
 
 // 4x4x4-MFMA split-K kernels for 2..8 tokens: X(token groups of 4, chunks per lane, row steps per
 // item, blocks per row group). Three and four token groups measured slower than the 16x16x32
 // kernels at 12-16 tokens and need more registers than 1024-thread groups allow.
-#ifndef W4A16_MFMA4_CONFIGS
 #define W4A16_MFMA4_CONFIGS(X)                                                               \
     X(1, 1, 1, 16) X(1, 2, 1, 16) X(1, 4, 1, 16) X(1, 1, 2, 16) X(1, 2, 2, 16) X(1, 4, 2, 16)  \
     X(2, 1, 1, 16) X(2, 2, 1, 16) X(2, 4, 1, 16) X(2, 1, 2, 16) X(2, 2, 2, 16)               \
     X(1, 1, 1, 8) X(1, 1, 2, 8) X(1, 3, 1, 8) X(2, 1, 1, 8) X(2, 1, 2, 8) X(2, 3, 1, 8)
-#endif
 
 // Grouped-expert GEMV over three-bit experts: X(lanes per row, 32-code blocks per lane per item).
 #define W4A16_MOE3_CONFIGS(X) X(8, 3) X(8, 1) X(4, 3) X(4, 1)

@@ -137,10 +137,7 @@ __device__ __forceinline__ void quantize_lane(uint4 a, uint4 b, uint32_t &w0, ui
 // Registers decide how well the arithmetic overlaps the memory traffic: one step per pass and
 // one 8-value slice at a time keep the kernel at 67 VGPRs, 7 waves per SIMD (28672 x 4096: 60.0
 // us, against 69.0 with both slices live at 75 VGPRs and 71.2-72.1 with two steps at 101).
-#ifndef W4A16_QUANT_QU
-#define W4A16_QUANT_QU 1
-#endif
-constexpr int QU = W4A16_QUANT_QU;
+constexpr int QU = 1;
 constexpr int kGroupsPerWave = 8;
 
 struct QuantBuf {
