@@ -67,7 +67,7 @@ def parse():
                     help="only run a plain 512 MiB device-to-device copy 5 times (reference "
                          "kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--profile-workload", default=None,
-                    choices=["c1", "c2", "c3a", "c3b", "c4", "c5a", "c5b"],
+                    choices=["c1", "c2", "c3a", "c3b", "c4", "c4_3bit", "c5a", "c5b"],
                     help="only launch this workload's GEMV --steps times on rotated copies "
                          "(for profiler runs; prints a short JSON line, no timing)")
     ap.add_argument("--batch", type=int, default=1, help="tokens M for --profile-workload")
@@ -599,7 +599,20 @@ def expert_tail(torch, np, w, synthetic, dev, cus):
 def profile_workload(torch, np, w, synthetic, dev, name, M, steps):
     """Launch one workload's GEMV `steps` times on rotated copies (no timing): a fixed command
     for rocprofv3 counter and trace runs."""
-    if name == "c4":
+    if name == "c4_3bit":
+        cid, N, K = synthetic.SHAPES["c4"]
+        m = synthetic.moe3(synthetic.MOE_EXPERTS, N, K, synthetic.MOE_TOPK, 0, config_id=cid)
+        qw = torch.from_numpy(m.qweight.view(np.int32)).to(dev)
+        sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
+        cp = list(zip(rotated(torch, qw, 2), rotated(torch, sc, 2)))
+        del qw, sc
+        x = torch.from_numpy(m.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        ids = torch.from_numpy(m.ids).to(dev)
+        y = torch.empty((m.topk, N), dtype=torch.float32, device=dev)
+        for i in range(steps):
+            w.moe_gemv3(cp[i % 2][0], cp[i % 2][1], ids, x, out=y)
+        plan = w.describe_moe3_plan(N, K, m.topk)
+    elif name == "c4":
         m = synthetic.config("c4", 0)
         qw = torch.from_numpy(m.qweight.view(np.int32)).to(dev)
         sc = torch.from_numpy(m.scales.view(np.float16)).to(dev)
