@@ -173,7 +173,7 @@ def test_batched_every_m_ragged(M):
                                    (12, 1000, 2304), (16, 4096, 2048), (6, 100, 384),
                                    (16, 2048, 4096), (8, 300, 14336), (4, 40000, 2304),
                                    (3, 40000, 1152), (16, 5, 65536), (16, 300, 2688),
-                                   (11, 14336, 2048), (7, 8192, 8192)])
+                                   (11, 14336, 2048), (7, 8192, 8192), (12, 4096, 14336)])
 def test_batched_mfma_plans(M, N, K):
     """Every MFMA form: whole-line loads with 2, 4 and 6 groups per item, rows below and above
     one row block, and the operand-order forms."""

@@ -108,10 +108,13 @@ def test_swiglu_invalid_and_repeated_ids():
 
 
 # (E, I, H, topk): I = 1024 takes 32 lanes per row, I = 384 4 lanes; H below and above the
-# rows of one wave step. The last: 300 slots (more than the 256 threads that stage ids and
-# router weights) over a 38400-long activation, on the staged combine form.
+# rows of one wave step. Then 300 slots (more than the 256 threads that stage ids and router
+# weights) over a 38400-long activation, on the staged combine form; and the split-K combine
+# forms with 8 chunks per lane (8 lanes: 64 slots of I = 256 and 16 of I = 768; 4 lanes: 64
+# slots of I = 128), the instances that hold spilled registers.
 DOWN_SHAPES = [(6, 256, 300, 3), (4, 128, 1, 1), (5, 384, 77, 4), (12, 1024, 2304, 8),
-               (3, 2048, 129, 2), (40, 512, 1000, 16), (300, 128, 20, 300)]
+               (3, 2048, 129, 2), (40, 512, 1000, 16), (300, 128, 20, 300), (70, 256, 100, 64),
+               (20, 768, 100, 16), (70, 128, 100, 64)]
 
 
 @pytest.mark.parametrize("E,I,H,topk", DOWN_SHAPES)
