@@ -184,6 +184,37 @@ def test_batched_mfma_plans(M, N, K):
     within(Y, ref, mag, f"batched M={M} {N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 300, 2304), (1, 300, 4096), (2, 300, 2304), (8, 512, 2304),
+                                   (16, 512, 2304), (16, 2048, 4096), (16, 300, 4992),
+                                   (16, 8192, 2048), (6, 26624, 2304), (12, 16384, 4096),
+                                   (16, 16384, 2304)])
+def test_scales_at_two_byte_offset(M, N, K):
+    """Scales need only 2-byte alignment: every form reads them correctly from an address that
+    is 2 mod 4 (a view starting one fp16 into its allocation)."""
+    plan = w.describe_plan(M, N, K)
+    d = synthetic.dense(N=N, K=K, seed=M + 3, M=M, config_id=807)
+    sc = torch.empty(N * (K // 128) + 1, dtype=torch.float16, device="cuda")
+    sc[1:] = f16(d.scales).reshape(-1)
+    view = sc[1:].view(N, K // 128)
+    assert view.data_ptr() % 4 == 2
+    print(f"scales+2B M={M} {N}x{K} plan={plan}", flush=True)
+    Y = host(w.gemv_batched(words(d.qweight), view, bf16(d.x)))
+    ref, mag = par_oracle.gemv_batched(d.qweight, d.scales, d.x, K, np.arange(N))
+    within(Y, ref, mag, f"scales+2B M={M} {N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 40, 131072), (2, 3, 1 << 20), (16, 5, 1 << 20)])
+def test_batched_long_rows(M, N, K):
+    """Batched calls accept K up to 2^20 (single-token calls up to 65536): rows of 2^17 and 2^20
+    values, every output against the oracle."""
+    plan = w.describe_plan(M, N, K)
+    d = synthetic.dense(N=N, K=K, seed=M + N, M=M, config_id=806)
+    print(f"batched M={M} {N}x{K} plan={plan}", flush=True)
+    Y = host(w.gemv_batched(words(d.qweight), f16(d.scales), bf16(d.x)))
+    ref, mag = oracle.gemv_batched(d.qweight, d.scales, d.x, K)
+    within(Y, ref, mag, f"batched M={M} {N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(2, 5000, 2304), (3, 333, 4096), (4, 20001, 4096), (4, 33, 14336),
                                    (3, 1000, 2048), (4, 999, 1024), (5, 77, 2304), (6, 4096, 14336),
                                    (8, 1500, 8192), (7, 3, 4096), (8, 8192, 512), (2, 17, 256),

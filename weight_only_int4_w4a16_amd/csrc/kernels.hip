@@ -1632,33 +1632,27 @@ __device__ __forceinline__ uint32_t max_over_rows(uint32_t m)
     return q[0] > q[1] ? (uint32_t)q[0] : (uint32_t)q[1];
 }
 
-// Scale words of an item: with GU even, dword k holds the fp16 scales of groups 2k (low half) and
-// 2k + 1 (high half); with GU odd, word k holds group k's scale in its low half.
+// Scale words of an item: word k holds group k's fp16 scale in its low half. One 16-bit load per
+// group and tile, so the scales need only their natural 2-byte alignment (dword loads of scale
+// pairs would need 4).
 template <int GU>
-constexpr int mfma_scale_words() { return GU % 2 == 0 ? GU / 2 : GU; }
+constexpr int mfma_scale_words() { return GU; }
 
 template <int T, int GU, bool XLDS>
 struct MfmaBuf {
     uint4 w[GU][T];
-    uint32_t s[mfma_scale_words<GU>()][T];   // raw scale words, split only where they are used
+    uint32_t s[mfma_scale_words<GU>()][T];   // raw scale words, converted where they are used
     uint4 x[XLDS ? 1 : GU][4];     // activation fragments (global-memory mode only)
 };
 
-// The GU scales of one row for groups s..s+GU-1. With GU even (and so the group count of a row
-// even, and s even) they are 4-byte aligned and come in GU/2 dword loads. The words are kept
-// whole: splitting a half off right after the load would make that point wait for the load.
+// The GU scales of one row for groups s..s+GU-1. The words are kept whole until use:
+// converting right after the load would make that point wait for the load.
 template <int GU>
 __device__ __forceinline__ void load_scales(const char *p, uint32_t (&out)[mfma_scale_words<GU>()])
 {
-    if constexpr (GU % 2 == 0) {
 #pragma unroll
-        for (int k = 0; k < GU / 2; ++k)
-            out[k] = reinterpret_cast<const uint32_t *>(p)[k];
-    } else {
-#pragma unroll
-        for (int k = 0; k < GU; ++k)
-            out[k] = reinterpret_cast<const uint16_t *>(p)[k];
-    }
+    for (int k = 0; k < GU; ++k)
+        out[k] = reinterpret_cast<const uint16_t *>(p)[k];
 }
 
 // Scale of group u of an item from its raw words.
@@ -1666,12 +1660,7 @@ template <int GU>
 __device__ __forceinline__ float mfma_scale(const uint32_t *words, int u)
 {
     typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-    if constexpr (GU % 2 == 0) {
-        const h2_t h = __builtin_bit_cast(h2_t, words[u >> 1]);
-        return (float)((u & 1) ? h.y : h.x);
-    } else {
-        return (float)__builtin_bit_cast(h2_t, words[u]).x;
-    }
+    return (float)__builtin_bit_cast(h2_t, words[u]).x;
 }
 
 template <int T, int KS, int XMODE, int GU, int WPB>

@@ -52,7 +52,7 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
 #define W4A16_MFMA_CONFIGS(X)                                                                \
     X(1, 1, 1, 6, 8) X(1, 1, 1, 4, 8) X(1, 1, 1, 2, 8) X(1, 1, 1, 1, 8)                       \
     X(1, 1, 2, 6, 8) X(1, 1, 2, 4, 8) X(1, 1, 2, 2, 8) X(1, 1, 2, 6, 4) X(1, 1, 2, 4, 4)      \
-    X(1, 1, 2, 2, 4) X(2, 4, 3, 2, 4) X(1, 8, 3, 2, 8) X(4, 4, 3, 2, 4)                      \
+    X(1, 1, 2, 2, 4) X(1, 8, 3, 2, 8) X(4, 4, 3, 2, 4)                                       \
     X(2, 4, 0, 2, 4) X(2, 2, 0, 2, 4) X(2, 1, 0, 2, 4) X(1, 1, 0, 2, 4) X(1, 1, 0, 1, 4)      \
     X(1, 1, 4, 2, 8)
 
