@@ -239,6 +239,7 @@ template <int L, int U>
 __device__ __forceinline__ int fold_rows(float (&v)[U], int lane)
 {
     static_assert(U <= L, "fold_rows needs U <= L");
+    static_assert((L & (L - 1)) == 0 && (U & (U - 1)) == 0, "fold_rows needs powers of two");
     constexpr int LB = __builtin_ctz(L);
     constexpr int UB = __builtin_ctz(U);
     int row = 0;

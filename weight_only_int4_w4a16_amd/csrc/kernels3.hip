@@ -120,6 +120,7 @@ __device__ __forceinline__ uint32_t quadmax(uint32_t m)
 template <int L>
 __device__ __forceinline__ float sum_lanes(float v)
 {
+    static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "lanes per row: a power of two");
     int x;
     if (L > 1) {
         x = __builtin_bit_cast(int, v);
