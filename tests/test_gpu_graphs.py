@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 def test_graph_replays_match_eager_calls():
     d = synthetic.dense(N=3000, K=2304, seed=1, M=16, config_id=960)
     m = synthetic.moe(E=12, N=512, K=2304, topk=4, seed=2, config_id=961)
+    m3 = synthetic.moe3(E=12, N=256, K=2304, topk=4, seed=2, config_id=964)
+    q3, s3 = words(m3.qweight), f16(m3.scales)
     qd, sd = words(d.qweight), f16(d.scales)
     qm, sm = words(m.qweight), f16(m.scales)
     x1 = bf16(d.x[0]).clone()
@@ -32,12 +34,14 @@ def test_graph_replays_match_eager_calls():
     Y = torch.empty((16, 3000), dtype=torch.float32, device="cuda")
     ym = torch.empty((4, 512), dtype=torch.float32, device="cuda")
     yb = torch.empty((3, 2, 512), dtype=torch.float32, device="cuda")
+    y3 = torch.empty((4, 256), dtype=torch.float32, device="cuda")
 
     def calls():
         w.gemv(qd, sd, x1, out=y1)
         w.gemv_batched(qd, sd, X, out=Y)
         w.moe_gemv(qm, sm, ids, xm, out=ym)
         w.moe_gemv_batched(qm, sm, ids2, X3[:, :2304], out=yb)
+        w.moe_gemv3(q3, s3, ids, xm, out=y3)
 
     calls()
     torch.cuda.synchronize()
@@ -54,10 +58,11 @@ def test_graph_replays_match_eager_calls():
         ids.copy_(torch.from_numpy(rng.choice(12, 4, replace=False).astype(np.int32)).cuda())
         g.replay()
         torch.cuda.synchronize()
-        got = [t.clone() for t in (y1, Y, ym, yb)]
+        got = [t.clone() for t in (y1, Y, ym, yb, y3)]
         calls()
         torch.cuda.synchronize()
-        for a, b, name in zip(got, (y1, Y, ym, yb), ("gemv", "batched", "moe", "moe_batched")):
+        for a, b, name in zip(got, (y1, Y, ym, yb, y3),
+                              ("gemv", "batched", "moe", "moe_batched", "moe3")):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
 
 
