@@ -289,11 +289,17 @@ def test_valid_arguments_reach_the_device_check_only():
     (8, 28672, 4096, 0, "mfma16x16x32_lds_lines"), (2, 28672, 4096, 0, "splitk "),
     (2, 14336, 2048, 0, "splitk tokens=2"), (4, 14336, 2048, 0, "mfma4x4x4_splitk token_groups=1 "
                                                               "chunks_per_lane=1 row_steps=2"),
-    (16, 8192, 8192, 0, "mfma16x16x32 tiles_per_wave=2 k_split=4"),
+    (16, 8192, 8192, 0, "mfma16x16x32_rows tiles_per_wave=2 k_split=4 groups_per_item=2 threads=256"),
+    (12, 8192, 8192, 0, "mfma16x16x32_rows tiles_per_wave=2 k_split=4"),
+    (8, 8192, 8192, 0, "mfma16x16x32_rows8 tiles_per_wave=2 k_split=4 groups_per_item=2 threads=256"),
+    (5, 8192, 8192, 0, "mfma16x16x32_rows8 tiles_per_wave=2 k_split=4"),
+    (8, 16384, 4096, 0, "mfma16x16x32_rows8 tiles_per_wave=2 k_split=4"),
+    (8, 12288, 8192, 0, "mfma4x4x4_splitk token_groups=2"),
+    (16, 4096, 14336, 0, "mfma16x16x32_rows tiles_per_wave=1 k_split=8 groups_per_item=2 threads=512"),
     (16, 14336, 2048, 0, "mfma16x16x32_lines tiles_per_wave=4 k_split=4"),
     (16, 300, 2688, 0, "mfma16x16x32 tiles_per_wave=1 k_split=1 groups_per_item=1"),
-    (16, 163840, 2304, 0, "mfma16x16x32_lds_lines tiles_per_wave=1 k_split=1 groups_per_item=2"), (8, 8192, 8192, 0, "mfma"),
-    (16, 2048, 4096, 0, "mfma16x16x32_lines tiles_per_wave=1 k_split=8"),
+    (16, 163840, 2304, 0, "mfma16x16x32_lds_lines tiles_per_wave=1 k_split=1 groups_per_item=2"),
+    (16, 2048, 4096, 0, "mfma16x16x32_rows tiles_per_wave=1 k_split=8"),
     (16, 4096, 2304, 0, "mfma16x16x32_lds_lines tiles_per_wave=1 k_split=1 groups_per_item=6 threads=256"),
 ])
 def test_default_dispatch(M, N, K, topk, kind):

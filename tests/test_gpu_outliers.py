@@ -76,11 +76,13 @@ DENSE_FORMS = [
     (8, 4096, 4096, "mfma4x4x4_splitk token_groups=2"),
     (16, 512, 128, "mfma16x16x32_lds "),
     (16, 512, 2304, "mfma16x16x32_lds_lines"),
-    (16, 2048, 4096, "mfma16x16x32_lines"),
+    (16, 2048, 4096, "mfma16x16x32_rows tiles_per_wave=1 k_split=8"),
+    (16, 14336, 2048, "mfma16x16x32_lines tiles_per_wave=4"),
     (16, 512, 4992, "mfma16x16x32 "),
     (5, 26624, 2304, "mfma16x16x32_lds8_lines"),
     (2, 26624, 2304, "mfma4x4x4_splitk token_groups=1 chunks_per_lane=3"),
-    (16, 8192, 8192, "mfma16x16x32 tiles_per_wave=2 k_split=4"),
+    (16, 8192, 8192, "mfma16x16x32_rows tiles_per_wave=2 k_split=4"),
+    (8, 8192, 8192, "mfma16x16x32_rows8 tiles_per_wave=2 k_split=4"),
 ]
 
 
@@ -153,7 +155,8 @@ SUBNORMAL_FORMS = [
     (1, 512, 4096, "splitk"),
     (4, 512, 2304, "mfma4x4x4_splitk"),
     (16, 512, 2304, "mfma16x16x32_lds_lines"),
-    (16, 2048, 4096, "mfma16x16x32_lines"),
+    (16, 2048, 4096, "mfma16x16x32_rows tiles_per_wave=1 k_split=8"),
+    (16, 14336, 2048, "mfma16x16x32_lines tiles_per_wave=4"),
 ]
 
 

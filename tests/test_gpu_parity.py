@@ -247,6 +247,36 @@ def test_batched_staged_8_slot_plans(M, N, K):
     within(Y, ref, mag, f"batched M={M} {N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,form,pad", [
+    (9, 8192, 1024, "mfma16x16x32_rows tiles_per_wave=2", 0),
+    (13, 8200, 2048, "mfma16x16x32_rows tiles_per_wave=2", 0),
+    (16, 8192, 3072, "mfma16x16x32_rows tiles_per_wave=2", 0),
+    (11, 8192, 1024, "mfma16x16x32_rows tiles_per_wave=2", 64),
+    (10, 300, 4096, "mfma16x16x32_rows tiles_per_wave=1 k_split=8", 0),
+    (15, 33, 6144, "mfma16x16x32_rows tiles_per_wave=1 k_split=8", 8),
+    (16, 4096, 2048, "mfma16x16x32_rows tiles_per_wave=1 k_split=8", 0),
+    (5, 8192, 1024, "mfma16x16x32_rows8", 0),
+    (6, 8192, 3072, "mfma16x16x32_rows8", 8),
+    (7, 8160, 2048, "mfma16x16x32_rows8", 0),
+    (8, 8190, 1024, "mfma16x16x32_rows8", 64),
+    (5, 16384, 1024, "mfma16x16x32_rows8", 0),
+])
+def test_batched_token_row_plans(M, N, K, form, pad):
+    """The global-activation 16x16x32 forms that load whole token rows and exchange them into
+    operand order through LDS: 16 and 8 token slots (slots past M repeat token M-1), one to
+    three items per wave, ragged row blocks pulled back, and activation rows with a stride
+    beyond K whose padding (NaN) must never be read."""
+    plan = w.describe_plan(M, N, K)
+    assert plan.startswith(form), plan
+    d = synthetic.dense(N=N, K=K, seed=M * 13 + N, M=M, config_id=808)
+    print(f"batched M={M} {N}x{K} pad={pad} plan={plan}", flush=True)
+    Xp = np.full((M, K + pad), 0x7FC0, np.uint16)
+    Xp[:, :K] = d.x
+    Y = host(w.gemv_batched(words(d.qweight), f16(d.scales), bf16(Xp)[:, :K]))
+    ref, mag = oracle.gemv_batched(d.qweight, d.scales, d.x, K)
+    within(Y, ref, mag, f"batched M={M} {N}x{K} pad={pad}")
+
+
 def test_batched_rows_match_single_token():
     N, K, M = 500, 8192, 16
     d = synthetic.dense(N=N, K=K, seed=9, M=M, config_id=802)

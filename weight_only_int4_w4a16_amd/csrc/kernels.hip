@@ -1614,6 +1614,14 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
 // (instruction j' of a group: lane (i, g) reads the 16 bytes 4j' + g of token i's 256-byte
 // group, so the four lanes of a token cover 64 contiguous bytes) and exchanged through LDS into
 // operand order (lane (i, g), word j comes from lane (i, j) of instruction g).
+//
+// XROWS (activations from global memory): an operand-order activation load touches 32 lines
+// (16 tokens, 16 bytes of each of a token's two lines per lane group). Instead each
+// instruction reads GU groups of 4 / GU whole token rows (64 lanes x 16 contiguous bytes per
+// token row, 8 lines), the item's chunks go through a per-wave LDS slot (XOR-swizzled so that
+// the operand-order reads of 16 slots fall in distinct banks), and each lane reads its operand
+// chunks back. With 8 slots (M <= 8) MFMA rows 8-15 repeat slots 0-7 (never stored) and half
+// the loads go away.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ f16x8_t as_f16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
@@ -1676,8 +1684,13 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     // again; their outputs are never stored.
     constexpr int SLOTS = XMODE == 4 ? 8 : 16;
     constexpr bool GLINES = XMODE == 3;        // global activations, whole-line loads via LDS
+    constexpr bool XROWS = XMODE == 5 || XMODE == 6;   // global activations, token-row loads
+    constexpr int XSLOTS = XMODE == 6 ? 8 : 16;        // XROWS: token slots loaded per item
+    constexpr int XCH = 16 * GU;                       // XROWS: 16-byte chunks of a token's item
+    constexpr int NXI = XROWS ? XSLOTS * GU / 4 : 4 * GU;   // activation loads per item and lane
     static_assert(!LINES || (T == 1 && GU % 2 == 0), "line loads pair the groups of one tile");
     static_assert(!GLINES || GU % 2 == 0, "line loads pair the groups of an item");
+    static_assert(!XROWS || GU == 1 || GU == 2 || GU == 4, "a token's item spans 16-64 lanes");
     static_assert(WPB % KS == 0, "waves per block must be a multiple of the K split");
     constexpr int RG = WPB / KS;               // row groups (waves with distinct rows) per block
     constexpr int TROWS = 16 * T;              // rows per wave item
@@ -1905,29 +1918,52 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
     } else {
         // One row block per work-group; KS waves split the groups of K into runs of GU.
         f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);           // [WPB][T][64]
-        // GLINES staging per wave after the reduction slots: weights [T][GU][64], then
-        // activation fragments [GU][4][64] (16 bytes each).
-        uint4 *stage_w = lds + (KS > 1 ? WPB * T * 64 : 0) + wave * (T + 4) * GU * 64;
-        uint4 *stage_x = stage_w + T * GU * 64;
+        // Staging per wave after the reduction slots. GLINES: weights [T][GU][64], then activation
+        // fragments [GU][4][64] (16 bytes each). XROWS: the item's activations, [XSLOTS][XCH]
+        // chunks, chunk c of slot m at position (m * XCH + c) ^ (m % 16) (see the loads below).
+        constexpr int RED = KS > 1 ? WPB * T * 64 : 0;
+        constexpr int STG = GLINES ? (T + 4) * GU * 64 : XROWS ? NXI * 64 : 0;
+        uint4 *stage_w = lds + RED + wave * STG;
+        uint4 *stage_x = GLINES ? stage_w + T * GU * 64 : stage_w;
         // Per wave, the factors 2^-e of the item's groups for the 16 token rows: [GU][16].
-        float *stage_f = reinterpret_cast<float *>(lds + (KS > 1 ? WPB * T * 64 : 0) +
-                                                   (GLINES ? WPB * (T + 4) * GU * 64 : 0)) +
-                         wave * GU * 16;
+        float *stage_f = reinterpret_cast<float *>(lds + RED + WPB * STG) + wave * GU * 16;
         const int64_t rb = blockIdx.x;
         const int gpk = GPR / KS;
         const int n_items = gpk / GU;
         const uint4 *xp = reinterpret_cast<const uint4 *>(X + (int64_t)tok * ldx) + (GLINES ? g : 4 * g);
         int ld_s = ks * gpk;
         const int s_last = ks * gpk + (n_items - 1) * GU;   // loads past the slice re-read its last item
+        // XROWS: instruction q of an item fills positions 64q + lane of the wave's staging slot,
+        // so each instruction reads XCH contiguous chunks (GU groups) of 4 / GU token rows: 8
+        // whole lines. Position p holds chunk p ^ (m % 16) of slot m = p / XCH (the XOR stays
+        // within the slot's 16-chunk group), which spreads the operand-order reads of the 16
+        // slots over distinct banks. Slots past M read token M-1.
+        int64_t xq[XROWS ? NXI : 1];
+        if constexpr (XROWS) {
+#pragma unroll
+            for (int q = 0; q < NXI; ++q) {
+                const int pos = 64 * q + lane;
+                const int m = pos / XCH;
+                const int c = (pos ^ (m & 15)) % XCH;
+                xq[q] = (int64_t)(m < M ? m : M - 1) * (ldx >> 3) + c;
+            }
+        }
         auto load = [&](Buf &buf) {
             const int s_ = ld_s < s_last ? ld_s : s_last;
             const char *wb = wbase(rb, s_);
             const char *sb = sbase(rb, s_);
+            if constexpr (XROWS) {
+                const uint4 *xi = reinterpret_cast<const uint4 *>(X) + (int64_t)s_ * 16;
 #pragma unroll
-            for (int u = 0; u < GU; ++u)
+                for (int q = 0; q < NXI; ++q)
+                    buf.x[q / 4][q % 4] = xi[xq[q]];
+            } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    buf.x[u][j] = xp[16 * (s_ + u) + (GLINES ? 4 * j : j)];
+                for (int u = 0; u < GU; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        buf.x[u][j] = xp[16 * (s_ + u) + (GLINES ? 4 * j : j)];
+            }
 #pragma unroll
             for (int t = 0; t < T; ++t) {
 #pragma unroll
@@ -1975,6 +2011,22 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         xr[u][j] = stage_x[(u * 4 + g) * 64 + i + 16 * j];
+            } else if constexpr (XROWS) {
+                // Token rows in, operand order out: lane (i, g) takes chunks 4g..4g+3 of each group
+                // of slot i % XSLOTS.
+#pragma unroll
+                for (int q = 0; q < NXI; ++q)
+                    stage_x[64 * q + lane] = buf.x[q / 4][q % 4];
+                const int m = i & (XSLOTS - 1);
+#pragma unroll
+                for (int u = 0; u < GU; ++u) {
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        wl[u][t] = buf.w[u][t];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        xr[u][j] = stage_x[m * XCH + 16 * u + ((4 * g + j) ^ (m & 15))];
+                }
             } else {
 #pragma unroll
                 for (int u = 0; u < GU; ++u) {
@@ -2181,8 +2233,8 @@ static hipError_t launch_mfma_t(const GemvArgs &a, const Plan &p, hipStream_t st
         return launch_splitk_t<1, L_, CL_, 1, true>(a, p, stream);
 
 #define W4A16_MFMA_CASE(T_, KS_, XL_, GU_, WPB_)                                             \
-    if (p.T == T_ && p.KS == KS_ && p.xlds == (XL_ == 1 || XL_ == 2 || XL_ == 4) &&          \
-        p.lines == (XL_ >= 2) && p.slots8 == (XL_ == 4) && p.V == GU_ &&                      \
+    if (p.T == T_ && p.KS == KS_ && p.xlds == xmode_xlds(XL_) && p.lines == xmode_lines(XL_) && \
+        p.slots8 == xmode_slots8(XL_) && p.trows == xmode_trows(XL_) && p.V == GU_ &&          \
         p.threads == 64 * WPB_)                                                              \
         return launch_mfma_t<T_, KS_, XL_, GU_, WPB_>(a, p, stream);
 

@@ -35,9 +35,9 @@ bool plan_instantiated(const Plan &p)
         p.mode == PLAN_MODE_COMBINE)                                                          \
         return true;
 #define W4A16_MFMA_MATCH(T_, KS_, XL_, GU_, WPB_)                                            \
-    if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ &&                                     \
-        p.xlds == (XL_ == 1 || XL_ == 2 || XL_ == 4) && p.lines == (XL_ >= 2) &&               \
-        p.slots8 == (XL_ == 4) && p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_))     \
+    if (p.kind == PLAN_MFMA && p.T == T_ && p.KS == KS_ && p.xlds == xmode_xlds(XL_) &&       \
+        p.lines == xmode_lines(XL_) && p.slots8 == xmode_slots8(XL_) &&                       \
+        p.trows == xmode_trows(XL_) && p.V == GU_ && (p.threads == 0 || p.threads == 64 * WPB_)) \
         return true;
 #define W4A16_MOE_BATCHED_MATCH(L_, V_)                                                       \
     if (p.kind == PLAN_MOE_BATCHED && p.L == L_ && p.V == V_)                                   \
@@ -204,7 +204,9 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
             return false;
         if (p->lines && (p->V % 2 != 0 || (p->xlds && p->T != 1)))
             return false;
-        if (p->slots8 && (M > 8 || !p->xlds || !p->lines))
+        if (p->slots8 && (M > 8 || !((p->xlds && p->lines) || p->trows)))
+            return false;
+        if (p->trows && (p->xlds || p->lines || (p->V != 1 && p->V != 2 && p->V != 4)))
             return false;
         const int64_t rows_per_block = 16LL * p->T * (wpb / p->KS);
         const int64_t row_blocks = (N + rows_per_block - 1) / rows_per_block;
@@ -226,10 +228,13 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
             p->blocks = row_blocks < cap ? row_blocks : cap;
         } else {
             // K-split partial sums, with line loads a staging slot per wave for the weights
-            // (T x groups per item) and activation fragments (4 x groups per item), and per wave
-            // the 16 token rows' group factors of an item (groups per item x 64 bytes).
+            // (T x groups per item) and activation fragments (4 x groups per item), with token-row
+            // loads one for the item's activations (token slots x groups per item x 256 bytes),
+            // and per wave the 16 token rows' group factors of an item (groups per item x 64
+            // bytes).
             p->lds_bytes = (p->KS > 1 ? (int64_t)wpb * p->T * 64 * 16 : 0) +
                            (p->lines ? (int64_t)wpb * (p->T + 4) * p->V * 1024 : 0) +
+                           (p->trows ? (int64_t)wpb * (p->slots8 ? 8 : 16) * p->V * 256 : 0) +
                            (int64_t)wpb * p->V * 64;
             if (p->lds_bytes > lds_limit)
                 return false;
@@ -251,7 +256,7 @@ bool finish_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_lim
 //  * other K, and every grouped-expert call: the staged kernel with the widest power-of-two lanes
 //    per row dividing the row's 16-byte chunks; rows of 72 chunks (K = 2304) use 8 lanes with
 //    3 chunks per item;
-//  * 2-16 tokens: MFMA (see mfma_slots8_plan, mfma4_plan and mfma_plan), except 2 tokens with K
+//  * 2-16 tokens: MFMA (see mfma_slots8_plan, mfma_rows8_plan, mfma4_plan and mfma_plan), except 2 tokens with K
 //    a multiple of 2048, which stay on split-K VALU.
 namespace {
 
@@ -298,11 +303,14 @@ Plan splitk(int MT, int L, int CL, int U, bool moe)
 //  1. activations staged in LDS with whole-line weight loads, 8 waves of 16 rows per
 //     work-group, when there are enough row blocks to fill the chip (N/128 >= 0.8 * CUs) and the
 //     staging fits in LDS: tall matrices (163840 x 2304, 28672 x 4096);
-//  2. activations from global memory with whole-line weight and activation loads, K split over
-//     4 waves, four 16-row tiles per wave when that still fills the chip (14336 x 2048), else
-//     two (8192 x 8192);
-//  3. the same with one tile per wave and K split over 8 waves, for short matrices with long
-//     rows (4096 x 14336, 2048 x 4096);
+//  2. activations from global memory, K split over 4 waves: four 16-row tiles per wave with
+//     whole-line weight and activation loads when that still fills the chip (14336 x 2048:
+//     9.7 us against 10.6 with token-row activation loads; 16384 x 4096: 13.8 against 15.9),
+//     else two tiles with token-row activation loads (8192 x 8192: 16.1-16.4 us against
+//     17.9-18.1 with operand-order loads);
+//  3. token-row loads with one tile per wave and K split over 8 waves, for short matrices with
+//     long rows (4096 x 14336: 21.2 us against 25.1 with whole-line loads; 4096 x 4096: 9.7
+//     against 11.5; 1024 x 2048: 5.9 against 6.3);
 //  4. staged activations with whole-line loads in 4-wave work-groups (4096 x 2304, small N);
 //  5. the remaining forms, which cover every K that is a multiple of 128.
 // Groups per item: even so that line pairs (or both 64-byte halves of a line) go together.
@@ -327,23 +335,25 @@ static bool mfma_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, P
         }
         return false;
     };
-    auto global = [&](int T, int KS, int GU, int wpb, bool whole_lines, Plan *out) {
+    // Activation loads of the global forms: 0 operand order, 1 whole lines, 2 token rows.
+    auto global = [&](int T, int KS, int GU, int wpb, int xload, Plan *out) {
         Plan c{};
         c.kind = PLAN_MFMA;
         c.T = T;
         c.KS = KS;
         c.V = GU;
-        c.lines = whole_lines;
+        c.lines = xload == 1;
+        c.trows = xload == 2;
         c.threads = 64 * wpb;
         return gpr % (KS * GU) == 0 && try_plan(c, 1, M, N, K, 0, cus, lds_limit, out);
     };
     if (N / 128 >= (int64_t)cus * 4 / 5 && lines(8, p))
         return true;
-    if (N / 64 >= (int64_t)cus * 4 / 5 && global(4, 4, 2, 4, true, p))
+    if (N / 64 >= (int64_t)cus * 4 / 5 && global(4, 4, 2, 4, 1, p))
         return true;
-    if (N / 32 >= cus && global(2, 4, 2, 4, false, p))
+    if (N / 32 >= cus && global(2, 4, 2, 4, 2, p))
         return true;
-    if (gpr % 16 == 0 && global(1, 8, 2, 8, true, p))
+    if (gpr % 16 == 0 && global(1, 8, 2, 8, 2, p))
         return true;
     if (lines(4, p))
         return true;
@@ -363,7 +373,7 @@ static bool mfma_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, P
     }
     static const int mf[][3] = {{2, 4, 2}, {2, 2, 2}, {2, 1, 2}, {1, 1, 2}, {1, 1, 1}};
     for (int i = 0; i < (int)(sizeof(mf) / sizeof(mf[0])); ++i)
-        if (global(mf[i][0], mf[i][1], mf[i][2], 4, false, p))
+        if (global(mf[i][0], mf[i][1], mf[i][2], 4, 0, p))
             return true;
     return false;
 }
@@ -428,6 +438,32 @@ static bool mfma_slots8_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_l
     c.slots8 = true;
     c.threads = 512;
     return try_plan(c, 2, M, N, K, 0, cus, lds_limit, p);
+}
+
+// 5-8 tokens on matrices of up to 16384 rows: the global-activation 16x16x32 form with 8 token
+// slots loaded as token rows, two 16-row tiles per wave and K split over 4 waves, when its
+// 32-row work-groups spread evenly over the CUs (whole rounds within 10 %). Same-box sweeps
+// against the 4x4x4 kernel: 8192 x 8192 at 5-8 tokens 13.1-13.5 us against 13.9-15.3, 8192 x
+// 4096 8.6 against 9.8-10.1, 8192 x 14336 20.3-21.4 against 21.9-24.2, 16384 x 4096 13.8-14.5
+// against 14.0-14.9; with uneven rounds the 4x4x4 kernel stays ahead (12288 x 8192: 18.6-19.8
+// us against 21.9-22.7; 14336 x 2048 at 8: 9.3 against 9.9; 4096 x 14336 at 8: 17.7 against
+// 18.3).
+static bool mfma_rows8_plan(int M, int64_t N, int64_t K, int cus, int64_t lds_limit, Plan *p)
+{
+    const int64_t gpr = K / 128;
+    const int64_t blocks = (N + 31) / 32;
+    const int64_t rounds = (blocks + cus - 1) / cus;
+    if (M < 5 || M > 8 || N > 16384 || gpr % 8 != 0 || blocks * 10 < rounds * cus * 9)
+        return false;
+    Plan c{};
+    c.kind = PLAN_MFMA;
+    c.T = 2;
+    c.KS = 4;
+    c.V = 2;
+    c.trows = true;
+    c.slots8 = true;
+    c.threads = 256;
+    return try_plan(c, 1, M, N, K, 0, cus, lds_limit, p);
 }
 
 // Whether 3 or 4 tokens are better served by the MFMA kernel than by the VALU ones: tall
@@ -522,10 +558,12 @@ bool make_plan(int M, int64_t N, int64_t K, int topk, int cus, int64_t lds_limit
     }
     // 2 tokens where split-K VALU does not apply (it wins where it does: 8192 x 8192 at 2 tokens
     // 9.0 us against 9.7, 14336 x 2048 5.9 against 6.2), and 5-8 tokens on matrices of up to
-    // 16384 rows (8192 x 8192 at 5-6 tokens: 12.4-12.7 against 13.1-14.0 us; 16384 x 4096 at 8:
-    // 13.5 against 13.8; 4096 x 2304 at 8: 5.7 against 10.8). Taller matrices at 5-8 tokens
-    // keep the 16x16x32 kernels (28672 x 4096 at 8: 18.5 against 19.5 us; 163840 x 2304 at 6:
-    // 37.0 against 48.6).
+    // 16384 rows where the 8-slot token-row form does not apply (16384 x 4096 at 8 with the
+    // operand-order 16x16x32 form: 13.5 against 13.8; 4096 x 2304 at 8: 5.7 against 10.8).
+    // Taller matrices at 5-8 tokens keep the 16x16x32 kernels (28672 x 4096 at 8: 18.5 against
+    // 19.5 us; 163840 x 2304 at 6: 37.0 against 48.6).
+    if (!moe && mfma_rows8_plan(M, N, K, cus, lds_limit, p))
+        return true;
     if (!moe && (M == 2 || (M >= 5 && M <= 8 && N <= 16384)) &&
         mfma4_plan(M, N, K, cus, lds_limit, p))
         return true;
@@ -753,8 +791,10 @@ int describe_plan(const Plan &p, char *buf, size_t len)
         n = snprintf(buf, len,
                      "mfma16x16x32%s tiles_per_wave=%d k_split=%d groups_per_item=%d threads=%d "
                      "blocks=%lld lds=%lld",
-                     p.lines ? (p.xlds ? (p.slots8 ? "_lds8_lines" : "_lds_lines") : "_lines")
-                             : p.xlds ? "_lds" : "",
+                     p.lines   ? (p.xlds ? (p.slots8 ? "_lds8_lines" : "_lds_lines") : "_lines")
+                     : p.trows ? (p.slots8 ? "_rows8" : "_rows")
+                     : p.xlds  ? "_lds"
+                               : "",
                      p.T,
                      p.KS, p.V, p.threads,
                      (long long)p.blocks, (long long)p.lds_bytes);

@@ -48,13 +48,14 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
 // MFMA kernels: X(16-row tiles per wave, waves splitting K, activation mode, groups per item,
 // waves per work-group). Activation mode: 0 from global memory, 1 staged in LDS, 2 staged with
 // whole-line weight loads, 3 from global memory with whole-line weight and activation loads,
-// 4 as 2 with 8 token slots staged (M <= 8).
+// 4 as 2 with 8 token slots staged (M <= 8), 5 from global memory as whole token rows
+// exchanged into operand order via LDS, 6 as 5 with 8 token slots (M <= 8).
 #define W4A16_MFMA_CONFIGS(X)                                                                \
     X(1, 1, 1, 6, 8) X(1, 1, 1, 4, 8) X(1, 1, 1, 2, 8) X(1, 1, 1, 1, 8)                       \
     X(1, 1, 2, 6, 8) X(1, 1, 2, 4, 8) X(1, 1, 2, 2, 8) X(1, 1, 2, 6, 4) X(1, 1, 2, 4, 4)      \
-    X(1, 1, 2, 2, 4) X(1, 8, 3, 2, 8) X(4, 4, 3, 2, 4)                                       \
+    X(1, 1, 2, 2, 4) X(1, 8, 5, 2, 8) X(4, 4, 3, 2, 4)                                       \
     X(2, 4, 0, 2, 4) X(2, 2, 0, 2, 4) X(2, 1, 0, 2, 4) X(1, 1, 0, 2, 4) X(1, 1, 0, 1, 4)      \
-    X(1, 1, 4, 2, 8)
+    X(1, 1, 4, 2, 8) X(2, 4, 5, 2, 4) X(2, 4, 6, 2, 4)
 
 // 4x4x4-MFMA split-K kernels for 2..8 tokens: X(token groups of 4, chunks per lane, row steps per
 // item, blocks per row group). Three and four token groups measured slower than the 16x16x32
@@ -67,13 +68,23 @@ enum PlanMode { PLAN_MODE_DENSE = 0, PLAN_MODE_MOE = 1, PLAN_MODE_SWIGLU = 2,
 // Grouped-expert GEMV over three-bit experts: X(lanes per row, 32-code blocks per lane per item).
 #define W4A16_MOE3_CONFIGS(X) X(8, 3) X(8, 1) X(4, 3) X(4, 1)
 
+// Activation modes of the 16x16x32 kernel (its XMODE template argument) as plan flags:
+// 0 global, operand order; 1 staged; 2 staged, whole-line weights; 3 global, whole-line weights
+// and activations; 4 mode 2 with 8 token slots; 5 global, token-row activation loads; 6 mode 5
+// with 8 token slots.
+constexpr bool xmode_xlds(int x) { return x == 1 || x == 2 || x == 4; }
+constexpr bool xmode_lines(int x) { return x >= 2 && x <= 4; }
+constexpr bool xmode_slots8(int x) { return x == 4 || x == 6; }
+constexpr bool xmode_trows(int x) { return x == 5 || x == 6; }
+
 struct Plan {
     int kind;
     int MT, L, V, U;   // VALU: tokens, lanes per row, chunks per lane per item, row steps per item
     int T, KS;         // MFMA: 16-row tiles per wave, waves splitting K (V: groups per item)
     bool xlds;         // MFMA: activations of all 16 token slots staged in LDS
     bool lines;        // MFMA (staged activations): whole-line weight loads permuted via LDS
-    bool slots8;       // MFMA (staged, whole lines, M <= 8): 8 token slots staged instead of 16
+    bool slots8;       // MFMA (M <= 8): 8 token slots instead of 16 (staged whole-line or trows)
+    bool trows;        // MFMA (global activations): whole token rows loaded, exchanged via LDS
     bool moe;          // rows through expert ids (grouped and SwiGLU forms)
     int mode;          // PlanMode (staged VALU)
     int64_t kr;        // combine form: length of one weight row (K is the activation length)
