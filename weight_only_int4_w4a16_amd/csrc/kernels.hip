@@ -831,15 +831,22 @@ gemv_splitk_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc
         ++cp_item;
     };
 
+    // The scheduling barriers keep each item's loads ahead of the previous item's arithmetic:
+    // left alone, the compiler sinks them into it and then waits for every load in flight at the
+    // top of the loop (4096 x 14336 and 8192 x 8192 at one token 2 % faster with them, 8192 x 8192
+    // at 4 tokens on the 4x4x4 kernel 4 %).
     int i = 0;
     for (; i + 2 < n_items; i += 2) {
         load(bufB);
+        __builtin_amdgcn_sched_barrier(0);
         compute(bufA);
         load(bufA);
+        __builtin_amdgcn_sched_barrier(0);
         compute(bufB);
     }
     if (i + 1 < n_items) {
         load(bufB);
+        __builtin_amdgcn_sched_barrier(0);
         compute(bufA);
         compute(bufB);
     } else {
@@ -1066,15 +1073,22 @@ gemv_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         ++cp_item;
     };
 
+    // The scheduling barriers keep each item's loads ahead of the previous item's arithmetic:
+    // left alone, the compiler sinks them into it and then waits for every load in flight at the
+    // top of the loop (4096 x 14336 and 8192 x 8192 at one token 2 % faster with them, 8192 x 8192
+    // at 4 tokens on the 4x4x4 kernel 4 %).
     int i = 0;
     for (; i + 2 < n_items; i += 2) {
         load(bufB);
+        __builtin_amdgcn_sched_barrier(0);
         compute(bufA);
         load(bufA);
+        __builtin_amdgcn_sched_barrier(0);
         compute(bufB);
     }
     if (i + 1 < n_items) {
         load(bufB);
+        __builtin_amdgcn_sched_barrier(0);
         compute(bufA);
         compute(bufB);
     } else {
@@ -1647,11 +1661,14 @@ __device__ __forceinline__ uint32_t max_over_rows(uint32_t m)
 template <int GU>
 constexpr int mfma_scale_words() { return GU; }
 
+// The 16-byte members come first: an x array placed after an odd number of scale pairs sits
+// at an offset that is not a multiple of 16, and the compiler then kept part of the buffer in
+// scratch memory.
 template <int T, int GU, bool XLDS>
 struct MfmaBuf {
     uint4 w[GU][T];
-    uint32_t s[mfma_scale_words<GU>()][T];   // raw scale words, converted where they are used
     uint4 x[XLDS ? 1 : GU][4];     // activation fragments (global-memory mode only)
+    uint32_t s[mfma_scale_words<GU>()][T];   // raw scale words, converted where they are used
 };
 
 // The GU scales of one row for groups s..s+GU-1. The words are kept whole until use:
@@ -1795,20 +1812,26 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             const int64_t rb = ld_rb < n_rb ? ld_rb : n_rb - 1;
             const char *wb = wbase(rb, ld_s);
             const char *sb = sbase(rb, ld_s);
+            // Scales first: the compiler finishes their words (moves, shifts) where they arrive
+            // and waits for them there, which then does not wait for the item's other loads
+            // (28672 x 4096 and 163840 x 2304 at 16 tokens 1 % faster, with the scheduling
+            // barriers of the loop below).
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-#pragma unroll
-                for (int u = 0; u < GU; ++u) {
-                    // LINES: buf.w[2p + h] holds instruction h of line pair p (whole lines)
-                    const uint32_t o = LINES ? loff[0][u & 1] + 128 * (u >> 1) : woff[t] + 64 * u;
-                    buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + o));
-                }
                 uint32_t sv[mfma_scale_words<GU>()];
                 load_scales<GU>(sb + soff[t], sv);
 #pragma unroll
                 for (int k = 0; k < mfma_scale_words<GU>(); ++k)
                     buf.s[k][t] = sv[k];
             }
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int u = 0; u < GU; ++u) {
+                    // LINES: buf.w[2p + h] holds instruction h of line pair p (whole lines)
+                    const uint32_t o = LINES ? loff[0][u & 1] + 128 * (u >> 1) : woff[t] + 64 * u;
+                    buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + o));
+                }
             const bool wrap = ld_s + GU == GPR;
             ld_s = wrap ? 0 : ld_s + GU;
             ld_rb += wrap ? gridDim.x : 0;
@@ -1904,12 +1927,15 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
         int64_t it = 0;
         for (; it + 2 < n_items; it += 2) {
             load(bufB);
+            __builtin_amdgcn_sched_barrier(0);
             compute(bufA);
             load(bufA);
+            __builtin_amdgcn_sched_barrier(0);
             compute(bufB);
         }
         if (it + 1 < n_items) {
             load(bufB);
+            __builtin_amdgcn_sched_barrier(0);
             compute(bufA);
             compute(bufB);
         } else {
@@ -1965,12 +1991,14 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                         buf.x[u][j] = xp[16 * (s_ + u) + (GLINES ? 4 * j : j)];
             }
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
+            for (int t = 0; t < T; ++t)
 #pragma unroll
                 for (int u = 0; u < GU; ++u) {
                     const uint32_t o = GLINES ? loff[t][u & 1] + 128 * (u >> 1) : woff[t] + 64 * u;
                     buf.w[u][t] = load_weights(reinterpret_cast<const uint4 *>(wb + o));
                 }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
                 uint32_t sv[mfma_scale_words<GU>()];
                 load_scales<GU>(sb + soff[t], sv);
 #pragma unroll
@@ -2072,27 +2100,22 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 mma_group(wl[u], scv, xb, fac, acc);
             }
         };
-        // A ring of RING item buffers: the loads of item it + RING - 1 are issued before item it is
-        // computed. The loop is unrolled by RING so every buffer index is a constant. Two buffers:
-        // these forms hold 16 token slots of activation fragments per item in registers, and a
-        // third buffer makes the compiler spill them (measured slower on every shape).
-        constexpr int RING = 2;
-        Buf ring[RING];
-#pragma unroll
-        for (int r = 0; r < RING - 1; ++r)
-            load(ring[r]);
+        // Two item buffers: the loads of item it + 1 are issued before item it is computed. These
+        // forms hold 16 token slots of activation fragments per item in registers; a third buffer
+        // measured slower (8192 x 8192 at 8-16 tokens: 14.5-16.5 against 13.3-16.1 us). Loading
+        // the scales first or pinning the loads with scheduling barriers, which helps the staged
+        // forms above, measured 1-6 % slower here (14336 x 2048 and 8192 x 8192 at 8-16 tokens).
+        Buf bufA, bufB;
+        load(bufA);
         int it = 0;
-        for (; it + RING <= n_items; it += RING) {
-#pragma unroll
-            for (int r = 0; r < RING; ++r) {
-                load(ring[(r + RING - 1) % RING]);
-                compute(ring[r]);
-            }
+        for (; it + 2 <= n_items; it += 2) {
+            load(bufB);
+            compute(bufA);
+            load(bufA);
+            compute(bufB);
         }
-#pragma unroll
-        for (int r = 0; r < RING - 1; ++r)
-            if (it + r < n_items)
-                compute(ring[r]);
+        if (it < n_items)
+            compute(bufA);
         if (KS > 1) {
             if (ks != 0) {
 #pragma unroll
