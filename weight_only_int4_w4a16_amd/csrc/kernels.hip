@@ -1848,18 +1848,23 @@ gemv_mfma_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
             const int slot = m & (SLOTS - 1);
             const int tm = slot < M ? slot : M - 1;
             const uint4 *xr = reinterpret_cast<const uint4 *>(X + (int64_t)tm * ldx) + 16 * s;
-            uint32_t mx = 0;
-#pragma unroll 4
+            // All 16 words in flight at once, then the maximum and the conversion from registers.
+            uint4 xv[16];
+#pragma unroll
             for (int q = 0; q < 16; ++q)
-                mx = abs_max8(xr[q], mx);
+                xv[q] = xr[q];
+            uint32_t mx = 0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                mx = abs_max8(xv[q], mx);
             const int e = group_exponent(fold_halves(mx));
             offl[idx] = pow2f(-e);
             if (m < SLOTS) {
                 const float pe = pow2f(e);
-#pragma unroll 4
+#pragma unroll
                 for (int q = 0; q < 16; ++q)
                     xl[(s * 4 + (q & 3)) * (4 * SLOTS) + (q >> 2) * SLOTS + m] =
-                        stage_words(xr[q], pe);
+                        stage_words(xv[q], pe);
             }
         }
         __syncthreads();
