@@ -78,6 +78,18 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h)
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// The fp32 values of the fp16 scales held by lanes 4*(lane/4) + r, r = 0..3: one conversion,
+// then DPP quad broadcasts. The full row and bank masks write every lane, so the destination
+// needs no previous value.
+__device__ __forceinline__ void quad_scales(uint16_t sv, float (&s4)[4])
+{
+    const int f = __builtin_bit_cast(int, half_bits_to_float(sv));
+    s4[0] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(f, 0x00, 0xF, 0xF, false));
+    s4[1] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(f, 0x55, 0xF, 0xF, false));
+    s4[2] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(f, 0xAA, 0xF, 0xF, false));
+    s4[3] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(f, 0xFF, 0xF, 0xF, false));
+}
+
 // a if take else b, computed with masks so it never becomes a branch (branches around the loads
 // make the compiler fall back to waiting for every outstanding load at the join).
 template <typename T>
@@ -1031,11 +1043,8 @@ gemv_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__restrict__ sc,
                 unpack_chunk(buf.w[j][u], p);
                 // scales of the block's rows 0..3 (lane 4b + r holds row r's)
                 const int sv = buf.s[j][u];
-                const float s4[4] = {
-                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0x00, 0xF, 0xF, false)),
-                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0x55, 0xF, 0xF, false)),
-                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xAA, 0xF, 0xF, false)),
-                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xFF, 0xF, 0xF, false))};
+                float s4[4];
+                quad_scales((uint16_t)sv, s4);
 #pragma unroll
                 for (int g = 0; g < TG; ++g) {
                     f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1543,11 +1552,8 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
                 uint32_t p[4][4];
                 unpack_chunk(buf.w[j][u], p);
                 const int sv = buf.s[j][u];
-                const float s4[4] = {
-                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0x00, 0xF, 0xF, false)),
-                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0x55, 0xF, 0xF, false)),
-                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xAA, 0xF, 0xF, false)),
-                    half_bits_to_float((uint16_t)__builtin_amdgcn_update_dpp(0, sv, 0xFF, 0xF, 0xF, false))};
+                float s4[4];
+                quad_scales((uint16_t)sv, s4);
                 f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
