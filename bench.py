@@ -223,18 +223,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded int4 weights uniform in [-8,7], fp16 scales uniform in "
-                "[0.001,0.01], bf16 activations ~N(0,1))",
+        "data": "synthetic: seeded int4 codes uniform in [-8,7], fp16 scales in [0.001,0.01], "
+                "bf16 x ~N(0,1)",
         "config": {
-            "workload": "W4A16 GEMV at M=1, output head 163840x2304 (int4 weights 8 per uint32 "
-                        "along K, fp16 scale per 128-group, bf16 x, fp32 y)",
+            "workload": "W4A16 GEMV, M=1, output head 163840x2304 (int4 8 per uint32 along K, "
+                        "fp16 scale per 128-group, bf16 x, fp32 y)",
             "M": 1,
             "shape": [dh.N, dh.K],
             "bytes_per_call": bytes_h,
-            "rotated_weight_copies": R,
             "us_per_call": round(step_us, 3),
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-            "device": f"{props.name} {getattr(props, 'gcnArchName', '')} {cus} CUs",
+            "device": f"{getattr(props, 'gcnArchName', props.name).split(':')[0]}, {cus} CUs",
         },
         "roofline": {
             "bound": "hbm",
@@ -667,8 +666,7 @@ def cpu_baseline(d, bytes_per_call, target_s):
     return {"value": round(bytes_per_call * calls / el / 1e9, 4), "unit": "GB/s",
             "cores": 1, "kind": "oracle",
             "sample": f"{calls} whole calls of the {d.N}x{d.K} GEMV (every row), {el:.1f} s, "
-                      f"single-threaded C oracle in float64",
-            "ms_per_call": round(el / calls * 1e3, 1),
+                      f"one-thread C oracle, fp64",
             "host": host_description()}
 
 
