@@ -260,12 +260,14 @@ def test_batched_staged_8_slot_plans(M, N, K):
     (7, 8160, 2048, "mfma16x16x32_rows8", 0),
     (8, 8190, 1024, "mfma16x16x32_rows8", 64),
     (5, 16384, 1024, "mfma16x16x32_rows8", 0),
+    (16, 8192, 1024, "mfma16x16x32_rows tiles_per_wave=2", 1 << 21),
+    (7, 8192, 1024, "mfma16x16x32_rows8", 1 << 21),
 ])
 def test_batched_token_row_plans(M, N, K, form, pad):
     """The global-activation 16x16x32 forms that load whole token rows and exchange them into
     operand order through LDS: 16 and 8 token slots (slots past M repeat token M-1), one to
     three items per wave, ragged row blocks pulled back, and activation rows with a stride
-    beyond K whose padding (NaN) must never be read."""
+    beyond K whose padding (NaN) must never be read, up to 4 MiB between rows."""
     plan = w.describe_plan(M, N, K)
     assert plan.startswith(form), plan
     d = synthetic.dense(N=N, K=K, seed=M * 13 + N, M=M, config_id=808)
