@@ -1637,11 +1637,11 @@ gemv_moe_batched_mfma4_kernel(const uint4 *__restrict__ qw, const uint16_t *__re
 //
 // XROWS (activations from global memory): an operand-order activation load touches 32 lines
 // (16 tokens, 16 bytes of each of a token's two lines per lane group). Instead each
-// instruction reads GU groups of 4 / GU whole token rows (64 lanes x 16 contiguous bytes per
-// token row, 8 lines), the item's chunks go through a per-wave LDS slot (XOR-swizzled so that
-// the operand-order reads of 16 slots fall in distinct banks), and each lane reads its operand
-// chunks back. With 8 slots (M <= 8) MFMA rows 8-15 repeat slots 0-7 (never stored) and half
-// the loads go away.
+// instruction reads the item's GU groups (256 * GU contiguous bytes) of 4 / GU token rows:
+// 1 KB in 8 lines when the rows are 128-byte aligned. The item's chunks go through a per-wave
+// LDS slot (XOR-swizzled so that the operand-order reads of 16 slots fall in distinct banks)
+// and each lane reads its operand chunks back. With 8 slots (M <= 8) MFMA rows 8-15 repeat
+// slots 0-7 (never stored) and half the loads go away.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ f16x8_t as_f16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
